@@ -1,0 +1,177 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MI355X (gfx950) fused MXFP4 Mixture-of-Experts
+ * forward: route sort -> dynamic MXFP4 activation quant -> gate_up GEMM with
+ * fused SwiGLU (+ MXFP4 requant) -> down GEMM weighted by the routing weights
+ * and accumulated per token into bf16.
+ *
+ * The operation follows the FP4 ("a4w4") pipeline of kernelindex.com
+ * amd-moe-mxfp4 submission 754773 (`custom_kernel`, FP4 branch): activations
+ * are MXFP4-quantized before stage 1, the bf16 SwiGLU output is re-quantized
+ * before stage 2, and the routing weight is applied in stage 2 only.  Weight
+ * rows follow submission 723815's `_reference_forward`: rows 0..I-1 of the
+ * gate_up weight are the gate projection, rows I..2I-1 the up projection,
+ * act = silu(gate) * up.
+ *
+ * MXFP4 tensor format (both pages): two E2M1 codes per byte, element 2j in the
+ * low nibble and 2j+1 in the high nibble; one e8m0 scale byte (value
+ * 2^(s-127)) per 32 consecutive elements along the contraction dimension K.
+ * Activation quantization (OCP MX v1.0): scale = 2^(floor(log2 amax) - 2)
+ * clamped to the e8m0 range, codes = round-to-nearest-even of x / scale,
+ * saturating at +-6, sign kept.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device and must
+ *    be 256-byte aligned.  bf16 tensors are passed as uint16_t bit patterns.
+ *  - The caller owns every buffer, including the workspace.  The library keeps
+ *    no pointer after a call returns and allocates no device memory.
+ *  - Work is enqueued asynchronously on `stream`; nothing synchronizes with the
+ *    host.  Device-side faults surface at the caller's next synchronization.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is enqueued and outputs are untouched.
+ *  - Return value: one of the MOE_MXFP4_* status codes below.
+ *  - Concurrent calls on different streams must use different workspaces and
+ *    outputs.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_MXFP4_OK = 0,
+    MOE_MXFP4_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size      */
+    MOE_MXFP4_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or shape too large */
+    MOE_MXFP4_ERR_WORKSPACE = 3,    /* workspace smaller than required           */
+    MOE_MXFP4_ERR_HIP = 4           /* a HIP runtime call or launch failed       */
+};
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* moe_mxfp4_status_string(int status);
+
+/* Limits of this implementation (host-validated):
+ *   D, I: multiples of 256, 256 <= D, I <= 65536
+ *   1 <= E <= 1024, 1 <= topk <= 32, 0 <= M, M * topk < 2^31 / 64. */
+
+/* ---------------------------------------------------------------------------
+ * Weight preparation (offline, once per weight set).
+ *
+ * Permutes raw MXFP4 weights into the kernel layout.  Raw layouts:
+ *   w13       u8 [E, 2I, D/2]   gate_up codes (rows 0..I-1 gate, I..2I-1 up)
+ *   w13_scale u8 [E, 2I, D/32]  e8m0 scales
+ *   w2        u8 [E, D, I/2]    down codes
+ *   w2_scale  u8 [E, D, I/32]   e8m0 scales
+ * Outputs have exactly the same byte sizes; the mapping is a bijection
+ * (moe_mxfp4_unprepare_weights inverts it).  Inputs and outputs must not
+ * alias.  Prepared layout, per expert, for a matrix with N rows and K columns
+ * (gate_up: N = 2I, K = D; down: N = D, K = I):
+ *   codes  [N/64][K/128][4][64][16 B]: 16-row slice q of 64-row group n64,
+ *          K tile kt (128 elements); lane L holds row n64*64 + q*16 + L%16,
+ *          elements kt*128 + (L/16)*32 .. +32 (the raw 16 bytes).
+ *   scales [N/64][K/(128G)][4][64][G B], G = 4 if K % 512 == 0 else 2: lane
+ *          L's G bytes are the scales of row n64*64+q*16+L%16, 32-blocks
+ *          (kg*G + j)*4 + L/16 for j < G.
+ * For gate_up the rows are first interleaved so that each 64-row group holds
+ * gate rows c*32..c*32+31 followed by up rows I+c*32..I+c*32+31 (group c).
+ * ------------------------------------------------------------------------- */
+int moe_mxfp4_prepare_weights(const uint8_t* w13, const uint8_t* w13_scale,
+                              const uint8_t* w2, const uint8_t* w2_scale,
+                              int E, int D, int I,
+                              uint8_t* w13_out, uint8_t* w13_scale_out,
+                              uint8_t* w2_out, uint8_t* w2_scale_out,
+                              hipStream_t stream);
+
+/* Inverse of moe_mxfp4_prepare_weights (same arguments, prepared -> raw). */
+int moe_mxfp4_unprepare_weights(const uint8_t* w13p, const uint8_t* w13p_scale,
+                                const uint8_t* w2p, const uint8_t* w2p_scale,
+                                int E, int D, int I,
+                                uint8_t* w13_out, uint8_t* w13_scale_out,
+                                uint8_t* w2_out, uint8_t* w2_scale_out,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Forward.
+ *
+ * out[t, :] = bf16( sum_{s < topk, 0 <= e < E} topk_w[t, s] *
+ *                   W2[e] . Q( bf16( silu(Wg[e] . Q(hidden[t])) * (Wu[e] . Q(hidden[t])) ) ) )
+ * with e = topk_ids[t, s], Q = MXFP4 quantization per 32 along K, dot products
+ * of MXFP4 operands accumulated in fp32, the per-token sum over slots in fp32
+ * and one final rounding to bf16.
+ *
+ *   hidden    bf16 [M, D]            activations
+ *   w13..     prepared weights from moe_mxfp4_prepare_weights
+ *   topk_ids  i32  [M, topk]          expert per (token, slot); ids outside
+ *                                     [0, E) contribute nothing; a repeated
+ *                                     id counts once per slot.  A shared
+ *                                     expert is an ordinary id.
+ *   topk_w    f32  [M, topk]          routing weight per (token, slot)
+ *   out       bf16 [M, D]             fully overwritten
+ *   workspace device memory of at least moe_mxfp4_workspace_bytes(...) bytes
+ * M = 0 is a valid no-op.
+ * ------------------------------------------------------------------------- */
+size_t moe_mxfp4_workspace_bytes(int M, int D, int I, int E, int topk);
+
+int moe_mxfp4_forward(const uint16_t* hidden,
+                      const uint8_t* w13, const uint8_t* w13_scale,
+                      const uint8_t* w2, const uint8_t* w2_scale,
+                      const int32_t* topk_ids, const float* topk_w,
+                      uint16_t* out,
+                      int M, int D, int I, int E, int topk,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* The block_m (rows per expert block of the sorted route list) the forward
+ * uses for this shape, and the capacity (rows) of the sorted route list. */
+int moe_mxfp4_block_m(int M, int D, int I, int E, int topk);
+int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m);
+
+/* ---------------------------------------------------------------------------
+ * Single stages, canonical layouts (for tests and for quantizing weights).
+ * ------------------------------------------------------------------------- */
+
+/* MXFP4-quantize a bf16 matrix [rows, cols] (cols % 32 == 0) per 32 along a
+ * row: codes u8 [rows, cols/2], scales u8 [rows, cols/32] (row-major). */
+int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/* Route sort alone: expert-sorted, block_m-padded route lists.  A route is
+ * r = t*topk + s.  Experts appear in ascending order, each expert's routes in
+ * ascending r, padded with the id M*topk (weight 0) to a multiple of block_m.
+ *   sorted_route i32 [cap], sorted_w f32 [cap], block_expert i32 [cap/block_m]
+ *   (-1 past the last used block), num_valid i32 [2] = {padded rows, valid
+ *   routes}; cap = moe_mxfp4_route_capacity(M, E, topk, block_m).
+ * block_m must be 16, 32, 64 or 128. */
+int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w,
+                    int M, int E, int topk, int block_m,
+                    int32_t* sorted_route, float* sorted_w,
+                    int32_t* block_expert, int32_t* num_valid,
+                    hipStream_t stream);
+
+/* Forward that also exports its intermediates (any pointer may be NULL):
+ *   sorted_route i32 [cap], num_valid i32 [2]      the route list it used
+ *   h            bf16 [cap, I]  silu(gate)*up per sorted row, before requant
+ *   a2_codes     u8   [cap, I/2], a2_scales u8 [cap, I/32]  its MXFP4 form
+ * Rows of padding are unspecified.  cap as for moe_mxfp4_route with the
+ * block_m of moe_mxfp4_block_m. */
+int moe_mxfp4_forward_debug(const uint16_t* hidden,
+                            const uint8_t* w13, const uint8_t* w13_scale,
+                            const uint8_t* w2, const uint8_t* w2_scale,
+                            const int32_t* topk_ids, const float* topk_w,
+                            uint16_t* out,
+                            int M, int D, int I, int E, int topk,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t* sorted_route, int32_t* num_valid,
+                            uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,239 @@
+"""ctypes binding of libmoe_mxfp4.so (the C ABI in include/moe_mxfp4.h).
+
+Argument marshalling only: every function takes torch tensors, checks their
+dtype/shape/device, and passes raw device pointers, sizes and the current HIP
+stream to the library function of the same name.  There is no fallback: if
+the library is missing this module raises on import, and a non-zero status
+raises MoeMxfp4Error.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_mxfp4_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+_lib.moe_mxfp4_status_string.argtypes, _lib.moe_mxfp4_status_string.restype = [_I], ctypes.c_char_p
+_lib.moe_mxfp4_workspace_bytes.argtypes = [_I] * 5
+_lib.moe_mxfp4_workspace_bytes.restype = _SZ
+_lib.moe_mxfp4_block_m.argtypes, _lib.moe_mxfp4_block_m.restype = [_I] * 5, _I
+_lib.moe_mxfp4_route_capacity.argtypes = [_I] * 4
+_lib.moe_mxfp4_route_capacity.restype = _I64
+for _name in ("moe_mxfp4_prepare_weights", "moe_mxfp4_unprepare_weights"):
+    getattr(_lib, _name).argtypes = [_P] * 4 + [_I] * 3 + [_P] * 4 + [_P]
+    getattr(_lib, _name).restype = _I
+_lib.moe_mxfp4_forward.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
+_lib.moe_mxfp4_forward.restype = _I
+_lib.moe_mxfp4_forward_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
+_lib.moe_mxfp4_forward_debug.restype = _I
+_lib.moe_mxfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.moe_mxfp4_quantize.restype = _I
+_lib.moe_mxfp4_route.argtypes = [_P, _P] + [_I] * 4 + [_P] * 4 + [_P]
+_lib.moe_mxfp4_route.restype = _I
+
+EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
+           "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
+           "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
+           "moe_mxfp4_quantize", "moe_mxfp4_route")
+
+
+class MoeMxfp4Error(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: status {status}: {moe_mxfp4_status_string(status)}")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeMxfp4Error(fn, status)
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def moe_mxfp4_status_string(status: int) -> str:
+    return _lib.moe_mxfp4_status_string(int(status)).decode()
+
+
+def moe_mxfp4_workspace_bytes(M, D, I, E, topk) -> int:
+    return int(_lib.moe_mxfp4_workspace_bytes(M, D, I, E, topk))
+
+
+def moe_mxfp4_block_m(M, D, I, E, topk) -> int:
+    return int(_lib.moe_mxfp4_block_m(M, D, I, E, topk))
+
+
+def moe_mxfp4_route_capacity(M, E, topk, block_m) -> int:
+    return int(_lib.moe_mxfp4_route_capacity(M, E, topk, block_m))
+
+
+def _weight_dims(w13, w2):
+    E, twoI, Dh = w13.shape
+    return E, Dh * 2, twoI // 2
+
+
+def _weight_ptrs(w13, w13s, w2, w2s, E, D, I, tag):
+    u8 = torch.uint8
+    return (_ptr(w13, u8, (E, 2 * I, D // 2), tag + "w13"),
+            _ptr(w13s, u8, (E, 2 * I, D // 32), tag + "w13_scale"),
+            _ptr(w2, u8, (E, D, I // 2), tag + "w2"),
+            _ptr(w2s, u8, (E, D, I // 32), tag + "w2_scale"))
+
+
+def moe_mxfp4_prepare_weights(w13, w13_scale, w2, w2_scale, w13_out=None, w13_scale_out=None,
+                              w2_out=None, w2_scale_out=None, stream=None):
+    """Raw MXFP4 weights -> kernel layout (same shapes).  Returns the 4 outputs."""
+    E, D, I = _weight_dims(w13, w2)
+    outs = [o if o is not None else torch.empty_like(i)
+            for o, i in zip((w13_out, w13_scale_out, w2_out, w2_scale_out),
+                            (w13, w13_scale, w2, w2_scale))]
+    src = _weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, "")
+    dst = _weight_ptrs(*outs, E, D, I, "out ")
+    _check("moe_mxfp4_prepare_weights",
+           _lib.moe_mxfp4_prepare_weights(*src, E, D, I, *dst, _stream(stream)))
+    return tuple(outs)
+
+
+def moe_mxfp4_unprepare_weights(w13p, w13p_scale, w2p, w2p_scale, stream=None):
+    E, D, I = _weight_dims(w13p, w2p)
+    outs = [torch.empty_like(t) for t in (w13p, w13p_scale, w2p, w2p_scale)]
+    src = _weight_ptrs(w13p, w13p_scale, w2p, w2p_scale, E, D, I, "")
+    dst = _weight_ptrs(*outs, E, D, I, "out ")
+    _check("moe_mxfp4_unprepare_weights",
+           _lib.moe_mxfp4_unprepare_weights(*src, E, D, I, *dst, _stream(stream)))
+    return tuple(outs)
+
+
+def alloc_workspace(M, D, I, E, topk, device="cuda"):
+    n = moe_mxfp4_workspace_bytes(M, D, I, E, topk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace):
+    E, D, I = _weight_dims(w13, w2)
+    M = hidden.shape[0]
+    topk = topk_ids.shape[1]
+    args = (_ptr(hidden, torch.bfloat16, (M, D), "hidden"),
+            *_weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, ""),
+            _ptr(topk_ids, torch.int32, (M, topk), "topk_ids"),
+            _ptr(topk_w, torch.float32, (M, topk), "topk_w"),
+            _ptr(out, torch.bfloat16, (M, D), "out"),
+            M, D, I, E, topk, _ptr(workspace, torch.uint8, None, "workspace"),
+            workspace.numel())
+    return args, (M, D, I, E, topk)
+
+
+def moe_mxfp4_forward(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out=None,
+                      workspace=None, stream=None):
+    """Fused MXFP4 MoE forward on prepared weights; returns out (bf16 [M, D])."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        E, D, I = _weight_dims(w13, w2)
+        workspace = alloc_workspace(hidden.shape[0], D, I, E, topk_ids.shape[1], hidden.device)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward", _lib.moe_mxfp4_forward(*args, _stream(stream)))
+    return out
+
+
+def moe_mxfp4_forward_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out=None,
+                            workspace=None, stream=None):
+    """Forward that also returns its route list and intermediates (canonical layouts):
+    dict(out, sorted_route, num_valid, h, a2_codes, a2_scales, block_m)."""
+    E, D, I = _weight_dims(w13, w2)
+    M, topk = topk_ids.shape
+    dev = hidden.device
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        workspace = alloc_workspace(M, D, I, E, topk, dev)
+    bm = moe_mxfp4_block_m(M, D, I, E, topk)
+    cap = moe_mxfp4_route_capacity(M, E, topk, bm)
+    sr = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    nv = torch.empty(4, dtype=torch.int32, device=dev)
+    h = torch.empty((max(cap, 1), I), dtype=torch.bfloat16, device=dev)
+    a2c = torch.empty((max(cap, 1), I // 2), dtype=torch.uint8, device=dev)
+    a2s = torch.empty((max(cap, 1), I // 32), dtype=torch.uint8, device=dev)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_debug",
+           _lib.moe_mxfp4_forward_debug(*args, _ptr(sr), _ptr(nv), _ptr(h), _ptr(a2c), _ptr(a2s),
+                                        _stream(stream)))
+    return {"out": out, "sorted_route": sr[:cap], "num_valid": nv[:2], "h": h[:cap],
+            "a2_codes": a2c[:cap], "a2_scales": a2s[:cap], "block_m": bm, "cap": cap}
+
+
+def moe_mxfp4_quantize(x, codes=None, scales=None, stream=None):
+    """bf16 [rows, cols] -> (codes u8 [rows, cols/2], scales u8 [rows, cols/32])."""
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_mxfp4_quantize",
+           _lib.moe_mxfp4_quantize(_ptr(x, torch.bfloat16, (rows, cols), "x"), rows, cols,
+                                   _ptr(codes, torch.uint8, (rows, cols // 2), "codes"),
+                                   _ptr(scales, torch.uint8, (rows, cols // 32), "scales"),
+                                   _stream(stream)))
+    return codes, scales
+
+
+def moe_mxfp4_route(topk_ids, topk_w, E, block_m, stream=None):
+    """Route sort alone.  Returns dict(sorted_route, sorted_w, block_expert, num_valid, cap)."""
+    M, topk = topk_ids.shape
+    dev = topk_ids.device
+    cap = moe_mxfp4_route_capacity(M, E, topk, block_m)
+    sr = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    sw = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    be = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    nv = torch.empty(2, dtype=torch.int32, device=dev)
+    _check("moe_mxfp4_route",
+           _lib.moe_mxfp4_route(_ptr(topk_ids, torch.int32, (M, topk), "topk_ids"),
+                                _ptr(topk_w, torch.float32, (M, topk), "topk_w"),
+                                M, E, topk, block_m, _ptr(sr), _ptr(sw), _ptr(be), _ptr(nv),
+                                _stream(stream)))
+    return {"sorted_route": sr[:cap], "sorted_w": sw[:cap], "block_expert": be[:cap // block_m],
+            "num_valid": nv, "cap": cap}
+
+
+class MoeMxfp4:
+    """Holds prepared weights and a workspace; calling it runs the forward."""
+
+    def __init__(self, w13, w13_scale, w2, w2_scale, stream=None):
+        self.E, self.D, self.I = _weight_dims(w13, w2)
+        self.weights = moe_mxfp4_prepare_weights(w13, w13_scale, w2, w2_scale, stream=stream)
+        self._ws = None
+
+    def workspace(self, M, topk, device):
+        n = moe_mxfp4_workspace_bytes(M, self.D, self.I, self.E, topk)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+        return self._ws
+
+    def __call__(self, hidden, topk_ids, topk_w, out=None, stream=None):
+        ws = self.workspace(hidden.shape[0], topk_ids.shape[1], hidden.device)
+        return moe_mxfp4_forward(hidden, *self.weights, topk_ids, topk_w, out=out, workspace=ws,
+                                 stream=stream)

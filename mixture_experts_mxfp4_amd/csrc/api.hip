@@ -1,0 +1,317 @@
+// C ABI of the fused MXFP4 MoE forward (declared in include/moe_mxfp4.h):
+// host-side validation, workspace carving, block_m choice and the launch
+// sequence route sort -> activation quant -> stage 1 -> stage 2 -> finalize,
+// all asynchronous on the caller's stream with no host synchronization (grids
+// are sized for the worst-case route list; blocks past the real one exit).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "moe_kernels.h"
+#include "moe_mxfp4.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopk = 32;
+constexpr int64_t kMaxRoutes = int64_t(1) << 24;
+
+std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Checks that the current device is gfx950; returns its CU count in *n_cu.
+int device_check(int* n_cu)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_MXFP4_ERR_UNSUPPORTED;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        if (st == 1 && moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1) return MOE_MXFP4_ERR_UNSUPPORTED;
+    *n_cu = g_cu_count[dev].load(std::memory_order_relaxed);
+    return MOE_MXFP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool dims_ok(int D, int I)
+{
+    return D >= 256 && I >= 256 && D <= 65536 && I <= 65536 && D % 256 == 0 && I % 256 == 0;
+}
+
+int64_t route_capacity(int M, int E, int topk, int bm)
+{
+    const int64_t R = int64_t(M) * topk;
+    if (R <= 0) return 0;
+    const int64_t cap = R + (E < R ? E : R) * int64_t(bm - 1);
+    return (cap + bm - 1) / bm * bm;
+}
+
+// Rows per expert block.  Few routes per expert (decode, E=257): 16-row
+// blocks waste the least MFMA work on padding; with tens to thousands of
+// routes per expert, larger blocks read each expert's weights fewer times.
+int choose_block_m(int M, int E, int topk)
+{
+    const double avg = double(M) * topk / double(E);
+    if (avg < 8.0) return 16;
+    if (avg < 32.0) return 32;
+    return 64;
+}
+
+struct Layout {
+    int bm;
+    int64_t cap, nb;
+    size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a2q, a2s, acc, total;
+};
+
+Layout layout(int M, int D, int I, int E, int topk)
+{
+    Layout L;
+    L.bm = choose_block_m(M, E, topk);
+    L.cap = route_capacity(M, E, topk, L.bm);
+    L.nb = L.cap / L.bm;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    L.sorted_route = take(sizeof(int32_t) * size_t(L.cap));
+    L.sorted_w = take(sizeof(float) * size_t(L.cap));
+    L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
+    L.num_valid = take(sizeof(int32_t) * 4);
+    L.a1q = take(size_t(M) * D / 2);
+    L.a1s = take(size_t(M) * D / 32);
+    L.a2q = take(size_t(L.cap) * I / 2);
+    L.a2s = take(size_t(L.cap) * I / 32);
+    L.acc = take(sizeof(float) * size_t(M) * D);
+    L.total = off;
+    return L;
+}
+
+int check_shape(int M, int D, int I, int E, int topk)
+{
+    if (M < 0 || E < 1 || topk < 1 || topk > kMaxTopk || !dims_ok(D, I))
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    if (E > kMaxE || int64_t(M) * topk > kMaxRoutes) return MOE_MXFP4_ERR_UNSUPPORTED;
+    return MOE_MXFP4_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_MXFP4_OK : MOE_MXFP4_ERR_HIP; }
+
+struct DebugOut {
+    int32_t* sorted_route;
+    int32_t* num_valid;
+    uint16_t* h;
+    uint8_t* a2_codes;
+    uint8_t* a2_scales;
+};
+
+int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
+                 const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                 const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
+                 void* workspace, size_t workspace_bytes, const DebugOut* dbg,
+                 hipStream_t stream)
+{
+    int st = check_shape(M, D, I, E, topk);
+    if (st) return st;
+    if (M == 0) return MOE_MXFP4_OK;
+    const void* ptrs[] = {hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace};
+    for (const void* p : ptrs)
+        if (!p || !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return MOE_MXFP4_ERR_INVALID_ARG;
+    const Layout L = layout(M, D, I, E, topk);
+    if (workspace_bytes < L.total) return MOE_MXFP4_ERR_WORKSPACE;
+    int n_cu = 0;
+    st = device_check(&n_cu);
+    if (st) return st;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* sorted_route = reinterpret_cast<int32_t*>(ws + L.sorted_route);
+    float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
+    int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
+    int32_t* num_valid = reinterpret_cast<int32_t*>(ws + L.num_valid);
+    uint8_t* a1q = ws + L.a1q;
+    uint8_t* a1s = ws + L.a1s;
+    uint8_t* a2q = ws + L.a2q;
+    uint8_t* a2s = ws + L.a2s;
+    float* acc = reinterpret_cast<float*>(ws + L.acc);
+    const int nb = int(L.nb);
+
+    hipError_t e = moe::launch_route_sort(topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route,
+                                          sorted_w, block_expert, num_valid, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    const int Ga = (D % 512 == 0) ? 4 : 2;
+    e = moe::launch_quant_rows(hidden, M, D, a1q, a1s, Ga, acc, n_cu, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+
+    moe::Gemm1Args g1{a1q, a1s, w13, w13_scale, sorted_route, block_expert, num_valid, a2q, a2s,
+                      dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb};
+    e = moe::launch_gemm1(g1, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+
+    moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
+                      acc, M, D, I, topk, L.bm, nb};
+    e = moe::launch_gemm2(g2, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_finalize(acc, out, int64_t(M) * D, n_cu, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+
+    if (dbg) {
+        if (dbg->sorted_route &&
+            hipMemcpyAsync(dbg->sorted_route, sorted_route, sizeof(int32_t) * size_t(L.cap),
+                           hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+        if (dbg->num_valid && hipMemcpyAsync(dbg->num_valid, num_valid, sizeof(int32_t) * 2,
+                                             hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+        if (dbg->a2_codes || dbg->a2_scales) {
+            e = moe::launch_a2_to_canonical(a2q, a2s, L.cap, I, dbg->a2_codes, dbg->a2_scales,
+                                            stream);
+            if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+        }
+    }
+    return MOE_MXFP4_OK;
+}
+
+}  // namespace
+
+MOE_API const char* moe_mxfp4_status_string(int status)
+{
+    switch (status) {
+    case MOE_MXFP4_OK: return "ok";
+    case MOE_MXFP4_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer or bad size)";
+    case MOE_MXFP4_ERR_UNSUPPORTED: return "unsupported (device is not gfx950 or shape exceeds limits)";
+    case MOE_MXFP4_ERR_WORKSPACE: return "workspace too small";
+    case MOE_MXFP4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+MOE_API int moe_mxfp4_block_m(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk)) return 0;
+    return choose_block_m(M, E, topk);
+}
+
+MOE_API int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m)
+{
+    if (M < 0 || E < 1 || topk < 1 || block_m < 1) return 0;
+    return route_capacity(M, E, topk, block_m);
+}
+
+MOE_API size_t moe_mxfp4_workspace_bytes(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk)) return 0;
+    return layout(M, D, I, E, topk).total;
+}
+
+static int prepare_impl(const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2,
+                        const uint8_t* w2_scale, int E, int D, int I, uint8_t* w13_out,
+                        uint8_t* w13_scale_out, uint8_t* w2_out, uint8_t* w2_scale_out,
+                        int inverse, hipStream_t stream)
+{
+    if (E < 1 || !dims_ok(D, I)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (E > kMaxE) return MOE_MXFP4_ERR_UNSUPPORTED;
+    const void* ptrs[] = {w13, w13_scale, w2, w2_scale, w13_out, w13_scale_out, w2_out, w2_scale_out};
+    for (const void* p : ptrs)
+        if (!p || !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (w13 == w13_out || w2 == w2_out || w13_scale == w13_scale_out || w2_scale == w2_scale_out)
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    int n_cu = 0;
+    int st = device_check(&n_cu);
+    if (st) return st;
+    hipError_t e = moe::launch_prepare(w13, w13_scale, w13_out, w13_scale_out, E, 2 * I, D, I,
+                                       inverse, n_cu, stream);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_prepare(w2, w2_scale, w2_out, w2_scale_out, E, D, I, 0, inverse, n_cu, stream);
+    return hip_status(e);
+}
+
+MOE_API int moe_mxfp4_prepare_weights(const uint8_t* w13, const uint8_t* w13_scale,
+                                      const uint8_t* w2, const uint8_t* w2_scale, int E, int D,
+                                      int I, uint8_t* w13_out, uint8_t* w13_scale_out,
+                                      uint8_t* w2_out, uint8_t* w2_scale_out, hipStream_t stream)
+{
+    return prepare_impl(w13, w13_scale, w2, w2_scale, E, D, I, w13_out, w13_scale_out, w2_out,
+                        w2_scale_out, 0, stream);
+}
+
+MOE_API int moe_mxfp4_unprepare_weights(const uint8_t* w13p, const uint8_t* w13p_scale,
+                                        const uint8_t* w2p, const uint8_t* w2p_scale, int E,
+                                        int D, int I, uint8_t* w13_out, uint8_t* w13_scale_out,
+                                        uint8_t* w2_out, uint8_t* w2_scale_out,
+                                        hipStream_t stream)
+{
+    return prepare_impl(w13p, w13p_scale, w2p, w2p_scale, E, D, I, w13_out, w13_scale_out, w2_out,
+                        w2_scale_out, 1, stream);
+}
+
+MOE_API int moe_mxfp4_forward(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
+                              const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                              const float* topk_w, uint16_t* out, int M, int D, int I, int E,
+                              int topk, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, nullptr, stream);
+}
+
+MOE_API int moe_mxfp4_forward_debug(const uint16_t* hidden, const uint8_t* w13,
+                                    const uint8_t* w13_scale, const uint8_t* w2,
+                                    const uint8_t* w2_scale, const int32_t* topk_ids,
+                                    const float* topk_w, uint16_t* out, int M, int D, int I, int E,
+                                    int topk, void* workspace, size_t workspace_bytes,
+                                    int32_t* sorted_route, int32_t* num_valid, uint16_t* h,
+                                    uint8_t* a2_codes, uint8_t* a2_scales, hipStream_t stream)
+{
+    const void* opt[] = {sorted_route, num_valid, h, a2_codes, a2_scales};
+    for (const void* p : opt)
+        if (p && !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
+    DebugOut d{sorted_route, num_valid, h, a2_codes, a2_scales};
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, &d, stream);
+}
+
+MOE_API int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_MXFP4_OK;
+    if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 4))
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    int n_cu = 0;
+    int st = device_check(&n_cu);
+    if (st) return st;
+    return hip_status(moe::launch_quant_rows(x, rows, cols, codes, scales, 0, nullptr, n_cu, stream));
+}
+
+MOE_API int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w, int M, int E, int topk,
+                            int block_m, int32_t* sorted_route, float* sorted_w,
+                            int32_t* block_expert, int32_t* num_valid, hipStream_t stream)
+{
+    if (M < 0 || E < 1 || topk < 1 || topk > kMaxTopk) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    if (E > kMaxE || int64_t(M) * topk > kMaxRoutes) return MOE_MXFP4_ERR_UNSUPPORTED;
+    const void* ptrs[] = {topk_ids, topk_w, sorted_route, sorted_w, block_expert, num_valid};
+    for (const void* p : ptrs)
+        if (!p || !aligned(p, 4)) return MOE_MXFP4_ERR_INVALID_ARG;
+    int n_cu = 0;
+    int st = device_check(&n_cu);
+    if (st) return st;
+    const int64_t cap = route_capacity(M, E, topk, block_m);
+    return hip_status(moe::launch_route_sort(topk_ids, topk_w, M, topk, E, block_m,
+                                             int(cap / block_m), sorted_route, sorted_w,
+                                             block_expert, num_valid, stream));
+}

@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels of the MXFP4 MoE forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 ---
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
+{
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------ MXFP4 quantizer ---
+//
+// OCP MX v1.0 rule for one 32-element block: X = 2^(floor(log2 amax) - 2),
+// e8m0 byte = floor(log2 amax) - 2 + 127 clamped to [0, 254] (0 for an all-zero
+// block); each element becomes the E2M1 code nearest to |x| / X, ties to the
+// even mantissa, saturating at 6, with the sign bit of x.
+//
+// Inputs are bf16 bit patterns, so everything below is exact: the block
+// maximum is taken on the 15 magnitude bits (monotonic for finite values), the
+// scale byte comes from its exponent field, and |x| / X is rebuilt as
+// significand * 2^p without ever forming an fp32 denormal.
+
+// e8m0 scale byte from the largest |x| (15-bit magnitude pattern) of a block.
+__device__ __forceinline__ uint32_t mx_scale_from_amax(uint32_t amax_mag)
+{
+    uint32_t ea = amax_mag >> 7;              // biased exponent of amax (0: zero/subnormal)
+    return ea >= 2u ? ea - 2u : 0u;           // floor(log2 amax) - 2 + 127, clamped at 0
+}
+
+// E2M1 code of one bf16 element under scale byte s.
+__device__ __forceinline__ uint32_t mx_code(uint32_t bits16, uint32_t s)
+{
+    uint32_t mag = bits16 & 0x7FFFu;
+    uint32_t ex = mag >> 7, man = mag & 0x7Fu;
+    int sig = ex ? int(128u | man) : int(man);
+    int p = (ex ? int(ex) - 134 : -133) + 127 - int(s);        // |x| / X = sig * 2^p
+    float v = 0.0f;
+    if (p >= -30) v = float(sig) * __builtin_bit_cast(float, uint32_t(p + 127) << 23);
+    // round to nearest even onto {0, .5, 1, 1.5, 2, 3, 4, 6}: midpoints
+    // .25 .75 1.25 1.75 2.5 3.5 5, a midpoint going to the even neighbour
+    uint32_t idx = uint32_t(v > 0.25f) + uint32_t(v >= 0.75f) + uint32_t(v > 1.25f) +
+                   uint32_t(v >= 1.75f) + uint32_t(v > 2.5f) + uint32_t(v >= 3.5f) +
+                   uint32_t(v > 5.0f);
+    return idx | ((bits16 >> 12) & 0x8u);
+}
+
+// ------------------------------------------------------------- MFMA -----
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 (format code 4).
+// Lane L supplies 32 E2M1 values (16 bytes) of A row L%16 / B column L%16 at K
+// offsets (L/16)*32 .. +32, and one e8m0 scale byte for that 32-block; lane L
+// receives D[4*(L/16) + i][L%16] in element i.
+__device__ __forceinline__ v4f mfma_fp4_16x16x128(uint4 a, uint4 b, v4f c, uint32_t sa,
+                                                   uint32_t sb)
+{
+    v8i A = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
+    v8i B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, int(sa), 0,
+                                                            int(sb));
+}
+
+// ------------------------------------------------------------- loads ----
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p)
+{
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Non-temporal 16-byte load for single-use weight streams.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const uint8_t* p)
+{
+    v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// G (2 or 4) consecutive scale bytes as one word.
+template <int G>
+__device__ __forceinline__ uint32_t ld_scales(const uint8_t* p)
+{
+    if constexpr (G == 4) return *reinterpret_cast<const uint32_t*>(p);
+    else return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// Position of 32-block kb inside a row of activation scales, grouped so that
+// lane L's G bytes for K tiles kg*G .. kg*G+G-1 are adjacent.
+__device__ __host__ __forceinline__ int act_scale_pos(int kb, int G)
+{
+    return (kb / (4 * G)) * (4 * G) + (kb % 4) * G + (kb / 4) % G;
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe_mxfp4.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+size_t route_lds_bytes(int E);
+hipError_t route_allow_lds(int bytes);   // lift the 64 KiB dynamic-LDS default
+hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int topk, int E, int bm,
+                             int nb_cap, int32_t* sorted_route, float* sorted_w,
+                             int32_t* block_expert, int32_t* num_valid, hipStream_t stream);
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                             uint8_t* scales, int scale_G, float* zero_f32, int n_cu,
+                             hipStream_t stream);
+
+hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
+                          uint8_t* dst_scales, int E, int N, int K, int gate_up_I, int inverse,
+                          int n_cu, hipStream_t stream);
+
+struct Gemm1Args {
+    const uint8_t *a1q, *a1s, *w13p, *w13sp;
+    const int32_t *sorted_route, *block_expert, *num_valid;
+    uint8_t *a2q, *a2s;
+    uint16_t* h_dbg;
+    int M, D, I, topk, block_m, nb_cap;
+};
+hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
+
+hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t rows, int I,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+struct Gemm2Args {
+    const uint8_t *a2q, *a2s, *w2p, *w2sp;
+    const int32_t* sorted_route;
+    const float* sorted_w;
+    const int32_t *block_expert, *num_valid;
+    float* acc;
+    int M, D, I, topk, block_m, nb_cap;
+};
+hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
+
+hipError_t launch_finalize(const float* acc, uint16_t* out, int64_t n, int n_cu,
+                           hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,110 @@
+"""The C-ABI library loads and exports every declared symbol; host-side sizing
+and validation behave as documented.  No kernel is launched (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+
+@pytest.fixture(scope="module")
+def binding():
+    from mixture_experts_mxfp4_amd import binding as b
+    return b
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_mxfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_mxfp4_prepare_weights", "moe_mxfp4_forward",
+                     "moe_mxfp4_workspace_bytes", "moe_mxfp4_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(binding):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+    assert set(binding.EXPORTS) == set(declared_functions())
+
+
+def test_library_links_no_torch(binding):
+    out = subprocess.run(["ldd", binding.LIB_PATH], capture_output=True, text=True).stdout
+    assert "torch" not in out and "c10" not in out
+
+
+def test_status_strings(binding):
+    for s in range(5):
+        assert binding.moe_mxfp4_status_string(s)
+    assert binding.moe_mxfp4_status_string(99) == "unknown status"
+
+
+def test_block_m_and_capacity(binding):
+    assert binding.moe_mxfp4_block_m(16, 7168, 256, 257, 9) == 16
+    assert binding.moe_mxfp4_block_m(64, 7168, 2048, 33, 9) == 32
+    assert binding.moe_mxfp4_block_m(4096, 7168, 2048, 33, 9) == 64
+    assert binding.moe_mxfp4_block_m(16, 7168, 100, 257, 9) == 0       # I % 256 != 0
+    for M, E, k, bm in [(16, 257, 9, 16), (1, 1, 1, 16), (4096, 33, 9, 64), (3, 500, 2, 32)]:
+        cap = binding.moe_mxfp4_route_capacity(M, E, k, bm)
+        assert cap % bm == 0
+        # every expert with n routes pads to ceil(n/bm)*bm: worst case bounded by cap
+        assert cap >= M * k + min(E, M * k) * (bm - 1)
+    assert binding.moe_mxfp4_route_capacity(0, 8, 2, 16) == 0
+
+
+def test_workspace_bytes(binding):
+    assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 257, 9) > 16 * 7168 * 4
+    assert binding.moe_mxfp4_workspace_bytes(16, 7000, 256, 257, 9) == 0
+    assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 2000, 9) == 0     # E > 1024
+
+
+def test_host_validation_without_device(binding):
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    lib.moe_mxfp4_forward.argtypes = binding._lib.moe_mxfp4_forward.argtypes
+    lib.moe_mxfp4_forward.restype = ctypes.c_int
+    null = ctypes.c_void_p(0)
+    # null pointers with M > 0 -> invalid argument, before touching the device
+    assert lib.moe_mxfp4_forward(*([null] * 8), 4, 512, 256, 9, 3, null, 1 << 30, null) == 1
+    # bad dims
+    assert lib.moe_mxfp4_forward(*([null] * 8), 4, 500, 256, 9, 3, null, 1 << 30, null) == 1
+    assert lib.moe_mxfp4_forward(*([null] * 8), 4, 512, 256, 0, 3, null, 1 << 30, null) == 1
+    assert lib.moe_mxfp4_forward(*([null] * 8), 4, 512, 256, 9, 33, null, 1 << 30, null) == 1
+    # M = 0 is a no-op
+    assert lib.moe_mxfp4_forward(*([null] * 8), 0, 512, 256, 9, 3, null, 0, null) == 0
+    # misaligned pointers
+    fake = ctypes.c_void_p(0x1000 + 8)
+    ok = ctypes.c_void_p(0x1000)
+    args = [fake] + [ok] * 7
+    assert lib.moe_mxfp4_forward(*args, 4, 512, 256, 9, 3, ok, 1 << 30, null) == 1
+    # workspace too small
+    args = [ok] * 8
+    assert lib.moe_mxfp4_forward(*args, 4, 512, 256, 9, 3, ok, 16, null) == 3
+    lib.moe_mxfp4_quantize.argtypes = binding._lib.moe_mxfp4_quantize.argtypes
+    assert lib.moe_mxfp4_quantize(ok, 4, 33, ok, ok, null) == 1
+    lib.moe_mxfp4_route.argtypes = binding._lib.moe_mxfp4_route.argtypes
+    assert lib.moe_mxfp4_route(ok, ok, 4, 8, 2, 24, ok, ok, ok, ok, null) == 1    # block_m 24
+    lib.moe_mxfp4_prepare_weights.argtypes = binding._lib.moe_mxfp4_prepare_weights.argtypes
+    assert lib.moe_mxfp4_prepare_weights(*([ok] * 4), 2, 512, 256, *([null] * 4), null) == 1
+    # in-place (aliasing) prepare is rejected
+    assert lib.moe_mxfp4_prepare_weights(*([ok] * 4), 2, 512, 256, *([ok] * 4), null) == 1
+
+
+def test_binding_refuses_wrong_dtypes(binding):
+    import torch
+    h = torch.zeros(2, 512, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        binding._ptr(h, torch.bfloat16, (2, 512), "hidden")

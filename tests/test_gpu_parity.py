@@ -1,0 +1,287 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Bit-exact: MXFP4 codes/scales (activation quantizer, fused stage-1 requant),
+route lists, weight preparation.  Floating point: the end-to-end tolerance
+|gpu - oracle| <= 2e-2 rms + 2^-7 |oracle| on >= 99.9 % of elements, none
+beyond 0.1 rms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_mxfp4_amd import inputs
+from tests.moe_cases import Case, bf16_to_f64, check_close, custom_case, log, workload_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def binding(gpu_device):
+    from mixture_experts_mxfp4_amd import binding as b
+    return b
+
+
+# ------------------------------------------------------------- quantizer ---
+
+def _adversarial_rows(cols, rng):
+    rows = []
+    for scale in (2.0 ** -130, 2.0 ** -125, 2.0 ** -20, 1.0, 2.0 ** 40, 2.0 ** 120):
+        x = rng.standard_normal(cols) * scale
+        rows.append(x)
+        t = np.round(rng.standard_normal(cols) * 8) / 4 * scale      # exact midpoints
+        rows.append(t)
+    z = np.zeros(cols)
+    z[1::3] = -0.0
+    rows.append(z)
+    sat = np.full(cols, 1.875)
+    sat[::2] = -1.75
+    rows.append(sat)
+    return np.stack(rows)
+
+
+def _f32_to_bf16_bits(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (13, 512), (64, 7168), (257, 2048)])
+def test_quantize_bit_exact(binding, rows, cols):
+    log(f"quantize rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-30, 30, (rows, 1)))
+    if rows >= 13:
+        adv = _adversarial_rows(cols, rng)
+        x[: adv.shape[0]] = adv[: rows]
+    bits = _f32_to_bf16_bits(x)
+    codes, scales = binding.moe_mxfp4_quantize(inputs.bits_to_bf16(bits).cuda())
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_rows(bits)
+    np.testing.assert_array_equal(scales.cpu().numpy(), os_)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc)
+
+
+def test_quantize_weights_of_decode_bit_exact(binding):
+    """The product quantizer on the decode workload's full gate_up weight."""
+    w = inputs.WORKLOADS["decode"]
+    log("quantize decode weights (257 x 512 x 7168)")
+    w13f, _ = inputs.make_weights(w.E, w.D, w.I, w.seed, device="cuda")
+    flat = w13f.reshape(-1, w.D)
+    codes, scales = binding.moe_mxfp4_quantize(flat)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_rows(inputs.bf16_bits(flat))
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+# ----------------------------------------------------------------- route ---
+
+def _route_cases():
+    out = []
+    for name, w in inputs.WORKLOADS.items():
+        out.append((name, w.M, w.E, w.n_routed, w.routing, w.seed))
+    return out
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("case", _route_cases(), ids=lambda c: c[0])
+def test_route_matches_oracle(binding, case, bm):
+    name, M, E, n_routed, routing, seed = case
+    log(f"route {name} bm={bm}")
+    _, ids, tw = inputs.make_activations(M, 256, E, n_routed, routing, seed)
+    got = binding.moe_mxfp4_route(ids.cuda(), tw.cuda(), E, bm)
+    torch.cuda.synchronize()
+    want = oracle.route(ids.numpy(), tw.numpy(), E, bm)
+    n = int(want["num_valid"][0])
+    np.testing.assert_array_equal(got["num_valid"].cpu().numpy(), want["num_valid"])
+    np.testing.assert_array_equal(got["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+    np.testing.assert_array_equal(got["sorted_w"].cpu().numpy()[:n], want["sorted_w"])
+    be = got["block_expert"].cpu().numpy()
+    np.testing.assert_array_equal(be[: n // bm], want["block_expert"])
+    assert np.all(be[n // bm:] == -1)
+
+
+@pytest.mark.parametrize("M,E,k,bm", [(1, 1, 1, 16), (5, 3, 4, 16), (300, 7, 5, 32),
+                                      (2000, 1024, 8, 16), (513, 64, 32, 64)])
+def test_route_edge_cases(binding, M, E, k, bm):
+    """Invalid ids (-1, E, large), duplicates within a row, one hot expert."""
+    log(f"route edge M={M} E={E} k={k} bm={bm}")
+    rng = np.random.default_rng(M + E)
+    ids = rng.integers(-2, E + 2, (M, k)).astype(np.int32)
+    ids[:, 0] = 0                                   # a hot expert
+    if k > 1:
+        ids[::3, 1] = ids[::3, 0]                   # duplicates
+    ids[::7, -1] = 1 << 20
+    tw = rng.random((M, k)).astype(np.float32)
+    got = binding.moe_mxfp4_route(torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), E, bm)
+    torch.cuda.synchronize()
+    want = oracle.route(ids, tw, E, bm)
+    n = int(want["num_valid"][0])
+    np.testing.assert_array_equal(got["num_valid"].cpu().numpy(), want["num_valid"])
+    np.testing.assert_array_equal(got["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+    np.testing.assert_array_equal(got["sorted_w"].cpu().numpy()[:n], want["sorted_w"])
+    np.testing.assert_array_equal(got["block_expert"].cpu().numpy()[: n // bm],
+                                  want["block_expert"])
+
+
+# --------------------------------------------------------------- prepare ---
+
+def _layout_reference(raw_codes, raw_scales, N, K, gate_up_I):
+    """The documented prepared layout, rebuilt with numpy for one expert."""
+    rows = np.arange(N)
+    if gate_up_I:
+        c, q, j = rows // 64, (rows % 64) // 16, rows % 16
+        perm = np.where(q < 2, 0, gate_up_I) + c * 32 + (q & 1) * 16 + j
+    else:
+        perm = rows
+    KT = K // 128
+    G = 4 if K % 512 == 0 else 2
+    codes = raw_codes[perm]                              # prepared row order [N, K/2]
+    # [N/64, 4, 16, KT, 4(k-chunk), 16B] -> [N/64, KT, 4, (k-chunk, 16 rows), 16B]
+    t = codes.reshape(N // 64, 4, 16, KT, 4, 16).transpose(0, 3, 1, 4, 2, 5)
+    pc = t.reshape(-1)
+    sc = raw_scales[perm]                                 # [N, K/32]
+    s = sc.reshape(N // 64, 4, 16, KT // G, G, 4).transpose(0, 3, 1, 5, 2, 4)
+    ps = s.reshape(-1)
+    return pc, ps
+
+
+@pytest.mark.parametrize("E,D,I", [(3, 512, 256), (2, 768, 768), (1, 7168, 2048)])
+def test_prepare_layout_and_round_trip(binding, E, D, I):
+    log(f"prepare E={E} D={D} I={I}")
+    rng = np.random.default_rng(D + I)
+    raw = [rng.integers(0, 256, s).astype(np.uint8)
+           for s in ((E, 2 * I, D // 2), (E, 2 * I, D // 32), (E, D, I // 2), (E, D, I // 32))]
+    dev = [torch.from_numpy(a).cuda() for a in raw]
+    prep = binding.moe_mxfp4_prepare_weights(*dev)
+    back = binding.moe_mxfp4_unprepare_weights(*prep)
+    torch.cuda.synchronize()
+    for a, b in zip(raw, back):
+        np.testing.assert_array_equal(b.cpu().numpy(), a)
+    p = [t.cpu().numpy() for t in prep]
+    for e in range(E):
+        pc, ps = _layout_reference(raw[0][e], raw[1][e], 2 * I, D, I)
+        np.testing.assert_array_equal(p[0][e].reshape(-1), pc)
+        np.testing.assert_array_equal(p[1][e].reshape(-1), ps)
+        pc, ps = _layout_reference(raw[2][e], raw[3][e], D, I, 0)
+        np.testing.assert_array_equal(p[2][e].reshape(-1), pc)
+        np.testing.assert_array_equal(p[3][e].reshape(-1), ps)
+
+
+# --------------------------------------------------------------- forward ---
+
+def _check_intermediates(case, dbg):
+    """h per sorted row against the oracle's h; the fused requant bit-exact
+    against the oracle quantizer applied to the GPU's own h."""
+    sr = dbg["sorted_route"].cpu().numpy()
+    n = int(dbg["num_valid"].cpu().numpy()[0])
+    bm = dbg["block_m"]
+    want_route = oracle.route(case.ids, case.tw, case.E, bm)
+    np.testing.assert_array_equal(sr[:n], want_route["sorted_route"])
+    valid = np.nonzero(sr[:n] < case.M * case.topk)[0]
+    h_gpu = dbg["h"].cpu().view(torch.int16).numpy().view(np.uint16)[valid]
+    _, h_or = case.run_oracle(want_h=True)
+    r = sr[valid]
+    h_ref = h_or[r // case.topk, r % case.topk]
+    g, o = bf16_to_f64(h_gpu), bf16_to_f64(h_ref)
+    rms = float(np.sqrt(np.mean(o * o)))
+    assert np.all(np.abs(g - o) <= 2.0 ** -6 * np.abs(o) + 1e-3 * rms)
+    exact = float(np.mean(h_gpu == h_ref))
+    log(f"h exact-bits fraction {exact:.4f}")
+    assert exact >= 0.95
+    codes, scales = oracle.quantize_rows(h_gpu)
+    np.testing.assert_array_equal(dbg["a2_scales"].cpu().numpy()[valid], scales)
+    np.testing.assert_array_equal(dbg["a2_codes"].cpu().numpy()[valid], codes)
+
+
+def test_forward_tiny_full_and_intermediates(binding):
+    case = workload_case("tiny")
+    dbg = case.run_gpu(debug=True)
+    out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(out, case.run_oracle(), "tiny")
+    _check_intermediates(case, dbg)
+
+
+@pytest.mark.parametrize("name,n_sample", [("decode", 16), ("small_batch", 24),
+                                           ("prefill", 48), ("large_prefill", 16)])
+def test_forward_workload_sampled(binding, name, n_sample):
+    case = workload_case(name)
+    out = case.run_gpu()
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([[0, case.M - 1],
+                                     rng.choice(case.M, min(n_sample, case.M), replace=False)]))
+    log(f"{name}: oracle on {toks.size} tokens")
+    want = case.run_oracle(tokens=toks)
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)[toks]
+    check_close(got, want, name)
+    full = out.cpu().float()
+    assert torch.isfinite(full).all()
+
+
+@pytest.mark.parametrize("M,D,I,E,n_routed,seed", [
+    (1, 512, 256, 9, 2, 21),          # single token
+    (37, 768, 768, 5, 3, 22),         # ragged M, D and I not multiples of 512
+    (130, 1024, 512, 33, 8, 23),      # several blocks per expert
+    (3, 256, 256, 2, 1, 24),          # smallest dims
+])
+def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
+    log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
+    case = custom_case(M, D, I, E, n_routed, seed)
+    dbg = case.run_gpu(debug=True)
+    out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(out, case.run_oracle(), f"shape M={M} D={D} I={I} E={E}")
+    _check_intermediates(case, dbg)
+
+
+def test_forward_invalid_and_duplicate_ids(binding):
+    M, D, I, E = 20, 512, 256, 6
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, E, (M, 4)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]            # duplicate slot
+    ids[::2, 2] = -1                 # invalid
+    ids[1::4, 3] = E + 3             # invalid
+    tw = rng.random((M, 4)).astype(np.float32)
+    case = custom_case(M, D, I, E, 2, 31, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
+    out = case.run_gpu().cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(out, case.run_oracle(), "invalid/duplicate ids")
+
+
+def test_forward_all_tokens_one_expert(binding):
+    """Every token routed to expert 0 (many blocks of one expert) plus the shared one."""
+    M, D, I, E = 300, 512, 512, 4
+    ids = np.zeros((M, 2), np.int32)
+    ids[:, 1] = E - 1
+    tw = np.ones((M, 2), np.float32)
+    tw[:, 0] = 0.25
+    case = custom_case(M, D, I, E, 1, 41, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
+    out = case.run_gpu().cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(out, case.run_oracle(), "one hot expert")
+
+
+def test_forward_no_valid_routes(binding):
+    M, D, I, E = 4, 512, 256, 3
+    ids = np.full((M, 2), -1, np.int32)
+    tw = np.ones((M, 2), np.float32)
+    case = custom_case(M, D, I, E, 1, 51, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
+    out = case.run_gpu()
+    assert torch.all(out.cpu().float() == 0)
+
+
+def test_forward_m_zero(binding):
+    E, D, I = 2, 512, 256
+    w = [torch.zeros(s, dtype=torch.uint8, device="cuda")
+         for s in ((E, 2 * I, D // 2), (E, 2 * I, D // 32), (E, D, I // 2), (E, D, I // 32))]
+    h = torch.zeros((0, D), dtype=torch.bfloat16, device="cuda")
+    out = binding.moe_mxfp4_forward(h, *w, torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                                    torch.zeros((0, 2), dtype=torch.float32, device="cuda"),
+                                    workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert out.shape == (0, D)
+
+
+def test_forward_repeatable(binding):
+    """Two calls on one workspace give the same output within fp32-atomic order noise."""
+    case = workload_case("tiny")
+    a = case.run_gpu().cpu().float()
+    b = case.run_gpu().cpu().float()
+    rms = float(a.pow(2).mean().sqrt())
+    assert float((a - b).abs().max()) <= 2.0 ** -7 * float(a.abs().max()) + 1e-6 * rms
