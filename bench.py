@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MXFP4 MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step = one full forward (prologue = route sort + activation quant, stage 1,
+stage 2, per-token slot reduction) through the C ABI on a seeded synthetic DeepSeek-R1-shaped batch
+whose inputs are already resident in HBM.  Prepared weights are kept in
+several copies and rotated step by step, so that every forward streams its
+experts' weights from HBM rather than from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: the metric (algorithmic GB/s for M <= 16 workloads,
+TFLOP/s for M >= 1024), microseconds per forward, the roofline of the dominant
+kernel (stage 1) timed with HIP events on the launch stream inside the timed
+region, and the CPU oracle timed on a bounded sample of the same workload.
+
+Helper modes (used to make the committed rocprofv3 summaries):
+    --copy-calibration         run a plain 1 GiB device copy (counter scale)
+    --summarize-stats DIR      print the kernel-time summary of a rocprofv3 run
+    --summarize-pmc DIR        print per-kernel counter means of a --pmc run
+"""
+import argparse
+import csv
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/forward + HBM GB/s (M≤16) / MXFP4 MFMA TFLOPS (M≥1024), D=7168"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA
+MALL_BYTES = 256 << 20
+STAGE1_KERNEL = "gemm1_swiglu_quant_kernel"
+STAGE1_SOURCES = ("mixture_experts_mxfp4_amd/csrc/gemm1.hip",
+                  "mixture_experts_mxfp4_amd/csrc/moe_common.h")
+
+
+# ---------------------------------------------------------------- helpers ---
+
+def _hip():
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            lib = ctypes.CDLL(name)
+            break
+        except OSError:
+            continue
+    else:
+        raise RuntimeError("libamdhip64.so not found")
+    lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class Events:
+    """Raw hipEvent_t handles created through the HIP runtime.  They are
+    created without the system-scope fence, which otherwise adds several
+    microseconds of idle time at every record between two kernels."""
+
+    def __init__(self, n):
+        self.hip = _hip()
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h),
+                                                    HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[a]),
+                                            ctypes.c_void_p(self.ev[b])) == 0
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w, ids_np, tokens=None):
+    """Algorithmic bytes / FLOPs of a forward over `tokens` (default all):
+    the active experts' weights and scales (1.59375*I*D bytes each: w13 codes
+    I*D + scales I*D/16, w2 codes I*D/2 + scales I*D/32), hidden and output
+    (2*M*D bytes each), ids and weights (8*M*topk); 6*I*D FLOPs per valid
+    (token, slot).  Stage 1 alone: 1.0625*I*D bytes per active expert,
+    4*I*D FLOPs per valid (token, slot)."""
+    import numpy as np
+    ids = ids_np if tokens is None else ids_np[tokens]
+    M, k = ids.shape
+    valid = (ids >= 0) & (ids < w.E)
+    n_active = len(np.unique(ids[valid]))
+    n_valid = int(valid.sum())
+    ID = w.I * w.D
+    return {
+        "n_active": n_active, "n_valid": n_valid,
+        "bytes": n_active * ID * 1.59375 + 4.0 * M * w.D + 8.0 * M * k,
+        "flops": 6.0 * ID * n_valid,
+        "stage1_bytes": n_active * ID * 1.0625,
+        "stage1_flops": 4.0 * ID * n_valid,
+    }
+
+
+def load_traffic(workload):
+    """HBM traffic of the stage-1 kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current stage-1 source; else None."""
+    path = os.path.join(ROOT, "profiles", f"stage1_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("stage1_source_sha256_16") != source_hash(STAGE1_SOURCES):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------- CPU leg ---
+
+def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0):
+    """The CPU oracle on a bounded sample of the same workload (its first
+    tokens), weights quantized by the oracle itself (untimed, like the GPU's
+    weight preparation)."""
+    import numpy as np
+
+    import oracle
+    from mixture_experts_mxfp4_amd import inputs
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    per_tok_cpu_s = 16e-9 * 3 * w.I * w.D * w.topk         # measured oracle cost ~16 ns/MAC
+    n = int(max(1, min(w.M, round(target_cpu_s / per_tok_cpu_s))))
+    toks = np.arange(n)
+    ids_np = ids.numpy()
+    used = np.unique(ids_np[toks][(ids_np[toks] >= 0) & (ids_np[toks] < w.E)])
+    remap = np.full(w.E, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    sub_ids = np.where((ids_np >= 0) & (ids_np < w.E), remap[np.clip(ids_np, 0, w.E - 1)], -1)
+    sub_ids = sub_ids.astype(np.int32)
+    sel = torch_index(used)
+    w13, w13s = oracle.quantize_rows(inputs.bf16_bits(w13f[sel]).reshape(-1, w.D), threads)
+    w2, w2s = oracle.quantize_rows(inputs.bf16_bits(w2f[sel]).reshape(-1, w.I), threads)
+    Eu = used.size
+    wq = (w13.reshape(Eu, 2 * w.I, w.D // 2), w13s.reshape(Eu, 2 * w.I, w.D // 32),
+          w2.reshape(Eu, w.D, w.I // 2), w2s.reshape(Eu, w.D, w.I // 32))
+    hb = inputs.bf16_bits(hidden)
+    t0 = time.perf_counter()
+    oracle.forward(hb, *wq, sub_ids, tw.numpy(), tokens=toks, nthreads=threads)
+    dt = time.perf_counter() - t0
+    alg = algorithmic(w, ids_np, toks)
+    return {"seconds": dt, "tokens": n, "threads": threads, "alg": alg}
+
+
+def torch_index(np_idx):
+    import torch
+    return torch.from_numpy(np_idx.astype("int64"))
+
+
+# ------------------------------------------------------------- GPU leg ----
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from mixture_experts_mxfp4_amd import binding, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hidden, ids, tw = inputs.make_activations(w.M, w.D, w.E, w.n_routed, w.routing, w.seed)
+    w13f, w2f = inputs.make_weights(w.E, w.D, w.I, w.seed, device=dev)
+
+    # MXFP4 weights from the library's own quantizer, then the kernel layout
+    raw = [binding.moe_mxfp4_quantize(w13f.reshape(-1, w.D)),
+           binding.moe_mxfp4_quantize(w2f.reshape(-1, w.I))]
+    w13 = raw[0][0].view(w.E, 2 * w.I, w.D // 2)
+    w13s = raw[0][1].view(w.E, 2 * w.I, w.D // 32)
+    w2 = raw[1][0].view(w.E, w.D, w.I // 2)
+    w2s = raw[1][1].view(w.E, w.D, w.I // 32)
+    prepared = binding.moe_mxfp4_prepare_weights(w13, w13s, w2, w2s)
+    del raw, w13, w13s, w2, w2s
+    ids_np = ids.numpy()
+    alg = algorithmic(w, ids_np)
+    per_copy_active = alg["n_active"] * w.I * w.D * 1.59375
+    copies = args.copies or int(max(2, min(8, np.ceil(3 * (MALL_BYTES + (64 << 20)) / per_copy_active))))
+    weight_sets = [prepared] + [tuple(t.clone() for t in prepared) for _ in range(copies - 1)]
+
+    h_d, ids_d, tw_d = hidden.to(dev), ids.to(dev), tw.to(dev)
+    out = torch.empty_like(h_d)
+    ws = binding.alloc_workspace(w.M, w.D, w.I, w.E, w.topk, dev)
+    torch.cuda.synchronize()
+
+    # untimed warm-up; the last warm-up pass also records every stage boundary
+    stage_ev = Events(5)
+    for i in range(args.warmup):
+        ev = stage_ev.ev if i == args.warmup - 1 else [None] * 5
+        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
+    torch.cuda.synchronize()
+    stages_us = None
+    if args.warmup > 0:
+        names = ["prologue", "stage1", "stage2", "reduce"]
+        stages_us = {n: round(1000 * stage_ev.ms(j, j + 1), 2) for j, n in enumerate(names)}
+
+    # timed region: exactly K forwards; HIP events bracket stage 1 of every step
+    step_ev = Events(2 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev = [None, step_ev.ev[2 * i], step_ev.ev[2 * i + 1], None, None]
+        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = 1000.0 * (t1 - t0) / args.steps
+    stage1_ms = sum(step_ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+    step_ev.close()
+    stage_ev.close()
+
+    sec = ms_per_step / 1000.0
+    # roofline: which peak bounds the whole forward of this workload
+    hbm_bound = alg["bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)
+    if hbm_bound:
+        value, unit = alg["bytes"] / sec / 1e9, "GB/s"
+        achieved = alg["stage1_bytes"] / (stage1_ms / 1000.0) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        value, unit = alg["flops"] / sec / 1e12, "TFLOP/s"
+        achieved = alg["stage1_flops"] / (stage1_ms / 1000.0) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4)}
+    roof["traffic"] = load_traffic(args.workload)
+    roof["kernel"] = STAGE1_KERNEL
+    roof["kernel_us"] = round(stage1_ms * 1000.0, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, hidden, ids, tw, w13f, w2f, args.cpu_sample_s)
+        ca = cb["alg"]
+        cval = ca["bytes"] / cb["seconds"] / 1e9 if hbm_bound else ca["flops"] / cb["seconds"] / 1e12
+        cpu = {"value": round(cval, 4), "unit": unit, "cores": cb["threads"], "kind": "oracle",
+               "sample": f"first {cb['tokens']} of {w.M} tokens of the {w.name} workload "
+                         f"({cb['seconds']:.2f} s wall, fp64 C oracle, {cb['threads']} threads)"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3 if unit == "TFLOP/s" else 1),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: M={w.M} D={w.D} I={w.I} E={w.E} top{w.topk} "
+                               f"({w.n_routed} routed {w.routing} + shared expert {w.E - 1})",
+                   "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
+                   "routing": w.routing, "seed": w.seed, "global_batch": w.M,
+                   "parallelism": "single GPU", "block_m": binding.moe_mxfp4_block_m(
+                       w.M, w.D, w.I, w.E, w.topk), "weight_copies": copies},
+        "us_per_forward": round(ms_per_step * 1000.0, 2),
+        "tokens_per_s": round(w.M / sec, 1),
+        "hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
+        "mfma_tflops": round(alg["flops"] / sec / 1e12, 3),
+        "roofline_frac_forward": round(max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
+                                           alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)) / sec, 4),
+        "active_experts": alg["n_active"],
+        "stage_us_warmup": stages_us,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line, ensure_ascii=False), flush=True)
+
+
+# ------------------------------------------------------- profiling helpers ---
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
+
+
+def _rows(pattern):
+    files = sorted(glob.glob(pattern, recursive=True))
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def summarize_stats(d):
+    rows = _rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    print(f"{'kernel':80s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        name = r.get("Name", "")[:80]
+        print(f"{name:80s} {r.get('Calls', ''):>6s} {float(r.get('AverageNs', 0)) / 1000:10.2f} "
+              f"{float(r.get('MinNs', 0)) / 1000:10.2f} {float(r.get('MaxNs', 0)) / 1000:10.2f} "
+              f"{float(r.get('Percentage', 0)):6.2f}")
+
+
+def summarize_pmc(d):
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in rows:
+        key = (r.get("Kernel_Name", "")[:80], r.get("Counter_Name", ""))
+        acc.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    print(f"{'kernel':80s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
+    for (k, c), v in sorted(acc.items()):
+        print(f"{k:80s} {c:>12s} {len(v):10d} {sum(v) / len(v):18.1f}")
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode",
+                   choices=["tiny", "decode", "small_batch", "prefill", "large_prefill"])
+    p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-s", type=float, default=16.0,
+                   help="CPU-seconds of oracle work in the baseline sample")
+    p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--summarize-stats", metavar="DIR")
+    p.add_argument("--summarize-pmc", metavar="DIR")
+    args = p.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported.", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.steps < 1:
+        p.error("--steps must be >= 1")
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device and must
- *    be 256-byte aligned.  bf16 tensors are passed as uint16_t bit patterns.
+ *    be 16-byte aligned (the forward's workspace 256-byte aligned).  bf16
+ *    tensors are passed as uint16_t bit patterns.
  *  - The caller owns every buffer, including the workspace.  The library keeps
  *    no pointer after a call returns and allocates no device memory.
  *  - Work is enqueued asynchronously on `stream`; nothing synchronizes with the
@@ -57,7 +58,7 @@ const char* moe_mxfp4_status_string(int status);
 
 /* Limits of this implementation (host-validated):
  *   D, I: multiples of 256, 256 <= D, I <= 65536
- *   1 <= E <= 1024, 1 <= topk <= 32, 0 <= M, M * topk < 2^31 / 64. */
+ *   1 <= E <= 1024, 1 <= topk <= 32, 0 <= M, M * topk <= 2^24. */
 
 /* ---------------------------------------------------------------------------
  * Weight preparation (offline, once per weight set).
@@ -101,8 +102,9 @@ int moe_mxfp4_unprepare_weights(const uint8_t* w13p, const uint8_t* w13p_scale,
  * out[t, :] = bf16( sum_{s < topk, 0 <= e < E} topk_w[t, s] *
  *                   W2[e] . Q( bf16( silu(Wg[e] . Q(hidden[t])) * (Wu[e] . Q(hidden[t])) ) ) )
  * with e = topk_ids[t, s], Q = MXFP4 quantization per 32 along K, dot products
- * of MXFP4 operands accumulated in fp32, the per-token sum over slots in fp32
- * and one final rounding to bf16.
+ * of MXFP4 operands accumulated in fp32; each weighted expert contribution
+ * rounded to bf16, the per-token sum over slots in fp32 in slot order and one
+ * final rounding to bf16 (deterministic).
  *
  *   hidden    bf16 [M, D]            activations
  *   w13..     prepared weights from moe_mxfp4_prepare_weights
@@ -169,6 +171,22 @@ int moe_mxfp4_forward_debug(const uint16_t* hidden,
                             int32_t* sorted_route, int32_t* num_valid,
                             uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
                             hipStream_t stream);
+
+/* Forward that records caller-created HIP events on `stream` at the stage
+ * boundaries, for timing: stage_events[0] before the prologue (route sort and
+ * activation quant, one launch), [1] after it, [2] after stage 1 (gate_up +
+ * SwiGLU + requant), [3] after stage 2 (down projection x routing weight),
+ * [4] after the per-token sum over slots.  Any entry (or the array) may be
+ * NULL.  The events are only recorded; the caller reads them after
+ * synchronizing. */
+int moe_mxfp4_forward_profiled(const uint16_t* hidden,
+                               const uint8_t* w13, const uint8_t* w13_scale,
+                               const uint8_t* w2, const uint8_t* w2_scale,
+                               const int32_t* topk_ids, const float* topk_w,
+                               uint16_t* out,
+                               int M, int D, int I, int E, int topk,
+                               void* workspace, size_t workspace_bytes,
+                               hipEvent_t* stage_events, hipStream_t stream);
 
 #ifdef __cplusplus
 }

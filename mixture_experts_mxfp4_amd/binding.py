@@ -33,6 +33,8 @@ _lib.moe_mxfp4_forward.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
 _lib.moe_mxfp4_forward.restype = _I
 _lib.moe_mxfp4_forward_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
 _lib.moe_mxfp4_forward_debug.restype = _I
+_lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P]
+_lib.moe_mxfp4_forward_profiled.restype = _I
 _lib.moe_mxfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.moe_mxfp4_quantize.restype = _I
 _lib.moe_mxfp4_route.argtypes = [_P, _P] + [_I] * 4 + [_P] * 4 + [_P]
@@ -41,7 +43,7 @@ _lib.moe_mxfp4_route.restype = _I
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
            "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
-           "moe_mxfp4_quantize", "moe_mxfp4_route")
+           "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -157,6 +159,19 @@ def moe_mxfp4_forward(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ou
         workspace = alloc_workspace(hidden.shape[0], D, I, E, topk_ids.shape[1], hidden.device)
     args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
     _check("moe_mxfp4_forward", _lib.moe_mxfp4_forward(*args, _stream(stream)))
+    return out
+
+
+def moe_mxfp4_forward_profiled(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out,
+                               workspace, stage_events, stream=None):
+    """Forward recording HIP events (raw hipEvent_t handles, ints or None) at the
+    five stage boundaries; see include/moe_mxfp4.h."""
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    if len(stage_events) != 5:
+        raise ValueError("stage_events: expected 5 entries")
+    ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+    _check("moe_mxfp4_forward_profiled",
+           _lib.moe_mxfp4_forward_profiled(*args, ev, _stream(stream)))
     return out
 
 

@@ -1,6 +1,7 @@
 // C ABI of the fused MXFP4 MoE forward (declared in include/moe_mxfp4.h):
 // host-side validation, workspace carving, block_m choice and the launch
-// sequence route sort -> activation quant -> stage 1 -> stage 2 -> finalize,
+// sequence prologue (route sort + activation quant) -> stage 1 -> stage 2 ->
+// per-token slot reduction,
 // all asynchronous on the caller's stream with no host synchronization (grids
 // are sized for the worst-case route list; blocks past the real one exit).
 #include <hip/hip_runtime.h>
@@ -75,7 +76,7 @@ int choose_block_m(int M, int E, int topk)
 struct Layout {
     int bm;
     int64_t cap, nb;
-    size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a2q, a2s, acc, total;
+    size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a2q, a2s, partial, total;
 };
 
 Layout layout(int M, int D, int I, int E, int topk)
@@ -94,7 +95,7 @@ Layout layout(int M, int D, int I, int E, int topk)
     L.a1s = take(size_t(M) * D / 32);
     L.a2q = take(size_t(L.cap) * I / 2);
     L.a2s = take(size_t(L.cap) * I / 32);
-    L.acc = take(sizeof(float) * size_t(M) * D);
+    L.partial = take(sizeof(uint16_t) * size_t(M) * topk * D);
     L.total = off;
     return L;
 }
@@ -115,7 +116,14 @@ struct DebugOut {
     uint16_t* h;
     uint8_t* a2_codes;
     uint8_t* a2_scales;
+    hipEvent_t* events;     // 5 stage-boundary events (entries may be null)
 };
+
+bool mark(const DebugOut* d, int i, hipStream_t stream)
+{
+    if (!d || !d->events || !d->events[i]) return true;
+    return hipEventRecord(d->events[i], stream) == hipSuccess;
+}
 
 int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
                  const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
@@ -145,27 +153,27 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     uint8_t* a1s = ws + L.a1s;
     uint8_t* a2q = ws + L.a2q;
     uint8_t* a2s = ws + L.a2s;
-    float* acc = reinterpret_cast<float*>(ws + L.acc);
+    uint16_t* partial = reinterpret_cast<uint16_t*>(ws + L.partial);
     const int nb = int(L.nb);
 
-    hipError_t e = moe::launch_route_sort(topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route,
-                                          sorted_w, block_expert, num_valid, stream);
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    if (!mark(dbg, 0, stream)) return MOE_MXFP4_ERR_HIP;
     const int Ga = (D % 512 == 0) ? 4 : 2;
-    e = moe::launch_quant_rows(hidden, M, D, a1q, a1s, Ga, acc, n_cu, stream);
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
+                         block_expert, num_valid, hidden, D, Ga, a1q, a1s};
+    hipError_t e = moe::launch_prologue(pa, n_cu, stream);
+    if (e != hipSuccess || !mark(dbg, 1, stream)) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm1Args g1{a1q, a1s, w13, w13_scale, sorted_route, block_expert, num_valid, a2q, a2s,
                       dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb};
     e = moe::launch_gemm1(g1, stream);
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    if (e != hipSuccess || !mark(dbg, 2, stream)) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      acc, M, D, I, topk, L.bm, nb};
+                      partial, M, D, I, topk, L.bm, nb};
     e = moe::launch_gemm2(g2, stream);
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
-    e = moe::launch_finalize(acc, out, int64_t(M) * D, n_cu, stream);
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    if (e != hipSuccess || !mark(dbg, 3, stream)) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_reduce_slots(partial, topk_ids, M, D, E, topk, out, n_cu, stream);
+    if (e != hipSuccess || !mark(dbg, 4, stream)) return MOE_MXFP4_ERR_HIP;
 
     if (dbg) {
         if (dbg->sorted_route &&
@@ -278,7 +286,7 @@ MOE_API int moe_mxfp4_forward_debug(const uint16_t* hidden, const uint8_t* w13,
     const void* opt[] = {sorted_route, num_valid, h, a2_codes, a2_scales};
     for (const void* p : opt)
         if (p && !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
-    DebugOut d{sorted_route, num_valid, h, a2_codes, a2_scales};
+    DebugOut d{sorted_route, num_valid, h, a2_codes, a2_scales, nullptr};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream);
 }
@@ -293,7 +301,7 @@ MOE_API int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, ui
     int n_cu = 0;
     int st = device_check(&n_cu);
     if (st) return st;
-    return hip_status(moe::launch_quant_rows(x, rows, cols, codes, scales, 0, nullptr, n_cu, stream));
+    return hip_status(moe::launch_quant_rows(x, rows, cols, codes, scales, 0, n_cu, stream));
 }
 
 MOE_API int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w, int M, int E, int topk,
@@ -314,4 +322,16 @@ MOE_API int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w, int M,
     return hip_status(moe::launch_route_sort(topk_ids, topk_w, M, topk, E, block_m,
                                              int(cap / block_m), sorted_route, sorted_w,
                                              block_expert, num_valid, stream));
+}
+
+MOE_API int moe_mxfp4_forward_profiled(const uint16_t* hidden, const uint8_t* w13,
+                                       const uint8_t* w13_scale, const uint8_t* w2,
+                                       const uint8_t* w2_scale, const int32_t* topk_ids,
+                                       const float* topk_w, uint16_t* out, int M, int D, int I,
+                                       int E, int topk, void* workspace, size_t workspace_bytes,
+                                       hipEvent_t* stage_events, hipStream_t stream)
+{
+    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, stage_events};
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, &d, stream);
 }

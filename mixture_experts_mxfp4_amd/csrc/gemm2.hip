@@ -1,13 +1,21 @@
 // Stage 2: grouped down-projection GEMM on gfx950 block-scaled FP4 MFMA; the
-// epilogue multiplies by the routing weight and accumulates per token.
+// epilogue multiplies by the routing weight; a final pass sums the topk
+// contributions of every token.
 //
 // Semantics (kernelindex submission 754773: stage 2 receives the sorted
-// routing weights and accumulates atomically, `mode: atomic`; kernelindex
-// submission 723815 `_reference_forward`: out[t] += w * (act @ W_down^T)):
-// y = Q(h) . down_row over K = I for each sorted row, then
-// out[token, :] += sorted_w[row] * y.  Sums go to an fp32 accumulator with
-// hardware fp32 atomics (the per-token order of the topk contributions is not
-// fixed, every order is a valid fp32 sum); a final pass rounds once to bf16.
+// routing weights and accumulates the experts' contributions per token;
+// kernelindex submission 723815 `_reference_forward`: out[t] += w * (act @
+// W_down^T)): y = Q(h) . down_row over K = I for each sorted row, and
+// out[t, :] = sum over the token's valid slots s of topk_w[t, s] * y(t, s).
+//
+// The pages accumulate with atomics (`mode: atomic`).  On MI355X fp32 atomics
+// to L2 sustain ~0.27 G element-adds per microsecond, which made them the
+// bottleneck of the prefill shapes; instead each sorted row's weighted result
+// is stored once, as bf16, at its route index r = t*topk + s (plain coalesced
+// stores, no read-modify-write), and a reduction kernel adds the topk rows of
+// each token in a fixed slot order in fp32 and rounds once to bf16.  The
+// result is deterministic.  The extra rounding of each weighted contribution
+// to bf16 is bounded by 2^-9 of that contribution.
 //
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows and
 // 256 output columns; each wave owns 64 columns = 4 MFMA tiles per row tile
@@ -27,8 +35,8 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
                       const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
                       const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
                       const int32_t* __restrict__ block_expert,
-                      const int32_t* __restrict__ num_valid, float* __restrict__ acc_out, int M,
-                      int D, int I, int topk)
+                      const int32_t* __restrict__ num_valid, uint16_t* __restrict__ partial,
+                      int M, int D, int I, int topk)
 {
     constexpr int BM = 16 * RT;
     const int blk = blockIdx.y;
@@ -83,9 +91,9 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
             const int sr = sorted_route[srow];
             if (sr < R) {
                 const float w = sorted_w[srow];
-                float* dst = acc_out + int64_t(sr / topk) * D + n64 * 64 + lane % 16;
+                uint16_t* dst = partial + int64_t(sr) * D + n64 * 64 + lane % 16;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) unsafeAtomicAdd(dst + q * 16, w * acc[rt][q][i]);
+                for (int q = 0; q < 4; ++q) dst[q * 16] = uint16_t(f32_to_bf16_rne(w * acc[rt][q][i]));
             }
         }
     }
@@ -96,7 +104,7 @@ static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream)
 {
     hipLaunchKernelGGL((gemm2_weighted_kernel<RT, G>), dim3(a.D / 256, a.nb_cap),
                        dim3(kGemmThreads), 0, stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
-                       a.sorted_w, a.block_expert, a.num_valid, a.acc, a.M, a.D, a.I, a.topk);
+                       a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk);
     return hipGetLastError();
 }
 
@@ -112,32 +120,47 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream)
     }
 }
 
-// fp32 accumulator -> bf16 output, one rounding (8 elements per thread).
-__global__ void finalize_bf16_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out,
-                                     int64_t n8)
+// out[t, :] = bf16( sum_{s < topk, 0 <= ids[t,s] < E} partial[t*topk + s, :] ),
+// fp32 sum in slot order; 8 columns per thread.
+__global__ void __launch_bounds__(256)
+reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restrict__ ids, int M,
+                    int D, int E, int topk, uint16_t* __restrict__ out)
 {
+    const int64_t n8 = int64_t(M) * (D / 8);
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
          i += int64_t(gridDim.x) * blockDim.x) {
-        const float4 lo = reinterpret_cast<const float4*>(acc + i * 8)[0];
-        const float4 hi = reinterpret_cast<const float4*>(acc + i * 8)[1];
+        const int64_t t = i / (D / 8);
+        const int64_t c8 = i % (D / 8);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < topk; ++s) {
+            const int e = ids[t * topk + s];
+            if (e < 0 || e >= E) continue;
+            const uint4 v = ld16(reinterpret_cast<const uint8_t*>(partial + (t * topk + s) * D + c8 * 8));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += bf16_to_f32(w[j] & 0xFFFFu);
+                acc[2 * j + 1] += bf16_to_f32(w[j] >> 16);
+            }
+        }
         uint4 o;
-        o.x = f32_to_bf16_rne(lo.x) | (f32_to_bf16_rne(lo.y) << 16);
-        o.y = f32_to_bf16_rne(lo.z) | (f32_to_bf16_rne(lo.w) << 16);
-        o.z = f32_to_bf16_rne(hi.x) | (f32_to_bf16_rne(hi.y) << 16);
-        o.w = f32_to_bf16_rne(hi.z) | (f32_to_bf16_rne(hi.w) << 16);
-        *reinterpret_cast<uint4*>(out + i * 8) = o;
+        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+        o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+        *reinterpret_cast<uint4*>(out + t * D + c8 * 8) = o;
     }
 }
 
-hipError_t launch_finalize(const float* acc, uint16_t* out, int64_t n, int n_cu,
-                           hipStream_t stream)
+hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
+                               int topk, uint16_t* out, int n_cu, hipStream_t stream)
 {
-    const int64_t n8 = n / 8;
+    const int64_t n8 = int64_t(M) * (D / 8);
     if (n8 == 0) return hipSuccess;
     int64_t blocks = (n8 + 255) / 256;
     if (blocks > int64_t(n_cu) * 16) blocks = int64_t(n_cu) * 16;
-    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, acc,
-                       out, n8);
+    hipLaunchKernelGGL(reduce_slots_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, partial,
+                       ids, M, D, E, topk, out);
     return hipGetLastError();
 }
 

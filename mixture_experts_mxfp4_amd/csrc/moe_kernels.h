@@ -14,8 +14,21 @@ hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int top
                              int32_t* block_expert, int32_t* num_valid, hipStream_t stream);
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                             uint8_t* scales, int scale_G, float* zero_f32, int n_cu,
-                             hipStream_t stream);
+                             uint8_t* scales, int scale_G, int n_cu, hipStream_t stream);
+
+// Route sort (workgroup 0) + activation quantization (the other workgroups).
+struct PrologueArgs {
+    const int32_t* ids;
+    const float* tw;
+    int M, topk, E, bm, nb_cap;
+    int32_t *sorted_route;
+    float* sorted_w;
+    int32_t *block_expert, *num_valid;
+    const uint16_t* hidden;
+    int D, scale_G;
+    uint8_t *a1q, *a1s;
+};
+hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream);
 
 hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
                           uint8_t* dst_scales, int E, int N, int K, int gate_up_I, int inverse,
@@ -38,12 +51,12 @@ struct Gemm2Args {
     const int32_t* sorted_route;
     const float* sorted_w;
     const int32_t *block_expert, *num_valid;
-    float* acc;
+    uint16_t* partial;          // bf16 [M*topk][D], weighted contribution per route
     int M, D, I, topk, block_m, nb_cap;
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
 
-hipError_t launch_finalize(const float* acc, uint16_t* out, int64_t n, int n_cu,
-                           hipStream_t stream);
+hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
+                               int topk, uint16_t* out, int n_cu, hipStream_t stream);
 
 }  // namespace moe

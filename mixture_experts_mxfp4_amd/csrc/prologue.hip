@@ -1,0 +1,308 @@
+// Forward prologue: the route sort and the dynamic MXFP4 quantization of the
+// hidden states, in ONE launch (workgroup 0 sorts the routes, the other
+// workgroups quantize; neither depends on the other).
+//
+// Route sort.  What it computes follows the sorting workspace of kernelindex
+// submission 754773 (sorted ids / sorted weights / per-block expert ids /
+// num_valid, each expert's segment padded to a multiple of block_m) and the
+// routing kernels of submission 723815 (histogram over experts, exclusive
+// scan, scatter; expert ids outside [0, E) are ignored).  A route is
+// r = t*topk + s.  Design (one 1024-thread workgroup):
+//   pass 1  every wave walks its own contiguous range of routes, 64 at a time;
+//           lanes holding the same expert are found with ballots over the bits
+//           of the expert id, and the lowest such lane adds their count to the
+//           wave's private LDS histogram row (no atomics, no contention);
+//   scan    per expert: padded count, workgroup-wide exclusive scan -> expert
+//           base; per (wave, expert) start = base + counts of earlier waves;
+//   pass 2  the same walk again; each route lands at start + rank among equal
+//           lanes, so every expert's list is in ascending route order and the
+//           output is deterministic.
+// The code is kept compact (no unrolling) for short route lists: a kernel
+// that one workgroup runs once is bound by instruction fetch and memory
+// latency, not by arithmetic.  Long lists use a 4x unrolled walk that keeps
+// more loads in flight.
+//
+// Activation quantization (OCP MX v1.0; the FP4 branch of 754773 quantizes
+// the hidden states per 32 elements before the gate_up GEMM): four lanes own
+// one 32-element block (8 bf16 = 16 bytes each); the block maximum is reduced
+// across the four lanes, each lane writes 4 code bytes and the first lane the
+// scale byte.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int kPrologueThreads = 1024;
+constexpr int kRouteWaves = kPrologueThreads / kWave;
+
+// Lanes of this wave whose (valid) expert id equals mine.
+__device__ __forceinline__ uint64_t same_expert_lanes(int id, bool valid, int nbits)
+{
+    uint64_t peers = __ballot(valid);
+#pragma unroll 1
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (id >> b) & 1;
+        uint64_t set = __ballot(valid && bit);
+        peers &= bit ? set : ~set;
+    }
+    return peers;
+}
+
+template <int U>
+__device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
+                                int M, int topk, int E, int bm, int nb_cap,
+                                int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
+                                int32_t* __restrict__ block_expert,
+                                int32_t* __restrict__ num_valid, int32_t* lds)
+{
+    int32_t* cnt = lds;                                   // [waves][E]
+    int32_t* wave_sum = lds + kRouteWaves * E;            // [2][waves] scan scratch
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int R = M * topk;
+    const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int i = tid; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
+    __syncthreads();
+
+    const int per_wave = (R + kRouteWaves - 1) / kRouteWaves;
+    const int w_begin = min(R, wave * per_wave), w_end = min(R, w_begin + per_wave);
+
+    // pass 1: per-wave histogram
+#pragma unroll 1
+    for (int base = w_begin; base < w_end; base += kWave * U) {
+        int id[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int r = base + u * kWave + lane;
+            id[u] = r < w_end ? ids[r] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bool valid = id[u] >= 0 && id[u] < E;
+            uint64_t peers = same_expert_lanes(id[u], valid, nbits);
+            if (valid && (peers & lanes_below) == 0) cnt[wave * E + id[u]] += __popcll(peers);
+        }
+    }
+    __syncthreads();
+
+    // scan over experts of the padded counts (one expert per thread per round)
+    int carry = 0, valid_total = 0;
+#pragma unroll 1
+    for (int e0 = 0; e0 < E; e0 += kPrologueThreads) {
+        const int e = e0 + tid;
+        int total = 0;
+        if (e < E)
+#pragma unroll 1
+            for (int w = 0; w < kRouteWaves; ++w) total += cnt[w * E + e];
+        const int padded = (total + bm - 1) / bm * bm;
+        int inc = padded, vinc = total;               // inclusive scans within the wave
+#pragma unroll 1
+        for (int off = 1; off < kWave; off <<= 1) {
+            int a = __shfl_up(inc, off), b = __shfl_up(vinc, off);
+            if (lane >= off) { inc += a; vinc += b; }
+        }
+        if (lane == kWave - 1) { wave_sum[wave] = inc; wave_sum[kRouteWaves + wave] = vinc; }
+        __syncthreads();
+        int before = 0, all = 0, vall = 0;
+#pragma unroll 1
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int s = wave_sum[w];
+            before += (w < wave) ? s : 0;
+            all += s;
+            vall += wave_sum[kRouteWaves + w];
+        }
+        const int base_e = carry + before + inc - padded;
+        if (e < E) {
+            int run = base_e;
+#pragma unroll 1
+            for (int w = 0; w < kRouteWaves; ++w) {
+                int c = cnt[w * E + e];
+                cnt[w * E + e] = run;
+                run += c;
+            }
+#pragma unroll 1
+            for (int p = base_e + total; p < base_e + padded; ++p) {
+                sorted_route[p] = R;
+                sorted_w[p] = 0.0f;
+            }
+#pragma unroll 1
+            for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
+        }
+        carry += all;
+        valid_total += vall;
+        __syncthreads();
+    }
+    for (int b = carry / bm + tid; b < nb_cap; b += kPrologueThreads) block_expert[b] = -1;
+    if (tid == 0) {
+        num_valid[0] = carry;
+        num_valid[1] = valid_total;
+    }
+
+    // pass 2: stable scatter (each wave only touches its own histogram row)
+#pragma unroll 1
+    for (int base = w_begin; base < w_end; base += kWave * U) {
+        int id[U];
+        float wt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int r = base + u * kWave + lane;
+            id[u] = r < w_end ? ids[r] : -1;
+            wt[u] = r < w_end ? tw[r] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = base + u * kWave + lane;
+            const bool valid = id[u] >= 0 && id[u] < E;
+            const uint64_t peers = same_expert_lanes(id[u], valid, nbits);
+            const int start = valid ? cnt[wave * E + id[u]] : 0;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                const int pos = start + __popcll(peers & lanes_below);
+                sorted_route[pos] = r;
+                sorted_w[pos] = wt[u];
+                if ((peers & lanes_below) == 0) cnt[wave * E + id[u]] = start + __popcll(peers);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+// MXFP4 quantization of rows of bf16 (grid-stride over 8-element chunks, four
+// lanes per 32-element block).  scale_G = 0: scales row-major [rows][cols/32];
+// otherwise the grouped activation layout of act_scale_pos(., scale_G).
+__device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                int scale_G, int64_t block, int64_t nblocks, int nthreads)
+{
+    const int64_t chunks_per_row = cols / 8;
+    const int64_t n_chunks = rows * chunks_per_row;
+    const int64_t stride = nblocks * nthreads;
+    for (int64_t i0 = block * nthreads; i0 < n_chunks; i0 += stride) {
+        const int64_t i = i0 + threadIdx.x;
+        const bool in = i < n_chunks;          // whole 4-lane groups are in or out
+        uint4 v = in ? *reinterpret_cast<const uint4*>(x + i * 8) : make_uint4(0, 0, 0, 0);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = max(amax, w[j] & 0x7FFFu);
+            amax = max(amax, (w[j] >> 16) & 0x7FFFu);
+        }
+        amax = max(amax, uint32_t(__shfl_xor(int(amax), 1)));
+        amax = max(amax, uint32_t(__shfl_xor(int(amax), 2)));
+        const uint32_t s = mx_scale_from_amax(amax);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t c0 = mx_code(w[j] & 0xFFFFu, s), c1 = mx_code(w[j] >> 16, s);
+            packed |= (c0 | (c1 << 4)) << (8 * j);
+        }
+        if (in) {
+            reinterpret_cast<uint32_t*>(codes)[i] = packed;
+            if ((i & 3) == 0) {
+                const int64_t row = i / chunks_per_row;
+                const int kb = int((i % chunks_per_row) / 4);
+                const int pos = scale_G ? act_scale_pos(kb, scale_G) : kb;
+                scales[row * (cols / 32) + pos] = uint8_t(s);
+            }
+        }
+    }
+}
+
+template <int U>
+__global__ void __launch_bounds__(kPrologueThreads)
+route_sort_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw, int M,
+                  int topk, int E, int bm, int nb_cap, int32_t* __restrict__ sorted_route,
+                  float* __restrict__ sorted_w, int32_t* __restrict__ block_expert,
+                  int32_t* __restrict__ num_valid)
+{
+    extern __shared__ int32_t lds[];
+    route_sort_body<U>(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w, block_expert,
+                       num_valid, lds);
+}
+
+__global__ void __launch_bounds__(kPrologueThreads)
+quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int scale_G)
+{
+    quant_rows_body(x, rows, cols, codes, scales, scale_G, blockIdx.x, gridDim.x,
+                    kPrologueThreads);
+}
+
+template <int U>
+__global__ void __launch_bounds__(kPrologueThreads)
+prologue_kernel(PrologueArgs a)
+{
+    extern __shared__ int32_t lds[];
+    if (blockIdx.x == 0) {
+        route_sort_body<U>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
+                           a.sorted_w, a.block_expert, a.num_valid, lds);
+    } else {
+        quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, a.scale_G, blockIdx.x - 1,
+                        gridDim.x - 1, kPrologueThreads);
+    }
+}
+
+size_t route_lds_bytes(int E) { return sizeof(int32_t) * (size_t(kRouteWaves) * E + 2 * kRouteWaves); }
+
+static bool long_list(int M, int topk) { return int64_t(M) * topk > 4096; }
+
+hipError_t route_allow_lds(int bytes)
+{
+    const void* k[] = {reinterpret_cast<const void*>(&route_sort_kernel<1>),
+                       reinterpret_cast<const void*>(&route_sort_kernel<4>),
+                       reinterpret_cast<const void*>(&prologue_kernel<1>),
+                       reinterpret_cast<const void*>(&prologue_kernel<4>)};
+    for (const void* f : k) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int topk, int E, int bm,
+                             int nb_cap, int32_t* sorted_route, float* sorted_w,
+                             int32_t* block_expert, int32_t* num_valid, hipStream_t stream)
+{
+    if (long_list(M, topk))
+        hipLaunchKernelGGL(route_sort_kernel<4>, dim3(1), dim3(kPrologueThreads),
+                           route_lds_bytes(E), stream, ids, tw, M, topk, E, bm, nb_cap,
+                           sorted_route, sorted_w, block_expert, num_valid);
+    else
+        hipLaunchKernelGGL(route_sort_kernel<1>, dim3(1), dim3(kPrologueThreads),
+                           route_lds_bytes(E), stream, ids, tw, M, topk, E, bm, nb_cap,
+                           sorted_route, sorted_w, block_expert, num_valid);
+    return hipGetLastError();
+}
+
+static int64_t quant_blocks(int64_t rows, int64_t cols, int n_cu)
+{
+    const int64_t n_chunks = rows * (cols / 8);
+    int64_t blocks = (n_chunks + kPrologueThreads - 1) / kPrologueThreads;
+    return blocks > int64_t(n_cu) * 4 ? int64_t(n_cu) * 4 : blocks;
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                             uint8_t* scales, int scale_G, int n_cu, hipStream_t stream)
+{
+    const int64_t blocks = quant_blocks(rows, cols, n_cu);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), 0,
+                       stream, x, rows, cols, codes, scales, scale_G);
+    return hipGetLastError();
+}
+
+hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream)
+{
+    const int64_t blocks = 1 + quant_blocks(a.M, a.D, n_cu);
+    if (long_list(a.M, a.topk))
+        hipLaunchKernelGGL(prologue_kernel<4>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
+                           route_lds_bytes(a.E), stream, a);
+    else
+        hipLaunchKernelGGL(prologue_kernel<1>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
+                           route_lds_bytes(a.E), stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe
