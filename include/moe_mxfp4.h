@@ -75,9 +75,8 @@ const char* moe_mxfp4_status_string(int status);
  *   codes  [N/64][K/128][4][64][16 B]: 16-row slice q of 64-row group n64,
  *          K tile kt (128 elements); lane L holds row n64*64 + q*16 + L%16,
  *          elements kt*128 + (L/16)*32 .. +32 (the raw 16 bytes).
- *   scales [N/64][K/(128G)][4][64][G B], G = 4 if K % 512 == 0 else 2: lane
- *          L's G bytes are the scales of row n64*64+q*16+L%16, 32-blocks
- *          (kg*G + j)*4 + L/16 for j < G.
+ *   scales [N/64][K/128][64][4 B]: byte q of lane L's word at K tile kt is
+ *          the scale of row n64*64 + q*16 + L%16, 32-block kt*4 + L/16.
  * For gate_up the rows are first interleaved so that each 64-row group holds
  * gate rows c*32..c*32+31 followed by up rows I+c*32..I+c*32+31 (group c).
  * ------------------------------------------------------------------------- */
@@ -148,7 +147,7 @@ int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
  *   sorted_route i32 [cap], sorted_w f32 [cap], block_expert i32 [cap/block_m]
  *   (-1 past the last used block), num_valid i32 [2] = {padded rows, valid
  *   routes}; cap = moe_mxfp4_route_capacity(M, E, topk, block_m).
- * block_m must be 16, 32, 64 or 128. */
+ * block_m must be 16, 32, 64, 128 or 256. */
 int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w,
                     int M, int E, int topk, int block_m,
                     int32_t* sorted_route, float* sorted_w,

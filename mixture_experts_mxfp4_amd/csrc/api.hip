@@ -36,7 +36,8 @@ int device_check(int* n_cu)
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
         st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-        if (st == 1 && moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess)
+        if (st == 1 && (moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess ||
+                        moe::tile_allow_lds() != hipSuccess))
             return MOE_MXFP4_ERR_HIP;
         g_arch_state[dev].store(st, std::memory_order_relaxed);
     }
@@ -70,13 +71,15 @@ int choose_block_m(int M, int E, int topk)
     const double avg = double(M) * topk / double(E);
     if (avg < 8.0) return 16;
     if (avg < 32.0) return 32;
-    return 64;
+    if (avg < 256.0) return 64;
+    return 256;       // LDS-tiled kernels (gemm_tile.hip)
 }
 
 struct Layout {
     int bm;
     int64_t cap, nb;
-    size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a2q, a2s, partial, total;
+    size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
+        total;
 };
 
 Layout layout(int M, int D, int I, int E, int topk)
@@ -93,6 +96,10 @@ Layout layout(int M, int D, int I, int E, int topk)
     L.num_valid = take(sizeof(int32_t) * 4);
     L.a1q = take(size_t(M) * D / 2);
     L.a1s = take(size_t(M) * D / 32);
+    // sorted fragment-layout copy of a1, only for the tiled kernels
+    const bool tile = L.bm == 256;
+    L.a1f = take(tile ? size_t(L.cap) * D / 2 : 0);
+    L.a1fs = take(tile ? size_t(L.cap) * D / 32 : 0);
     L.a2q = take(size_t(L.cap) * I / 2);
     L.a2s = take(size_t(L.cap) * I / 32);
     L.partial = take(sizeof(uint16_t) * size_t(M) * topk * D);
@@ -151,26 +158,33 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     int32_t* num_valid = reinterpret_cast<int32_t*>(ws + L.num_valid);
     uint8_t* a1q = ws + L.a1q;
     uint8_t* a1s = ws + L.a1s;
+    uint8_t* a1f = ws + L.a1f;
+    uint8_t* a1fs = ws + L.a1fs;
     uint8_t* a2q = ws + L.a2q;
     uint8_t* a2s = ws + L.a2s;
     uint16_t* partial = reinterpret_cast<uint16_t*>(ws + L.partial);
     const int nb = int(L.nb);
 
     if (!mark(dbg, 0, stream)) return MOE_MXFP4_ERR_HIP;
-    const int Ga = (D % 512 == 0) ? 4 : 2;
+    // block_m 256 selects the LDS-tiled kernels (many routes per expert);
+    // smaller blocks the weight-streaming kernels.
+    const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
-                         block_expert, num_valid, hidden, D, Ga, a1q, a1s};
+                         block_expert, num_valid, hidden, D, a1q, a1s};
     hipError_t e = moe::launch_prologue(pa, n_cu, stream);
+    if (e == hipSuccess && tile)
+        e = moe::launch_gather_a1(a1q, a1s, sorted_route, num_valid, M, D, topk, L.cap, a1f, a1fs,
+                                  n_cu, stream);
     if (e != hipSuccess || !mark(dbg, 1, stream)) return MOE_MXFP4_ERR_HIP;
 
-    moe::Gemm1Args g1{a1q, a1s, w13, w13_scale, sorted_route, block_expert, num_valid, a2q, a2s,
-                      dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb};
-    e = moe::launch_gemm1(g1, stream);
+    moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
+                      a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap};
+    e = tile ? moe::launch_gemm1_tile(g1, stream) : moe::launch_gemm1(g1, stream);
     if (e != hipSuccess || !mark(dbg, 2, stream)) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      partial, M, D, I, topk, L.bm, nb};
-    e = moe::launch_gemm2(g2, stream);
+                      partial, M, D, I, topk, L.bm, nb, L.cap};
+    e = tile ? moe::launch_gemm2_tile(g2, stream) : moe::launch_gemm2(g2, stream);
     if (e != hipSuccess || !mark(dbg, 3, stream)) return MOE_MXFP4_ERR_HIP;
     e = moe::launch_reduce_slots(partial, topk_ids, M, D, E, topk, out, n_cu, stream);
     if (e != hipSuccess || !mark(dbg, 4, stream)) return MOE_MXFP4_ERR_HIP;
@@ -183,11 +197,10 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
         if (dbg->num_valid && hipMemcpyAsync(dbg->num_valid, num_valid, sizeof(int32_t) * 2,
                                              hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return MOE_MXFP4_ERR_HIP;
-        if (dbg->a2_codes || dbg->a2_scales) {
-            e = moe::launch_a2_to_canonical(a2q, a2s, L.cap, I, dbg->a2_codes, dbg->a2_scales,
-                                            stream);
-            if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
-        }
+        if ((dbg->a2_codes || dbg->a2_scales) &&
+            moe::launch_a2_to_canonical(a2q, a2s, L.cap, I, dbg->a2_codes, dbg->a2_scales,
+                                        stream) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
     }
     return MOE_MXFP4_OK;
 }
@@ -301,7 +314,7 @@ MOE_API int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, ui
     int n_cu = 0;
     int st = device_check(&n_cu);
     if (st) return st;
-    return hip_status(moe::launch_quant_rows(x, rows, cols, codes, scales, 0, n_cu, stream));
+    return hip_status(moe::launch_quant_rows(x, rows, cols, codes, scales, n_cu, stream));
 }
 
 MOE_API int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w, int M, int E, int topk,
@@ -309,7 +322,7 @@ MOE_API int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w, int M,
                             int32_t* block_expert, int32_t* num_valid, hipStream_t stream)
 {
     if (M < 0 || E < 1 || topk < 1 || topk > kMaxTopk) return MOE_MXFP4_ERR_INVALID_ARG;
-    if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256)
         return MOE_MXFP4_ERR_INVALID_ARG;
     if (E > kMaxE || int64_t(M) * topk > kMaxRoutes) return MOE_MXFP4_ERR_UNSUPPORTED;
     const void* ptrs[] = {topk_ids, topk_w, sorted_route, sorted_w, block_expert, num_valid};

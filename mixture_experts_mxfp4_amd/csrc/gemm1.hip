@@ -15,8 +15,10 @@
 // each wave runs RT x 4 MFMA tiles of 16x16x128, streaming its weight
 // fragments (1 KiB each, contiguous) with non-temporal loads and gathering the
 // block's activation rows by token id.  Partial sums meet in LDS; the epilogue
-// quantizes h with cross-lane reductions and writes it in the fragment order
-// that stage 2 loads directly.
+// quantizes h with cross-lane reductions and writes it in sorted-row order in
+// the fragment layout (moe_common.h) that stage 2 loads contiguously.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -24,9 +26,12 @@ namespace moe {
 
 constexpr int kGemmThreads = 256;
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// Loads of U consecutive K tiles are issued before their MFMAs so that every
+// wave keeps U x 4 KiB of weight fragments in flight.
+template <int RT>
+constexpr int g1_unroll() { return RT <= 2 ? 4 : 2; }
 
-template <int RT, int G>
+template <int RT>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
                           const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
@@ -34,9 +39,10 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                           const int32_t* __restrict__ block_expert,
                           const int32_t* __restrict__ num_valid, uint8_t* __restrict__ a2q,
                           uint8_t* __restrict__ a2s, uint16_t* __restrict__ h_dbg, int M, int D,
-                          int I, int topk)
+                          int I, int topk, int64_t cap)
 {
     constexpr int BM = 16 * RT;
+    constexpr int U = g1_unroll<RT>();
     __shared__ float red[4][RT][4][4][kWave];   // [wave][row tile][slice][i][lane]
 
     const int c = blockIdx.x;          // MXFP4 group of h = 64-row group of w13p
@@ -45,7 +51,7 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
-    const int KT = D / 128, NKG = KT / G;
+    const int KT = D / 128;
     const int64_t a_row = D / 2, as_row = D / 32;
 
     const uint8_t* a_ptr[RT];
@@ -53,14 +59,15 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     bool ok[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        int sr = sorted_route[blk * BM + rt * 16 + lane % 16];
+        const int sr = sorted_route[blk * BM + rt * 16 + lane % 16];
         ok[rt] = sr < R;
-        int64_t tok = ok[rt] ? sr / topk : 0;
+        const int64_t tok = ok[rt] ? sr / topk : 0;
         a_ptr[rt] = a1q + tok * a_row + (lane / 16) * 16;
-        as_ptr[rt] = a1s + tok * as_row + (lane / 16) * G;
+        as_ptr[rt] = a1s + tok * as_row;
     }
-    const uint8_t* wb = w13p + int64_t(e) * (2 * I) * a_row + int64_t(c) * KT * 4096 + lane * 16;
-    const uint8_t* sb = w13sp + int64_t(e) * (2 * I) * as_row + int64_t(c) * NKG * 256 * G + lane * G;
+    const uint8_t* wb = w13p + int64_t(e) * I * D + int64_t(c) * KT * 4096 + lane * 16;
+    const uint8_t* sb = w13sp + int64_t(e) * I * D / 16 + int64_t(c) * KT * 256 + lane * 4;
+    const int ash = 8 * (lane / 16);     // this lane's 32-block inside an A scale word
 
     v4f acc[RT][4];
 #pragma unroll
@@ -68,31 +75,35 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int kg0 = wave * NKG / 4, kg1 = (wave + 1) * NKG / 4;
-    for (int kg = kg0; kg < kg1; ++kg) {
-        uint32_t sw[4], sa[RT];
+    auto steps = [&](auto u_const, int kt) {
+        constexpr int UU = decltype(u_const)::value;
+        uint32_t sw[UU], sa[UU][RT];
+        uint4 b[UU][4], a[UU][RT];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sw[q] = ld_scales<G>(sb + (kg * 4 + q) * 64 * G);
+        for (int u = 0; u < UU; ++u) {
+            sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sa[rt] = ok[rt] ? ld_scales<G>(as_ptr[rt] + kg * 4 * G) : 0u;
+            for (int q = 0; q < 4; ++q) b[u][q] = ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int kt = kg * G + j;
-            uint4 b[4], a[RT];
+            for (int rt = 0; rt < RT; ++rt) {
+                sa[u][rt] = ok[rt] ? *reinterpret_cast<const uint32_t*>(as_ptr[rt] + (kt + u) * 4) : 0u;
+                a[u][rt] = ok[rt] ? ld16(a_ptr[rt] + (kt + u) * 64) : make_uint4(0, 0, 0, 0);
+            }
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) b[q] = ld16_nt(wb + int64_t(kt * 4 + q) * 1024);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                a[rt] = ok[rt] ? ld16(a_ptr[rt] + kt * 64) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < UU; ++u)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    acc[rt][q] = mfma_fp4_16x16x128(a[rt], b[q], acc[rt][q],
-                                                    (sa[rt] >> (8 * j)) & 0xFFu,
-                                                    (sw[q] >> (8 * j)) & 0xFFu);
-        }
-    }
+                    acc[rt][q] = mfma_fp4_16x16x128(a[u][rt], b[u][q], acc[rt][q],
+                                                    (sa[u][rt] >> ash) & 0xFFu,
+                                                    (sw[u] >> (8 * q)) & 0xFFu);
+    };
+    const int kt1 = (wave + 1) * KT / 4;
+    int kt = wave * KT / 4;
+    for (; kt + U <= kt1; kt += U) steps(std::integral_constant<int, U>{}, kt);
+    for (; kt < kt1; ++kt) steps(std::integral_constant<int, 1>{}, kt);
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -102,8 +113,6 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
             for (int i = 0; i < 4; ++i) red[wave][rt][q][i][lane] = acc[rt][q][i];
     __syncthreads();
 
-    const int KT2 = I / 128;
-    const int G2 = (I % 512 == 0) ? 4 : 2;
     for (int rt = wave; rt < RT; rt += 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -113,95 +122,78 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                 s4[q] = red[0][rt][q][i][lane] + red[1][rt][q][i][lane] +
                         red[2][rt][q][i][lane] + red[3][rt][q][i][lane];
             // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
-            const uint32_t h0 = f32_to_bf16_rne(silu_f32(s4[0]) * s4[2]);
-            const uint32_t h1 = f32_to_bf16_rne(silu_f32(s4[1]) * s4[3]);
-            const int row = 4 * (lane / 16) + i;                  // row within the tile
+            const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
+            const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
+            const int row = 4 * (lane / 16) + i;                     // row within the tile
             const int64_t srow = int64_t(blk) * BM + rt * 16 + row;  // sorted row
             if (h_dbg) {
                 h_dbg[srow * I + c * 32 + lane % 16] = uint16_t(h0);
                 h_dbg[srow * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
             }
             // MXFP4 group = the 32 columns held by the 16 lanes of this row
-            uint32_t amax = max(h0 & 0x7FFFu, h1 & 0x7FFFu);
-            amax = max(amax, uint32_t(__shfl_xor(int(amax), 1)));
-            amax = max(amax, uint32_t(__shfl_xor(int(amax), 2)));
-            amax = max(amax, uint32_t(__shfl_xor(int(amax), 4)));
-            amax = max(amax, uint32_t(__shfl_xor(int(amax), 8)));
-            const uint32_t s = mx_scale_from_amax(amax);
-            const uint32_t c0 = mx_code(h0, s), c1 = mx_code(h1, s);
-            // bytes: element 2b in the low nibble, 2b+1 in the high nibble
-            const uint32_t o0 = uint32_t(__shfl_xor(int(c0), 1));
-            const uint32_t o1 = uint32_t(__shfl_xor(int(c1), 1));
-            const uint32_t blo = c0 | (o0 << 4), bhi = c1 | (o1 << 4);
-            const uint32_t plo = blo | (uint32_t(__shfl_down(int(blo), 2)) << 8);
-            const uint32_t phi = bhi | (uint32_t(__shfl_down(int(bhi), 2)) << 8);
-            const uint32_t qlo = plo | (uint32_t(__shfl_down(int(plo), 4)) << 16);
-            const uint32_t qhi = phi | (uint32_t(__shfl_down(int(phi), 4)) << 16);
-            const uint32_t d1 = uint32_t(__shfl_down(int(qlo), 8));
-            const uint32_t d3 = uint32_t(__shfl_down(int(qhi), 8));
+            // (one DPP row): columns lane%16 (h0) and 16 + lane%16 (h1)
+            const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
+            const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
+            const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
+            const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
+            const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
             if (lane % 16 == 0) {
-                const int64_t rowtile = int64_t(blk) * RT + rt;
-                const int kt2 = c / 4;
-                const int L = (c % 4) * 16 + row;
-                *reinterpret_cast<uint4*>(a2q + ((rowtile * KT2 + kt2) * 64 + L) * 16) =
+                *reinterpret_cast<uint4*>(a2q + frag_code_off(srow, c / 4, c % 4, I / 128)) =
                     make_uint4(qlo, d1, qhi, d3);
-                a2s[((rowtile * (KT2 / G2) + kt2 / G2) * 64 + L) * G2 + kt2 % G2] = uint8_t(s);
+                a2s[frag_scale_off(srow, c / 4, cap) + c % 4] = uint8_t(s);
             }
         }
     }
 }
 
-template <int RT, int G>
+template <int RT>
 static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<RT, G>), dim3(a.I / 32, a.nb_cap),
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<RT>), dim3(a.I / 32, a.nb_cap),
                        dim3(kGemmThreads), 0, stream, a.a1q, a.a1s, a.w13p, a.w13sp,
                        a.sorted_route, a.block_expert, a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M,
-                       a.D, a.I, a.topk);
+                       a.D, a.I, a.topk, a.cap);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream)
 {
     if (a.nb_cap == 0) return hipSuccess;
-    const bool g4 = (a.D % 512) == 0;
     switch (a.block_m) {
-    case 16: return g4 ? launch_g1<1, 4>(a, stream) : launch_g1<1, 2>(a, stream);
-    case 32: return g4 ? launch_g1<2, 4>(a, stream) : launch_g1<2, 2>(a, stream);
-    case 64: return g4 ? launch_g1<4, 4>(a, stream) : launch_g1<4, 2>(a, stream);
+    case 16: return launch_g1<1>(a, stream);
+    case 32: return launch_g1<2>(a, stream);
+    case 64: return launch_g1<4>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-// Fragment-order a2 (codes + scales) -> canonical row-major [cap][I/2], [cap][I/32].
+// Fragment-layout a2 -> canonical row-major [cap][I/2] codes, [cap][I/32] scales.
 __global__ void a2_to_canonical_kernel(const uint8_t* __restrict__ a2q,
-                                       const uint8_t* __restrict__ a2s, int64_t rows, int I,
+                                       const uint8_t* __restrict__ a2s, int64_t cap, int I,
                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    const int ng = I / 32, KT2 = I / 128, G2 = (I % 512 == 0) ? 4 : 2;
-    const int64_t n = rows * ng;
+    const int ng = I / 32;
+    const int64_t n = cap * ng;
     for (int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; idx < n;
          idx += int64_t(gridDim.x) * blockDim.x) {
         const int64_t row = idx / ng;
         const int c = int(idx % ng);
-        const int64_t rowtile = row / 16;
-        const int kt2 = c / 4, L = (c % 4) * 16 + int(row % 16);
-        const uint4 v = ld16(a2q + ((rowtile * KT2 + kt2) * 64 + L) * 16);
-        if (codes) *reinterpret_cast<uint4*>(codes + row * (I / 2) + c * 16) = v;
-        if (scales)
-            scales[row * ng + c] = a2s[((rowtile * (KT2 / G2) + kt2 / G2) * 64 + L) * G2 + kt2 % G2];
+        if (codes)
+            *reinterpret_cast<uint4*>(codes + row * (I / 2) + c * 16) =
+                ld16(a2q + frag_code_off(row, c / 4, c % 4, I / 128));
+        if (scales) scales[row * ng + c] = a2s[frag_scale_off(row, c / 4, cap) + c % 4];
     }
 }
 
-hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t rows, int I,
+hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t cap, int I,
                                   uint8_t* codes, uint8_t* scales, hipStream_t stream)
 {
-    const int64_t n = rows * (I / 32);
+    const int64_t n = cap * (I / 32);
     if (n == 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(a2_to_canonical_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a2q,
-                       a2s, rows, I, codes, scales);
+                       a2s, cap, I, codes, scales);
     return hipGetLastError();
 }
 

@@ -20,8 +20,10 @@
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows and
 // 256 output columns; each wave owns 64 columns = 4 MFMA tiles per row tile
 // and runs the whole K = I loop, streaming 1 KiB weight fragments with
-// non-temporal loads; the A fragments (h, already in MFMA fragment order from
-// stage 1) are contiguous 1 KiB loads as well.
+// non-temporal loads; the A fragments (MXFP4 h, written by stage 1 in the
+// fragment layout) are contiguous 1 KiB loads as well.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -29,27 +31,40 @@ namespace moe {
 
 constexpr int kGemmThreads = 256;
 
-template <int RT, int G>
+template <int RT>
+constexpr int g2_unroll() { return RT <= 2 ? 4 : 2; }
+
+template <int RT>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
                       const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
                       const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
                       const int32_t* __restrict__ block_expert,
                       const int32_t* __restrict__ num_valid, uint16_t* __restrict__ partial,
-                      int M, int D, int I, int topk)
+                      int M, int D, int I, int topk, int64_t cap)
 {
     constexpr int BM = 16 * RT;
+    constexpr int U = g2_unroll<RT>();
     const int blk = blockIdx.y;
     if (blk * BM >= num_valid[0]) return;
     const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int n64 = blockIdx.x * 4 + wave;
-    const int KT = I / 128, NKG = KT / G;
+    const int KT = I / 128;
     const int R = M * topk;
 
     const uint8_t* wb = w2p + int64_t(e) * D * (I / 2) + int64_t(n64) * KT * 4096 + lane * 16;
-    const uint8_t* sb = w2sp + int64_t(e) * D * (I / 32) + int64_t(n64) * NKG * 256 * G + lane * G;
-    const int64_t rowtile0 = int64_t(blk) * RT;
+    const uint8_t* sb = w2sp + int64_t(e) * D * (I / 32) + int64_t(n64) * KT * 256 + lane * 4;
+    // A operand: the 1 KiB fragment of row tile rt at K tile kt; scales kt-major
+    const uint8_t* a_ptr[RT];
+    const uint8_t* as_ptr[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t row0 = int64_t(blk) * BM + rt * 16;
+        a_ptr[rt] = a2q + frag_code_off(row0, 0, 0, KT) + lane * 16;
+        as_ptr[rt] = a2s + frag_scale_off(row0 + lane % 16, 0, cap);
+    }
+    const int ash = 8 * (lane / 16);
 
     v4f acc[RT][4];
 #pragma unroll
@@ -57,31 +72,34 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int kg = 0; kg < NKG; ++kg) {
-        uint32_t sw[4], sa[RT];
+    auto steps = [&](auto u_const, int kt) {
+        constexpr int UU = decltype(u_const)::value;
+        uint32_t sw[UU], sa[UU][RT];
+        uint4 b[UU][4], a[UU][RT];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sw[q] = ld_scales<G>(sb + (kg * 4 + q) * 64 * G);
+        for (int u = 0; u < UU; ++u) {
+            sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            sa[rt] = ld_scales<G>(a2s + (((rowtile0 + rt) * NKG + kg) * 64 + lane) * G);
+            for (int q = 0; q < 4; ++q) b[u][q] = ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int kt = kg * G + j;
-            uint4 b[4], a[RT];
+            for (int rt = 0; rt < RT; ++rt) {
+                sa[u][rt] = *reinterpret_cast<const uint32_t*>(as_ptr[rt] + (kt + u) * cap * 4);
+                a[u][rt] = ld16(a_ptr[rt] + (kt + u) * 1024);
+            }
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) b[q] = ld16_nt(wb + int64_t(kt * 4 + q) * 1024);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                a[rt] = ld16(a2q + (((rowtile0 + rt) * KT + kt) * 64 + lane) * 16);
+        for (int u = 0; u < UU; ++u)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    acc[rt][q] = mfma_fp4_16x16x128(a[rt], b[q], acc[rt][q],
-                                                    (sa[rt] >> (8 * j)) & 0xFFu,
-                                                    (sw[q] >> (8 * j)) & 0xFFu);
-        }
-    }
+                    acc[rt][q] = mfma_fp4_16x16x128(a[u][rt], b[u][q], acc[rt][q],
+                                                    (sa[u][rt] >> ash) & 0xFFu,
+                                                    (sw[u] >> (8 * q)) & 0xFFu);
+    };
+    int kt = 0;
+    for (; kt + U <= KT; kt += U) steps(std::integral_constant<int, U>{}, kt);
+    for (; kt < KT; ++kt) steps(std::integral_constant<int, 1>{}, kt);
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -89,33 +107,36 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
         for (int i = 0; i < 4; ++i) {
             const int64_t srow = int64_t(blk) * BM + rt * 16 + 4 * (lane / 16) + i;
             const int sr = sorted_route[srow];
-            if (sr < R) {
-                const float w = sorted_w[srow];
-                uint16_t* dst = partial + int64_t(sr) * D + n64 * 64 + lane % 16;
+            const float w = sorted_w[srow];
+            uint16_t* dst = partial + int64_t(sr) * D + n64 * 64 + lane % 16;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q * 16] = uint16_t(f32_to_bf16_rne(w * acc[rt][q][i]));
+            for (int q = 0; q < 4; ++q) {
+                // columns lane%16 and lane%16 + 1 as one dword from the even lane
+                const uint32_t v = f32_to_bf16_rne(w * acc[rt][q][i]);
+                const uint32_t pair = v | (dpp<kDppXor1>(v) << 16);
+                if (sr < R && (lane & 1) == 0) *reinterpret_cast<uint32_t*>(dst + q * 16) = pair;
             }
         }
     }
 }
 
-template <int RT, int G>
+template <int RT>
 static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm2_weighted_kernel<RT, G>), dim3(a.D / 256, a.nb_cap),
+    hipLaunchKernelGGL((gemm2_weighted_kernel<RT>), dim3(a.D / 256, a.nb_cap),
                        dim3(kGemmThreads), 0, stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
-                       a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk);
+                       a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk,
+                       a.cap);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream)
 {
     if (a.nb_cap == 0) return hipSuccess;
-    const bool g4 = (a.I % 512) == 0;
     switch (a.block_m) {
-    case 16: return g4 ? launch_g2<1, 4>(a, stream) : launch_g2<1, 2>(a, stream);
-    case 32: return g4 ? launch_g2<2, 4>(a, stream) : launch_g2<2, 2>(a, stream);
-    case 64: return g4 ? launch_g2<4, 4>(a, stream) : launch_g2<4, 2>(a, stream);
+    case 16: return launch_g2<1>(a, stream);
+    case 32: return launch_g2<2>(a, stream);
+    case 64: return launch_g2<4>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -63,6 +63,44 @@ __device__ __forceinline__ uint32_t mx_code(uint32_t bits16, uint32_t s)
     return idx | ((bits16 >> 12) & 0x8u);
 }
 
+// ------------------------------------------------------- lane exchange ---
+//
+// DPP moves within rows of 16 lanes (a VALU operand modifier, no LDS round
+// trip): quad_perm xor 1 / xor 2, row rotate by 4 / 8, row shift so that
+// lane l reads lane l + n of its row (lanes past the row end read 0).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;    // row_ror:4
+constexpr int kDppRor8 = 0x128;    // row_ror:8
+template <int N>
+__device__ __forceinline__ uint32_t from_lane_plus(uint32_t v) { return dpp<0x100 + N>(v); }  // row_shl:N
+
+// Maximum over each row of 16 lanes, returned in every lane of the row.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
+{
+    v = max(v, dpp<kDppXor1>(v));
+    v = max(v, dpp<kDppXor2>(v));
+    v = max(v, dpp<kDppRor4>(v));
+    v = max(v, dpp<kDppRor8>(v));
+    return v;
+}
+
+// Pack the E2M1 codes of 8 consecutive lanes (element = lane) into a dword
+// held by lanes l % 8 == 0: element 2b in the low nibble of byte b.
+__device__ __forceinline__ uint32_t pack8_codes(uint32_t code)
+{
+    const uint32_t b = code | (dpp<kDppXor1>(code) << 4);
+    const uint32_t p2 = b | (from_lane_plus<2>(b) << 8);
+    return p2 | (from_lane_plus<4>(p2) << 16);
+}
+
+__device__ __forceinline__ float silu_fast(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }
+
 // ------------------------------------------------------------- MFMA -----
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 (format code 4).
@@ -93,19 +131,24 @@ __device__ __forceinline__ uint4 ld16_nt(const uint8_t* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// G (2 or 4) consecutive scale bytes as one word.
-template <int G>
-__device__ __forceinline__ uint32_t ld_scales(const uint8_t* p)
+// ------------------------------------------------- fragment layout -------
+//
+// Sorted-row MXFP4 operands (the gathered activations of the tiled path and
+// the stage-1 output h) are stored so that every wave-load is one contiguous
+// run: on gfx950 the vector memory path handles a load whose 64 lane
+// addresses are consecutive 16 B (or 4 B) chunks about four times faster than
+// one that touches several rows.
+//   codes  [rows/16][K/128][4 chunks of 32][16 rows][16 B]
+//   scales [K/128][rows][4 B]       (byte j = 32-block kt*4 + j of the row)
+// A 16x16x128 or 32x32x64 MFMA operand of 16 rows at K tile kt is then the
+// 1 KiB at frag_code_off(row0, kt, 0, KT), lane L holding row L%16, chunk L/16.
+__device__ __host__ __forceinline__ int64_t frag_code_off(int64_t row, int kt, int chunk, int KT)
 {
-    if constexpr (G == 4) return *reinterpret_cast<const uint32_t*>(p);
-    else return *reinterpret_cast<const uint16_t*>(p);
+    return (((row >> 4) * KT + kt) * 64 + chunk * 16 + (row & 15)) * 16;
 }
-
-// Position of 32-block kb inside a row of activation scales, grouped so that
-// lane L's G bytes for K tiles kg*G .. kg*G+G-1 are adjacent.
-__device__ __host__ __forceinline__ int act_scale_pos(int kb, int G)
+__device__ __host__ __forceinline__ int64_t frag_scale_off(int64_t row, int kt, int64_t rows)
 {
-    return (kb / (4 * G)) * (4 * G) + (kb % 4) * G + (kb / 4) % G;
+    return (int64_t(kt) * rows + row) * 4;
 }
 
 }  // namespace moe

@@ -14,7 +14,7 @@ hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int top
                              int32_t* block_expert, int32_t* num_valid, hipStream_t stream);
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                             uint8_t* scales, int scale_G, int n_cu, hipStream_t stream);
+                             uint8_t* scales, int n_cu, hipStream_t stream);
 
 // Route sort (workgroup 0) + activation quantization (the other workgroups).
 struct PrologueArgs {
@@ -25,7 +25,7 @@ struct PrologueArgs {
     float* sorted_w;
     int32_t *block_expert, *num_valid;
     const uint16_t* hidden;
-    int D, scale_G;
+    int D;
     uint8_t *a1q, *a1s;
 };
 hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream);
@@ -34,17 +34,28 @@ hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, u
                           uint8_t* dst_scales, int E, int N, int K, int gate_up_I, int inverse,
                           int n_cu, hipStream_t stream);
 
+// Gather the token-major activations a1 into sorted-row fragment layout
+// (tiled path), padding rows zeroed.
+hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_t* sorted_route,
+                            const int32_t* num_valid, int M, int D, int topk, int64_t cap,
+                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream);
+
+// a2 (fragment layout) -> canonical row-major codes [cap][I/2] and scales [cap][I/32].
+hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t cap, int I,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 struct Gemm1Args {
-    const uint8_t *a1q, *a1s, *w13p, *w13sp;
+    const uint8_t *a1q, *a1s;      // token-major activations (streaming kernels)
+    const uint8_t *a1f, *a1fs;     // sorted fragment-layout activations (tiled kernels)
+    const uint8_t *w13p, *w13sp;
     const int32_t *sorted_route, *block_expert, *num_valid;
-    uint8_t *a2q, *a2s;
+    uint8_t *a2q, *a2s;            // h in fragment layout, rows = cap
     uint16_t* h_dbg;
     int M, D, I, topk, block_m, nb_cap;
+    int64_t cap;
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
 
-hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t rows, int I,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 struct Gemm2Args {
     const uint8_t *a2q, *a2s, *w2p, *w2sp;
@@ -53,8 +64,14 @@ struct Gemm2Args {
     const int32_t *block_expert, *num_valid;
     uint16_t* partial;          // bf16 [M*topk][D], weighted contribution per route
     int M, D, I, topk, block_m, nb_cap;
+    int64_t cap;
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
+
+// LDS-tiled variants for block_m = 256.
+hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
+hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream);
+hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream);
 
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
                                int topk, uint16_t* out, int n_cu, hipStream_t stream);

@@ -169,11 +169,10 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
 }
 
 // MXFP4 quantization of rows of bf16 (grid-stride over 8-element chunks, four
-// lanes per 32-element block).  scale_G = 0: scales row-major [rows][cols/32];
-// otherwise the grouped activation layout of act_scale_pos(., scale_G).
+// lanes per 32-element block): codes [rows][cols/2], scales [rows][cols/32].
 __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                 uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                int scale_G, int64_t block, int64_t nblocks, int nthreads)
+                                int64_t block, int64_t nblocks, int nthreads)
 {
     const int64_t chunks_per_row = cols / 8;
     const int64_t n_chunks = rows * chunks_per_row;
@@ -189,8 +188,8 @@ __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, in
             amax = max(amax, w[j] & 0x7FFFu);
             amax = max(amax, (w[j] >> 16) & 0x7FFFu);
         }
-        amax = max(amax, uint32_t(__shfl_xor(int(amax), 1)));
-        amax = max(amax, uint32_t(__shfl_xor(int(amax), 2)));
+        amax = max(amax, dpp<kDppXor1>(amax));      // the block's four lanes
+        amax = max(amax, dpp<kDppXor2>(amax));
         const uint32_t s = mx_scale_from_amax(amax);
         uint32_t packed = 0;
 #pragma unroll
@@ -201,10 +200,7 @@ __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, in
         if (in) {
             reinterpret_cast<uint32_t*>(codes)[i] = packed;
             if ((i & 3) == 0) {
-                const int64_t row = i / chunks_per_row;
-                const int kb = int((i % chunks_per_row) / 4);
-                const int pos = scale_G ? act_scale_pos(kb, scale_G) : kb;
-                scales[row * (cols / 32) + pos] = uint8_t(s);
+                scales[i / 4] = uint8_t(s);        // block index = chunk index / 4
             }
         }
     }
@@ -224,10 +220,9 @@ route_sort_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw,
 
 __global__ void __launch_bounds__(kPrologueThreads)
 quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int scale_G)
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    quant_rows_body(x, rows, cols, codes, scales, scale_G, blockIdx.x, gridDim.x,
-                    kPrologueThreads);
+    quant_rows_body(x, rows, cols, codes, scales, blockIdx.x, gridDim.x, kPrologueThreads);
 }
 
 template <int U>
@@ -239,9 +234,59 @@ prologue_kernel(PrologueArgs a)
         route_sort_body<U>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
                            a.sorted_w, a.block_expert, a.num_valid, lds);
     } else {
-        quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, a.scale_G, blockIdx.x - 1,
-                        gridDim.x - 1, kPrologueThreads);
+        quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, blockIdx.x - 1, gridDim.x - 1,
+                        kPrologueThreads);
     }
+}
+
+// Sorted-row fragment copy of the quantized activations for the tiled
+// kernels: one thread per (sorted row, K tile), 64 code bytes + one scale word.
+// Consecutive threads take consecutive rows of a 16-row slice, so each store
+// instruction writes 256 contiguous bytes.  Rows past num_valid[0] are left
+// alone (never read); padding rows are zero.
+__global__ void __launch_bounds__(256)
+gather_a1_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
+                 const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ num_valid,
+                 int M, int D, int topk, int64_t cap, uint8_t* __restrict__ a1f,
+                 uint8_t* __restrict__ a1fs)
+{
+    const int KT = D / 128;
+    const int64_t rows = num_valid[0];
+    const int64_t n = rows * KT;
+    const int R = M * topk;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t slice = i / (16 * KT);
+        const int kt = int((i / 16) % KT);
+        const int64_t row = slice * 16 + (i % 16);
+        const int sr = sorted_route[row];
+        uint4 v[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                      make_uint4(0, 0, 0, 0)};
+        uint32_t sc = 0;
+        if (sr < R) {
+            const int64_t tok = sr / topk;
+            const uint8_t* src = a1q + tok * (D / 2) + kt * 64;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = ld16(src + c * 16);
+            sc = *reinterpret_cast<const uint32_t*>(a1s + tok * (D / 32) + kt * 4);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(a1f + frag_code_off(row, kt, c, KT)) = v[c];
+        *reinterpret_cast<uint32_t*>(a1fs + frag_scale_off(row, kt, cap)) = sc;
+    }
+}
+
+hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_t* sorted_route,
+                            const int32_t* num_valid, int M, int D, int topk, int64_t cap,
+                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream)
+{
+    const int64_t n = cap * (D / 128);
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > int64_t(n_cu) * 8) blocks = int64_t(n_cu) * 8;
+    hipLaunchKernelGGL(gather_a1_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a1q, a1s,
+                       sorted_route, num_valid, M, D, topk, cap, a1f, a1fs);
+    return hipGetLastError();
 }
 
 size_t route_lds_bytes(int E) { return sizeof(int32_t) * (size_t(kRouteWaves) * E + 2 * kRouteWaves); }
@@ -284,12 +329,12 @@ static int64_t quant_blocks(int64_t rows, int64_t cols, int n_cu)
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
-                             uint8_t* scales, int scale_G, int n_cu, hipStream_t stream)
+                             uint8_t* scales, int n_cu, hipStream_t stream)
 {
     const int64_t blocks = quant_blocks(rows, cols, n_cu);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), 0,
-                       stream, x, rows, cols, codes, scales, scale_G);
+                       stream, x, rows, cols, codes, scales);
     return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ def _route_cases():
     return out
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("case", _route_cases(), ids=lambda c: c[0])
 def test_route_matches_oracle(binding, case, bm):
     name, M, E, n_routed, routing, seed = case
@@ -135,13 +135,13 @@ def _layout_reference(raw_codes, raw_scales, N, K, gate_up_I):
     else:
         perm = rows
     KT = K // 128
-    G = 4 if K % 512 == 0 else 2
     codes = raw_codes[perm]                              # prepared row order [N, K/2]
     # [N/64, 4, 16, KT, 4(k-chunk), 16B] -> [N/64, KT, 4, (k-chunk, 16 rows), 16B]
     t = codes.reshape(N // 64, 4, 16, KT, 4, 16).transpose(0, 3, 1, 4, 2, 5)
     pc = t.reshape(-1)
     sc = raw_scales[perm]                                 # [N, K/32]
-    s = sc.reshape(N // 64, 4, 16, KT // G, G, 4).transpose(0, 3, 1, 5, 2, 4)
+    # [N/64, 4(q), 16, KT, 4(k-chunk)] -> [N/64, KT, (k-chunk, 16 rows), q]
+    s = sc.reshape(N // 64, 4, 16, KT, 4).transpose(0, 3, 4, 2, 1)
     ps = s.reshape(-1)
     return pc, ps
 
@@ -223,6 +223,8 @@ def test_forward_workload_sampled(binding, name, n_sample):
     (37, 768, 768, 5, 3, 22),         # ragged M, D and I not multiples of 512
     (130, 1024, 512, 33, 8, 23),      # several blocks per expert
     (3, 256, 256, 2, 1, 24),          # smallest dims
+    (1400, 512, 256, 5, 2, 25),       # LDS-tiled path (block_m 256), ragged blocks
+    (1000, 768, 512, 3, 1, 26),       # LDS-tiled path, D not a multiple of 512
 ])
 def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
