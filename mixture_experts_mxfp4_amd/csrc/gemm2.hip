@@ -18,10 +18,10 @@
 // to bf16 is bounded by 2^-9 of that contribution.
 //
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows and
-// 256 output columns; each wave owns 64 columns = 4 MFMA tiles per row tile
-// and runs the whole K = I loop, streaming 1 KiB weight fragments with
-// non-temporal loads; the A fragments (MXFP4 h, written by stage 1 in the
-// fragment layout) are contiguous 1 KiB loads as well.
+// 256*NG output columns; each wave owns NG groups of 64 columns (4 MFMA tiles
+// per row tile each) and runs the whole K = I loop for each, streaming 1 KiB
+// weight fragments with non-temporal loads; the A fragments (MXFP4 h, written
+// by stage 1 in the fragment layout) are contiguous 1 KiB loads as well.
 #include <type_traits>
 
 #include "moe_common.h"
@@ -36,7 +36,7 @@ constexpr int g2_unroll() { return RT <= 2 ? 4 : 2; }
 
 template <int RT>
 __global__ void __launch_bounds__(kGemmThreads)
-gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
+gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
                       const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
                       const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
                       const int32_t* __restrict__ block_expert,
@@ -120,23 +120,152 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
     }
 }
 
-template <int RT>
+// Each wave walks NG 64-column groups (group g of the wave's workgroup lies
+// at n64 = blockIdx.x*4*NG + g*4 + wave, so the four waves stream adjacent
+// groups); the K tiles of the whole walk are processed U at a time, and the
+// loads of the next U tiles are issued before the MFMAs of the current ones
+// (register double buffering), keeping 2 x U x 4 KiB in flight per wave.
+template <int RT, int U, int NG>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
+                      const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
+                      const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
+                      const int32_t* __restrict__ block_expert,
+                      const int32_t* __restrict__ num_valid, uint16_t* __restrict__ partial,
+                      int M, int D, int I, int topk, int64_t cap)
+{
+    constexpr int BM = 16 * RT;
+    const int blk = blockIdx.y;
+    if (blk * BM >= num_valid[0]) return;
+    const int e = block_expert[blk];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int KT = I / 128;                 // a multiple of U
+    const int R = M * topk;
+    const int n64_0 = blockIdx.x * 4 * NG + wave;
+
+    const uint8_t* wexp = w2p + int64_t(e) * D * (I / 2) + lane * 16;
+    const uint8_t* sexp = w2sp + int64_t(e) * D * (I / 32) + lane * 4;
+    // A operand: the 1 KiB fragment of row tile rt at K tile kt; scales kt-major
+    const uint8_t* a_ptr[RT];
+    const uint8_t* as_ptr[RT];
+    int sr[RT][4];
+    float wt[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t row0 = int64_t(blk) * BM + rt * 16;
+        a_ptr[rt] = a2q + frag_code_off(row0, 0, 0, KT) + lane * 16;
+        as_ptr[rt] = a2s + frag_scale_off(row0 + lane % 16, 0, cap);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sr[rt][i] = sorted_route[row0 + 4 * (lane / 16) + i];
+            wt[rt][i] = sorted_w[row0 + 4 * (lane / 16) + i];
+        }
+    }
+    const int ash = 8 * (lane / 16);
+
+    struct Chunk {
+        uint32_t sw[U], sa[U][RT];
+        uint4 b[U][4], a[U][RT];
+    };
+    // chunk c covers K tiles (c*U .. c*U+U-1) mod KT of group c*U / KT
+    auto load = [&](Chunk& ch, int c) {
+        const int g = (c * U) / KT, kt0 = (c * U) % KT;
+        const int64_t n64 = n64_0 + g * 4;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kt = kt0 + u;
+            ch.sw[u] = *reinterpret_cast<const uint32_t*>(sexp + (n64 * KT + kt) * 256);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ch.b[u][q] = ld16_nt(wexp + ((n64 * KT + kt) * 4 + q) * 1024);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                ch.sa[u][rt] = *reinterpret_cast<const uint32_t*>(as_ptr[rt] + int64_t(kt) * cap * 4);
+                ch.a[u][rt] = ld16(a_ptr[rt] + kt * 1024);
+            }
+        }
+    };
+    v4f acc[RT][4];
+    auto zero = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
+    auto compute = [&](const Chunk& ch) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[rt][q] = mfma_fp4_16x16x128(ch.a[u][rt], ch.b[u][q], acc[rt][q],
+                                                    (ch.sa[u][rt] >> ash) & 0xFFu,
+                                                    (ch.sw[u] >> (8 * q)) & 0xFFu);
+    };
+    auto store = [&](int c) {            // after the last chunk of a group
+        const int64_t n64 = n64_0 + ((c * U) / KT) * 4;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint16_t* dst = partial + int64_t(sr[rt][i]) * D + n64 * 64 + lane % 16;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // columns lane%16 and lane%16 + 1 as one dword from the even lane
+                    const uint32_t v = f32_to_bf16_rne(wt[rt][i] * acc[rt][q][i]);
+                    const uint32_t pair = v | (dpp<kDppXor1>(v) << 16);
+                    if (sr[rt][i] < R && (lane & 1) == 0)
+                        *reinterpret_cast<uint32_t*>(dst + q * 16) = pair;
+                }
+            }
+        }
+    };
+
+    const int nchunks = NG * KT / U;
+    Chunk c0, c1;
+    zero();
+    load(c0, 0);
+    for (int c = 0; c < nchunks; c += 2) {
+        if (c + 1 < nchunks) load(c1, c + 1);
+        compute(c0);
+        if (((c + 1) * U) % KT == 0) { store(c); zero(); }
+        if (c + 1 >= nchunks) break;
+        if (c + 2 < nchunks) load(c0, c + 2);
+        compute(c1);
+        if (((c + 2) * U) % KT == 0) { store(c + 1); zero(); }
+    }
+}
+
+template <int RT, int U, int NG>
 static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm2_weighted_kernel<RT>), dim3(a.D / 256, a.nb_cap),
+    hipLaunchKernelGGL((gemm2_weighted_kernel<RT, U, NG>), dim3(a.D / (256 * NG), a.nb_cap),
                        dim3(kGemmThreads), 0, stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
                        a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk,
                        a.cap);
     return hipGetLastError();
 }
 
+template <int RT>
+static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm2_simple_kernel<RT>), dim3(a.D / 256, a.nb_cap), dim3(kGemmThreads), 0,
+                       stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w,
+                       a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
+    return hipGetLastError();
+}
+
+// Few rows per block (decode, block_m 16): each wave walks two column groups
+// with double-buffered loads, which keeps enough weight bytes in flight with
+// half the workgroups.  Larger blocks keep one group per wave (their
+// register budget goes to the extra row tiles).
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream)
 {
     if (a.nb_cap == 0) return hipSuccess;
     switch (a.block_m) {
-    case 16: return launch_g2<1>(a, stream);
-    case 32: return launch_g2<2>(a, stream);
-    case 64: return launch_g2<4>(a, stream);
+    case 16: return (a.D / 256) % 2 == 0 ? launch_g2<1, 2, 2>(a, stream) : launch_g2<1, 2, 1>(a, stream);
+    case 32: return launch_g2_simple<2>(a, stream);
+    case 64: return launch_g2_simple<4>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

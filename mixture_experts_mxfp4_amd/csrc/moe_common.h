@@ -34,10 +34,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 // block); each element becomes the E2M1 code nearest to |x| / X, ties to the
 // even mantissa, saturating at 6, with the sign bit of x.
 //
-// Inputs are bf16 bit patterns, so everything below is exact: the block
-// maximum is taken on the 15 magnitude bits (monotonic for finite values), the
-// scale byte comes from its exponent field, and |x| / X is rebuilt as
-// significand * 2^p without ever forming an fp32 denormal.
+// Inputs are bf16 bit patterns: the block maximum is taken on the 15
+// magnitude bits (monotonic for finite values) and the scale byte comes from
+// its exponent field.
 
 // e8m0 scale byte from the largest |x| (15-bit magnitude pattern) of a block.
 __device__ __forceinline__ uint32_t mx_scale_from_amax(uint32_t amax_mag)
@@ -46,21 +45,26 @@ __device__ __forceinline__ uint32_t mx_scale_from_amax(uint32_t amax_mag)
     return ea >= 2u ? ea - 2u : 0u;           // floor(log2 amax) - 2 + 127, clamped at 0
 }
 
-// E2M1 code of one bf16 element under scale byte s.
+// E2M1 codes under scale byte s with gfx950's scaled conversion
+// v_cvt_scalef32_pk_fp4_f32: it divides by the power of two 2^(s-127) held in
+// the scale operand's exponent field, rounds to nearest even and saturates at
+// 6, keeping the sign.  For every finite bf16 input with |x| / 2^(s-127) < 8
+// (always the case when s comes from the block maximum) and every scale byte
+// 0..254 its codes equal the OCP rule above bit for bit (checked exhaustively
+// on the device; the GPU tests compare the quantizer with the CPU reference).
+__device__ __forceinline__ float mx_scale_operand(uint32_t s)
+{
+    return __builtin_bit_cast(float, s << 23);
+}
+// two elements -> one byte: x0 in the low nibble, x1 in the high nibble
+__device__ __forceinline__ uint32_t mx_code2(uint32_t bits0, uint32_t bits1, uint32_t s)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, bf16_to_f32(bits0), bf16_to_f32(bits1),
+                                                    mx_scale_operand(s), 0) & 0xFFu;
+}
 __device__ __forceinline__ uint32_t mx_code(uint32_t bits16, uint32_t s)
 {
-    uint32_t mag = bits16 & 0x7FFFu;
-    uint32_t ex = mag >> 7, man = mag & 0x7Fu;
-    int sig = ex ? int(128u | man) : int(man);
-    int p = (ex ? int(ex) - 134 : -133) + 127 - int(s);        // |x| / X = sig * 2^p
-    float v = 0.0f;
-    if (p >= -30) v = float(sig) * __builtin_bit_cast(float, uint32_t(p + 127) << 23);
-    // round to nearest even onto {0, .5, 1, 1.5, 2, 3, 4, 6}: midpoints
-    // .25 .75 1.25 1.75 2.5 3.5 5, a midpoint going to the even neighbour
-    uint32_t idx = uint32_t(v > 0.25f) + uint32_t(v >= 0.75f) + uint32_t(v > 1.25f) +
-                   uint32_t(v >= 1.75f) + uint32_t(v > 2.5f) + uint32_t(v >= 3.5f) +
-                   uint32_t(v > 5.0f);
-    return idx | ((bits16 >> 12) & 0x8u);
+    return mx_code2(bits16, bits16, s) & 0xFu;
 }
 
 // ------------------------------------------------------- lane exchange ---
@@ -97,6 +101,19 @@ __device__ __forceinline__ uint32_t pack8_codes(uint32_t code)
     const uint32_t b = code | (dpp<kDppXor1>(code) << 4);
     const uint32_t p2 = b | (from_lane_plus<2>(b) << 8);
     return p2 | (from_lane_plus<4>(p2) << 16);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// rows of 16, then row broadcasts of lane 15 / lane 31 into later rows).
+__device__ __forceinline__ int wave_inclusive_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return x;
 }
 
 __device__ __forceinline__ float silu_fast(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }

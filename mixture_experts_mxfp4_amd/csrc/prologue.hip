@@ -17,10 +17,11 @@
 //   pass 2  the same walk again; each route lands at start + rank among equal
 //           lanes, so every expert's list is in ascending route order and the
 //           output is deterministic.
-// The code is kept compact (no unrolling) for short route lists: a kernel
-// that one workgroup runs once is bound by instruction fetch and memory
-// latency, not by arithmetic.  Long lists use a 4x unrolled walk that keeps
-// more loads in flight.
+// Short route lists (M*topk <= 4096, decode) are sorted by a single wave
+// instead (route_sort_wave): a kernel that one workgroup runs once is bound by
+// barriers, instruction fetch and memory latency, not by arithmetic.  Long
+// lists use the workgroup sort with a 4x unrolled walk that keeps more loads
+// in flight.
 //
 // Activation quantization (OCP MX v1.0; the FP4 branch of 754773 quantizes
 // the hidden states per 32 elements before the gate_up GEMM): four lanes own
@@ -168,6 +169,94 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     }
 }
 
+// The same route sort for short route lists (decode): the workgroup stages
+// topk_ids / topk_w in LDS with one coalesced load, then ONE wave sorts from
+// LDS (one histogram row, DPP wave scans, no further barriers).  The output
+// order is identical to route_sort_body's (ascending route per expert).
+constexpr int kShortList = 4096;
+
+__device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* __restrict__ tw_g,
+                                int M, int topk, int E, int bm, int nb_cap,
+                                int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
+                                int32_t* __restrict__ block_expert,
+                                int32_t* __restrict__ num_valid, int32_t* lds)
+{
+    int32_t* ids = lds;                                          // [R]
+    float* tw = reinterpret_cast<float*>(lds + kShortList);      // [R]
+    int32_t* cnt = lds + 2 * kShortList;                         // [E]
+    for (int r = threadIdx.x; r < M * topk; r += kPrologueThreads) {
+        ids[r] = ids_g[r];
+        tw[r] = tw_g[r];
+    }
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;
+    const int lane = threadIdx.x;
+    const int R = M * topk;
+    const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+#pragma unroll 1
+    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // pass 1: histogram
+#pragma unroll 1
+    for (int base = 0; base < R; base += kWave) {
+        const int r = base + lane;
+        const int id = r < R ? ids[r] : -1;
+        const bool valid = id >= 0 && id < E;
+        const uint64_t peers = same_expert_lanes(id, valid, nbits);
+        if (valid && (peers & lanes_below) == 0) cnt[id] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+    // scan of padded counts; cnt[e] becomes the expert's first row
+    int carry = 0, vcarry = 0;
+#pragma unroll 1
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        const int total = e < E ? cnt[e] : 0;
+        const int padded = (total + bm - 1) / bm * bm;
+        const int inc = wave_inclusive_scan(padded);
+        const int vinc = wave_inclusive_scan(total);
+        const int base_e = carry + inc - padded;
+        if (e < E) {
+            cnt[e] = base_e;
+#pragma unroll 1
+            for (int p = base_e + total; p < base_e + padded; ++p) {
+                sorted_route[p] = R;
+                sorted_w[p] = 0.0f;
+            }
+#pragma unroll 1
+            for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
+        }
+        carry += __builtin_amdgcn_readlane(inc, kWave - 1);
+        vcarry += __builtin_amdgcn_readlane(vinc, kWave - 1);
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int b = carry / bm + lane; b < nb_cap; b += kWave) block_expert[b] = -1;
+    if (lane == 0) {
+        num_valid[0] = carry;
+        num_valid[1] = vcarry;
+    }
+    // pass 2: stable scatter
+#pragma unroll 1
+    for (int base = 0; base < R; base += kWave) {
+        const int r = base + lane;
+        const int id = r < R ? ids[r] : -1;
+        const float wt = r < R ? tw[r] : 0.0f;
+        const bool valid = id >= 0 && id < E;
+        const uint64_t peers = same_expert_lanes(id, valid, nbits);
+        const int start = valid ? cnt[id] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            const int pos = start + __popcll(peers & lanes_below);
+            sorted_route[pos] = r;
+            sorted_w[pos] = wt;
+            if ((peers & lanes_below) == 0) cnt[id] = start + __popcll(peers);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // MXFP4 quantization of rows of bf16 (grid-stride over 8-element chunks, four
 // lanes per 32-element block): codes [rows][cols/2], scales [rows][cols/32].
 __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
@@ -193,10 +282,7 @@ __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, in
         const uint32_t s = mx_scale_from_amax(amax);
         uint32_t packed = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t c0 = mx_code(w[j] & 0xFFFFu, s), c1 = mx_code(w[j] >> 16, s);
-            packed |= (c0 | (c1 << 4)) << (8 * j);
-        }
+        for (int j = 0; j < 4; ++j) packed |= mx_code2(w[j] & 0xFFFFu, w[j] >> 16, s) << (8 * j);
         if (in) {
             reinterpret_cast<uint32_t*>(codes)[i] = packed;
             if ((i & 3) == 0) {
@@ -206,6 +292,7 @@ __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, in
     }
 }
 
+// U = 0: single-wave sort (short lists); otherwise the workgroup sort.
 template <int U>
 __global__ void __launch_bounds__(kPrologueThreads)
 route_sort_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw, int M,
@@ -214,8 +301,13 @@ route_sort_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw,
                   int32_t* __restrict__ num_valid)
 {
     extern __shared__ int32_t lds[];
-    route_sort_body<U>(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w, block_expert,
-                       num_valid, lds);
+    if constexpr (U == 0) {
+        route_sort_wave(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w, block_expert,
+                        num_valid, lds);
+    } else {
+        route_sort_body<U>(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w,
+                           block_expert, num_valid, lds);
+    }
 }
 
 __global__ void __launch_bounds__(kPrologueThreads)
@@ -231,8 +323,13 @@ prologue_kernel(PrologueArgs a)
 {
     extern __shared__ int32_t lds[];
     if (blockIdx.x == 0) {
-        route_sort_body<U>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
-                           a.sorted_w, a.block_expert, a.num_valid, lds);
+        if constexpr (U == 0) {
+            route_sort_wave(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
+                            a.sorted_w, a.block_expert, a.num_valid, lds);
+        } else {
+            route_sort_body<U>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
+                               a.sorted_w, a.block_expert, a.num_valid, lds);
+        }
     } else {
         quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, blockIdx.x - 1, gridDim.x - 1,
                         kPrologueThreads);
@@ -289,15 +386,20 @@ hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_
     return hipGetLastError();
 }
 
-size_t route_lds_bytes(int E) { return sizeof(int32_t) * (size_t(kRouteWaves) * E + 2 * kRouteWaves); }
+size_t route_lds_bytes(int E)
+{
+    const size_t wg = size_t(kRouteWaves) * E + 2 * kRouteWaves;    // workgroup sort
+    const size_t wave = 2 * size_t(kShortList) + E;                  // single-wave sort
+    return sizeof(int32_t) * (wg > wave ? wg : wave);
+}
 
-static bool long_list(int M, int topk) { return int64_t(M) * topk > 4096; }
+static bool long_list(int M, int topk) { return int64_t(M) * topk > kShortList; }
 
 hipError_t route_allow_lds(int bytes)
 {
-    const void* k[] = {reinterpret_cast<const void*>(&route_sort_kernel<1>),
+    const void* k[] = {reinterpret_cast<const void*>(&route_sort_kernel<0>),
                        reinterpret_cast<const void*>(&route_sort_kernel<4>),
-                       reinterpret_cast<const void*>(&prologue_kernel<1>),
+                       reinterpret_cast<const void*>(&prologue_kernel<0>),
                        reinterpret_cast<const void*>(&prologue_kernel<4>)};
     for (const void* f : k) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -315,7 +417,7 @@ hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int top
                            route_lds_bytes(E), stream, ids, tw, M, topk, E, bm, nb_cap,
                            sorted_route, sorted_w, block_expert, num_valid);
     else
-        hipLaunchKernelGGL(route_sort_kernel<1>, dim3(1), dim3(kPrologueThreads),
+        hipLaunchKernelGGL(route_sort_kernel<0>, dim3(1), dim3(kPrologueThreads),
                            route_lds_bytes(E), stream, ids, tw, M, topk, E, bm, nb_cap,
                            sorted_route, sorted_w, block_expert, num_valid);
     return hipGetLastError();
@@ -345,7 +447,7 @@ hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream)
         hipLaunchKernelGGL(prologue_kernel<4>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
                            route_lds_bytes(a.E), stream, a);
     else
-        hipLaunchKernelGGL(prologue_kernel<1>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
+        hipLaunchKernelGGL(prologue_kernel<0>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
                            route_lds_bytes(a.E), stream, a);
     return hipGetLastError();
 }

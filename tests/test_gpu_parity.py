@@ -61,6 +61,37 @@ def test_quantize_bit_exact(binding, rows, cols):
     np.testing.assert_array_equal(codes.cpu().numpy(), oc)
 
 
+def _domain_blocks():
+    """Every finite bf16 value under every reachable scale byte s (0..252), in
+    blocks of 32 whose first element fixes the block maximum (and so s):
+    the largest bf16 with exponent field s + 2 (2 for s = 0); the other 31
+    elements run through every bf16 whose exponent field is <= that, both
+    signs.  About 8.4 M elements."""
+    blocks = []
+    for s in range(0, 253):
+        e_max = max(s + 2, 2)
+        amax = np.uint16((e_max << 7) | 0x7F)
+        mags = np.arange(0, (e_max + 1) << 7, dtype=np.uint32).astype(np.uint16)
+        vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+        n = -(-vals.size // 31) * 31
+        vals = np.concatenate([vals, np.zeros(n - vals.size, np.uint16)]).reshape(-1, 31)
+        blocks.append(np.concatenate([np.full((vals.shape[0], 1), amax, np.uint16), vals], 1))
+    b = np.concatenate(blocks).reshape(-1)
+    pad = -(-b.size // 256) * 256 - b.size
+    return np.concatenate([b, np.zeros(pad, np.uint16)]).reshape(-1, 256)
+
+
+def test_quantize_whole_domain_bit_exact(binding):
+    """The device quantizer equals the oracle on its whole input domain."""
+    bits = _domain_blocks()
+    log(f"quantize whole domain: {bits.size} elements")
+    codes, scales = binding.moe_mxfp4_quantize(inputs.bits_to_bf16(bits).cuda())
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_rows(bits)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
 def test_quantize_weights_of_decode_bit_exact(binding):
     """The product quantizer on the decode workload's full gate_up weight."""
     w = inputs.WORKLOADS["decode"]
