@@ -53,6 +53,13 @@ enum {
     MOE_MXFP4_ERR_HIP = 4           /* a HIP runtime call or launch failed       */
 };
 
+/* Kernel paths of the forward (moe_mxfp4_path). */
+enum {
+    MOE_MXFP4_PATH_DIRECT = 1,      /* few tokens: route-indexed, no route sort  */
+    MOE_MXFP4_PATH_STREAM = 2,      /* expert-sorted, weight-streaming kernels   */
+    MOE_MXFP4_PATH_TILED = 3        /* expert-sorted, LDS-tiled kernels          */
+};
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_mxfp4_status_string(int status);
 
@@ -101,9 +108,13 @@ int moe_mxfp4_unprepare_weights(const uint8_t* w13p, const uint8_t* w13p_scale,
  * out[t, :] = bf16( sum_{s < topk, 0 <= e < E} topk_w[t, s] *
  *                   W2[e] . Q( bf16( silu(Wg[e] . Q(hidden[t])) * (Wu[e] . Q(hidden[t])) ) ) )
  * with e = topk_ids[t, s], Q = MXFP4 quantization per 32 along K, dot products
- * of MXFP4 operands accumulated in fp32; each weighted expert contribution
- * rounded to bf16, the per-token sum over slots in fp32 in slot order and one
- * final rounding to bf16 (deterministic).
+ * of MXFP4 operands accumulated in fp32, the per-token sum over slots in fp32
+ * and one final rounding to bf16.  The result is deterministic; the order of
+ * that sum depends on the path (moe_mxfp4_path): on the sorted paths each
+ * weighted contribution is rounded to bf16 and the sum runs in slot order; on
+ * the DIRECT path the contributions stay fp32 and the sum runs over the
+ * experts in descending id order (partial sums of 16 interleaved subsets,
+ * then added in a fixed order).
  *
  *   hidden    bf16 [M, D]            activations
  *   w13..     prepared weights from moe_mxfp4_prepare_weights
@@ -127,8 +138,14 @@ int moe_mxfp4_forward(const uint16_t* hidden,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* The block_m (rows per expert block of the sorted route list) the forward
- * uses for this shape, and the capacity (rows) of the sorted route list. */
+/* The kernel path the forward takes for this shape (0 for an invalid shape):
+ * DIRECT when M <= 32, topk <= 16, E <= 1024 and block_m is 16; else TILED when
+ * block_m is 256; else STREAM.  The choice depends on the shape only. */
+int moe_mxfp4_path(int M, int D, int I, int E, int topk);
+
+/* The block_m (rows per expert block of the sorted route list; the row tile
+ * of the DIRECT path) the forward uses for this shape, and the capacity
+ * (rows) of the sorted route list. */
 int moe_mxfp4_block_m(int M, int D, int I, int E, int topk);
 int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m);
 
@@ -155,11 +172,14 @@ int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w,
                     hipStream_t stream);
 
 /* Forward that also exports its intermediates (any pointer may be NULL):
- *   sorted_route i32 [cap], num_valid i32 [2]      the route list it used
- *   h            bf16 [cap, I]  silu(gate)*up per sorted row, before requant
+ *   sorted_route i32 [cap], num_valid i32 [2]      the row -> route map it used
+ *   h            bf16 [cap, I]  silu(gate)*up per row, before requant
  *   a2_codes     u8   [cap, I/2], a2_scales u8 [cap, I/32]  its MXFP4 form
- * Rows of padding are unspecified.  cap as for moe_mxfp4_route with the
- * block_m of moe_mxfp4_block_m. */
+ * On the sorted paths the rows are the sorted route list (as moe_mxfp4_route
+ * with the block_m of moe_mxfp4_block_m); on the DIRECT path row r is route
+ * r (sorted_route[r] = r, or M*topk for an invalid id; num_valid = {M*topk,
+ * valid routes}).  Rows of padding and of invalid routes are unspecified.
+ * cap = moe_mxfp4_route_capacity(M, E, topk, block_m) >= M*topk. */
 int moe_mxfp4_forward_debug(const uint16_t* hidden,
                             const uint8_t* w13, const uint8_t* w13_scale,
                             const uint8_t* w2, const uint8_t* w2_scale,
@@ -173,7 +193,8 @@ int moe_mxfp4_forward_debug(const uint16_t* hidden,
 
 /* Forward that records caller-created HIP events on `stream` at the stage
  * boundaries, for timing: stage_events[0] before the prologue (route sort and
- * activation quant, one launch), [1] after it, [2] after stage 1 (gate_up +
+ * activation quant, one launch; none on the DIRECT path, whose stage 1
+ * quantizes the activations itself), [1] after it, [2] after stage 1 (gate_up +
  * SwiGLU + requant), [3] after stage 2 (down projection x routing weight),
  * [4] after the per-token sum over slots.  Any entry (or the array) may be
  * NULL.  The events are only recorded; the caller reads them after

@@ -24,6 +24,7 @@ _lib.moe_mxfp4_status_string.argtypes, _lib.moe_mxfp4_status_string.restype = [_
 _lib.moe_mxfp4_workspace_bytes.argtypes = [_I] * 5
 _lib.moe_mxfp4_workspace_bytes.restype = _SZ
 _lib.moe_mxfp4_block_m.argtypes, _lib.moe_mxfp4_block_m.restype = [_I] * 5, _I
+_lib.moe_mxfp4_path.argtypes, _lib.moe_mxfp4_path.restype = [_I] * 5, _I
 _lib.moe_mxfp4_route_capacity.argtypes = [_I] * 4
 _lib.moe_mxfp4_route_capacity.restype = _I64
 for _name in ("moe_mxfp4_prepare_weights", "moe_mxfp4_unprepare_weights"):
@@ -41,6 +42,7 @@ _lib.moe_mxfp4_route.argtypes = [_P, _P] + [_I] * 4 + [_P] * 4 + [_P]
 _lib.moe_mxfp4_route.restype = _I
 
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
+           "moe_mxfp4_path",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
            "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
            "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled")
@@ -87,6 +89,15 @@ def moe_mxfp4_workspace_bytes(M, D, I, E, topk) -> int:
 
 def moe_mxfp4_block_m(M, D, I, E, topk) -> int:
     return int(_lib.moe_mxfp4_block_m(M, D, I, E, topk))
+
+
+PATH_DIRECT, PATH_STREAM, PATH_TILED = 1, 2, 3
+PATH_NAMES = {PATH_DIRECT: "direct", PATH_STREAM: "stream", PATH_TILED: "tiled"}
+
+
+def moe_mxfp4_path(M, D, I, E, topk) -> int:
+    """Kernel path of the forward for this shape (PATH_DIRECT / _STREAM / _TILED; 0 if invalid)."""
+    return int(_lib.moe_mxfp4_path(M, D, I, E, topk))
 
 
 def moe_mxfp4_route_capacity(M, E, topk, block_m) -> int:
@@ -198,7 +209,8 @@ def moe_mxfp4_forward_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk
            _lib.moe_mxfp4_forward_debug(*args, _ptr(sr), _ptr(nv), _ptr(h), _ptr(a2c), _ptr(a2s),
                                         _stream(stream)))
     return {"out": out, "sorted_route": sr[:cap], "num_valid": nv[:2], "h": h[:cap],
-            "a2_codes": a2c[:cap], "a2_scales": a2s[:cap], "block_m": bm, "cap": cap}
+            "a2_codes": a2c[:cap], "a2_scales": a2s[:cap], "block_m": bm, "cap": cap,
+            "path": moe_mxfp4_path(M, D, I, E, topk)}
 
 
 def moe_mxfp4_quantize(x, codes=None, scales=None, stream=None):

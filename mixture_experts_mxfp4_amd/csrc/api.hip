@@ -1,9 +1,13 @@
 // C ABI of the fused MXFP4 MoE forward (declared in include/moe_mxfp4.h):
-// host-side validation, workspace carving, block_m choice and the launch
-// sequence prologue (route sort + activation quant) -> stage 1 -> stage 2 ->
-// per-token slot reduction,
-// all asynchronous on the caller's stream with no host synchronization (grids
-// are sized for the worst-case route list; blocks past the real one exit).
+// host-side validation, workspace carving, the choice of path and block_m,
+// and the launch sequence, all asynchronous on the caller's stream with no
+// host synchronization (grids are sized for the worst-case route list;
+// blocks past the real one exit):
+//   route-indexed path (few tokens): stage 1 (own route scan + activation
+//     quant) -> stage 2 -> per-token slot reduction;
+//   sorted paths: prologue (route sort + activation quant) [-> sorted copy of
+//     the activations for the tiled kernels] -> stage 1 -> stage 2 -> slot
+//     reduction.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -75,21 +79,52 @@ int choose_block_m(int M, int E, int topk)
     return 256;       // LDS-tiled kernels (gemm_tile.hip)
 }
 
+// Few tokens with few routes per expert: the route-indexed kernels, which
+// need no route sort (a single-workgroup sort costs more than their whole
+// bookkeeping); otherwise the expert-sorted kernels.
+int choose_path(int M, int E, int topk)
+{
+    const int64_t R = int64_t(M) * topk;
+    if (M <= moe::kDirectMaxTokens && topk <= moe::kMaxTopkDirect && R <= moe::kDirectMaxRoutes &&
+        E <= moe::kDirectMaxE && choose_block_m(M, E, topk) == 16)
+        return MOE_MXFP4_PATH_DIRECT;
+    return choose_block_m(M, E, topk) == 256 ? MOE_MXFP4_PATH_TILED : MOE_MXFP4_PATH_STREAM;
+}
+
 struct Layout {
+    int path;
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        total;
+        slot_expert, slot_layers, route_of, n_active, total;
 };
 
 Layout layout(int M, int D, int I, int E, int topk)
 {
     Layout L;
+    L.path = choose_path(M, E, topk);
     L.bm = choose_block_m(M, E, topk);
     L.cap = route_capacity(M, E, topk, L.bm);
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    L.slot_expert = L.slot_layers = L.route_of = L.n_active = 0;
+    if (L.path == MOE_MXFP4_PATH_DIRECT) {
+        // rows indexed by route: a2 codes and scales row-major; the expert
+        // slots with their token -> route tables
+        const size_t R = size_t(M) * topk;
+        const size_t slots = size_t(moe::direct_slots(M, E, topk));
+        L.sorted_route = L.sorted_w = L.block_expert = L.num_valid = L.a1q = L.a1s = 0;
+        L.a1f = L.a1fs = L.partial = 0;
+        L.a2q = take(R * I / 2);
+        L.a2s = take(R * I / 32);
+        L.slot_expert = take(sizeof(int32_t) * slots);
+        L.slot_layers = take(sizeof(int32_t) * slots);
+        L.route_of = take(sizeof(int32_t) * size_t(topk) * slots * size_t(M));
+        L.n_active = take(sizeof(int32_t));
+        L.total = off;
+        return L;
+    }
     L.sorted_route = take(sizeof(int32_t) * size_t(L.cap));
     L.sorted_w = take(sizeof(float) * size_t(L.cap));
     L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
@@ -132,6 +167,42 @@ bool mark(const DebugOut* d, int i, hipStream_t stream)
     return hipEventRecord(d->events[i], stream) == hipSuccess;
 }
 
+int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
+                   const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                   const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
+                   uint8_t* ws, const Layout& L, int n_cu, const DebugOut* dbg, hipStream_t stream)
+{
+    moe::DirectArgs a{hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ws + L.a2q,
+                      ws + L.a2s, reinterpret_cast<int32_t*>(ws + L.slot_expert),
+                      reinterpret_cast<int32_t*>(ws + L.slot_layers),
+                      reinterpret_cast<int32_t*>(ws + L.route_of),
+                      reinterpret_cast<int32_t*>(ws + L.n_active), out,
+                      dbg ? dbg->h : nullptr, M, D, I, E, topk};
+    (void)n_cu;
+    // no prologue on this path (events 0 and 1 bracket nothing) and the slot
+    // sum is part of stage 2 (events 3 and 4 likewise)
+    if (!mark(dbg, 0, stream) || !mark(dbg, 1, stream)) return MOE_MXFP4_ERR_HIP;
+    hipError_t e = moe::launch_gemm1_direct(a, stream);
+    if (e != hipSuccess || !mark(dbg, 2, stream)) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_gemm2_direct(a, stream);
+    if (e != hipSuccess || !mark(dbg, 3, stream) || !mark(dbg, 4, stream))
+        return MOE_MXFP4_ERR_HIP;
+    if (dbg) {
+        const int R = M * topk;
+        if ((dbg->sorted_route || dbg->num_valid) &&
+            moe::launch_direct_rows(topk_ids, R, E, dbg->sorted_route, dbg->num_valid, stream) !=
+                hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+        if (dbg->a2_codes && hipMemcpyAsync(dbg->a2_codes, a.a2q, size_t(R) * I / 2,
+                                            hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+        if (dbg->a2_scales && hipMemcpyAsync(dbg->a2_scales, a.a2s, size_t(R) * I / 32,
+                                             hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return MOE_MXFP4_ERR_HIP;
+    }
+    return MOE_MXFP4_OK;
+}
+
 int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
                  const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                  const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
@@ -152,6 +223,9 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     if (st) return st;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (L.path == MOE_MXFP4_PATH_DIRECT)
+        return forward_direct(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I,
+                              E, topk, ws, L, n_cu, dbg, stream);
     int32_t* sorted_route = reinterpret_cast<int32_t*>(ws + L.sorted_route);
     float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
     int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
@@ -223,6 +297,12 @@ MOE_API int moe_mxfp4_block_m(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk)) return 0;
     return choose_block_m(M, E, topk);
+}
+
+MOE_API int moe_mxfp4_path(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk)) return 0;
+    return choose_path(M, E, topk);
 }
 
 MOE_API int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m)

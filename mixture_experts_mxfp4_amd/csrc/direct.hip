@@ -1,0 +1,552 @@
+// Route-indexed path for small batches (decode): the two grouped GEMMs of the
+// forward without a route sort, a sorted route list, an activation-quant pass
+// or a reduction pass.
+//
+// Same semantics as the sorted path (gemm1.hip and gemm2.hip hold them and the
+// passages of the pages they follow).  What changes is the bookkeeping: with a
+// few hundred routes the sort, the padding and the separate passes are pure
+// launch and latency overhead (each dependent launch costs a few microseconds
+// of a ~60 us forward), so the forward is two kernels:
+//
+// Stage 1, workgroup (c, y): one 64-row group c of the gate_up weight of the
+//   y-th active expert in descending id order (grid.y runs to min(E, M*topk),
+//   an upper bound of the active experts; surplus workgroups leave at once).
+//   Its first wave marks the active experts in an LDS bitmap, picks its own
+//   and collects that expert's routes r = t*topk + s (ascending) in LDS.  It
+//   quantizes the activations itself: in the 16x16x128 MFMA layout a lane's A
+//   operand is one whole 32-element MX block of one row, so the block
+//   maximum, e8m0 scale and E2M1 codes come from the lane's registers (same
+//   rule and helpers as the standalone quantization kernel, identical codes).
+//   h is stored MXFP4 at its route index: a2 [M*topk][I/2] codes +
+//   [M*topk][I/32] scales.  The workgroups (0, y) publish slot y's expert and
+//   a token -> route table (one layer per repeat of the expert in a token's
+//   slots; almost always a single layer).
+//
+// Stage 2, workgroup n16: one 16-column slice of the output for all tokens.
+//   Its waves split the active experts; for each expert a wave streams the
+//   slice's down-projection fragments (1 KiB per K tile), gathers the MXFP4 h
+//   rows of the expert's tokens into the MFMA rows of those tokens, and adds
+//   topk_w * result to fp32 accumulators that stay in registers for the whole
+//   kernel; the waves' sums meet in LDS and the slice is written once, as
+//   bf16.  Every weight byte is read once, nothing is written per route and
+//   no workgroup depends on another; the per-token sum runs over the
+//   experts in descending id order (deterministic) with one rounding.
+//
+// Descending id order: a shared expert is conventionally the last id and has
+// a route from every token, the heaviest stage-1 work; its workgroups then
+// run first instead of forming the tail.
+#include <type_traits>
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int kDirThreads = 256;
+
+// Picks this workgroup's expert and its routes; run by one whole wave.
+// Pass 1 marks the experts that have a route in an LDS bitmap; the y-th
+// marked expert in descending id order is this workgroup's, or none
+// (*e_out = -1) when fewer than y + 1 experts are active (*active_out = the
+// number of active experts).  Pass 2 (the ids again, now in the L1 cache)
+// collects that expert's routes r = t*topk + s, ascending, into list[] and
+// their number into *n_out.  Ids outside [0, E) are skipped.
+__device__ __forceinline__ void active_expert_routes(const int32_t* __restrict__ ids, int R, int E,
+                                                     int y, uint32_t* bitmap, int32_t* list,
+                                                     int& n_out, int& e_out, int& active_out)
+{
+    const int lane = threadIdx.x % kWave;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int words = (E + 31) / 32;
+    if (lane < words) bitmap[lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int base = 0; base < R; base += 4 * kWave) {
+        int id[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = base + u * kWave + lane;
+            id[u] = r < R ? ids[r] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (id[u] >= 0 && id[u] < E) atomicOr(&bitmap[id[u] / 32], 1u << (id[u] % 32));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // word w of the bitmap on lane words-1-w (highest expert ids first); the
+    // y-th set bit in descending order
+    const int wi = words - 1 - lane;
+    uint32_t w = lane < words ? bitmap[wi] : 0u;
+    const int pc = __popc(w);
+    const int inc = wave_inclusive_scan(pc);
+    const bool mine = y >= inc - pc && y < inc;
+    int e = -1;
+    if (mine) {
+        for (int k = y - (inc - pc); k > 0; --k) w &= ~(0x80000000u >> __builtin_clz(w));  // drop the upper set bits
+        e = wi * 32 + 31 - __builtin_clz(w);
+    }
+    const uint64_t who = __ballot(mine);
+    e = who ? __builtin_amdgcn_readlane(e, __builtin_ctzll(who)) : -1;
+    int n = 0;
+    if (e >= 0) {
+#pragma unroll 1
+        for (int base = 0; base < R; base += 4 * kWave) {
+            int id[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = base + u * kWave + lane;
+                id[u] = r < R ? ids[r] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool hit = id[u] == e;
+                const uint64_t m = __ballot(hit);
+                if (hit) list[n + __popcll(m & below)] = base + u * kWave + lane;
+                n += __popcll(m);
+            }
+        }
+    }
+    n_out = n;
+    e_out = e;
+    active_out = __builtin_amdgcn_readlane(inc, kWave - 1);
+}
+
+// One 32-element MX block held by one lane as 64 bytes of bf16 (x[0] =
+// elements 0..7, ...): returns its 16 code bytes (byte b = elements 2b, 2b+1)
+// and the e8m0 scale byte.
+__device__ __forceinline__ uint4 mx_quant_lane_block(const uint4 (&x)[4], uint32_t& scale)
+{
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
+    }
+    const uint32_t s = mx_scale_from_amax(max(uint32_t(m.x), uint32_t(m.y)));
+    scale = s;
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
+        uint32_t d = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d |= mx_code2(w[j] & 0xFFFFu, w[j] >> 16, s) << (8 * j);
+        out[p] = d;
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// Slot y's entry for stage 2 (wave 0 of workgroup (0, y), after the route
+// scan): the expert (or -1), the number of layers L (the most routes any one
+// token has to this expert, 0 if none) and the token -> route table of each
+// layer l < L: route_of[(l*slots + y)*M + t] = the l-th route of token t to
+// this expert, or -1.  Layer 0 is written for every slot, so stage 2 can
+// read all of it without knowing which slots are active.  A token's routes to
+// one expert are adjacent in the ascending list; lane t finds them by binary
+// search.  Workgroup (0, 0) also stores the number of active experts.
+__device__ __forceinline__ void publish_slot(const DirectArgs& a, int y, const int32_t* list, int n,
+                                             int e, int active)
+{
+    const int lane = threadIdx.x % kWave;
+    const int slots = direct_slots(a.M, a.E, a.topk);
+    int first = 0, cnt = 0;
+    if (e >= 0 && lane < a.M) {
+        const int lo_key = lane * a.topk, hi_key = lo_key + a.topk;
+        int lo = 0, hi = n;
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (list[mid] < lo_key) lo = mid + 1; else hi = mid;
+        }
+        first = lo;
+        hi = n;
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (list[mid] < hi_key) lo = mid + 1; else hi = mid;
+        }
+        cnt = lo - first;
+    }
+    int layers = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) layers = max(layers, __shfl_xor(layers, off));
+    if (lane == 0) {
+        a.slot_expert[y] = e;
+        a.slot_layers[y] = layers;
+        if (y == 0) *a.n_active = active;
+    }
+    for (int l = 0; l < max(layers, 1); ++l)
+        if (lane < a.M)
+            a.route_of[(int64_t(l) * slots + y) * a.M + lane] = l < cnt ? list[first + l] : -1;
+}
+
+// ---------------------------------------------------------------- stage 1 --
+//
+// Workgroup (c, y): 64-row group c of the prepared gate_up weight of the
+// y-th active expert e (gate columns c*32..+31 and the matching up columns),
+// all K = D, four waves splitting K as in the sorted streaming kernel.
+template <int U>
+__global__ void __launch_bounds__(kDirThreads)
+gemm1_direct_kernel(DirectArgs a)
+{
+    __shared__ int32_t list[kDirectMaxRoutes];
+    __shared__ uint32_t bitmap[kDirectMaxE / 32];
+    __shared__ int32_t n_list, e_sel;
+    __shared__ float red[4][4][4][kWave];      // [wave][slice][i][lane]
+    const int c = blockIdx.x, y = blockIdx.y;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int R = a.M * a.topk;
+    const int D = a.D, I = a.I;
+    if (wave == 0) {
+        int nw, ew, active;
+        active_expert_routes(a.ids, R, a.E, y, bitmap, list, nw, ew, active);
+        if (lane == 0) {
+            n_list = nw;
+            e_sel = ew;
+        }
+        if (c == 0) publish_slot(a, y, list, nw, ew, active);
+    }
+    __syncthreads();
+    const int n = n_list, e = e_sel;
+    if (e < 0) return;
+
+    const int KT = D / 128;
+    const uint8_t* wb = a.w13p + int64_t(e) * I * D + int64_t(c) * KT * 4096 + lane * 16;
+    const uint8_t* sb = a.w13sp + int64_t(e) * I * D / 16 + int64_t(c) * KT * 256 + lane * 4;
+    const int kt_begin = wave * KT / 4, kt_end = (wave + 1) * KT / 4;
+
+#pragma unroll 1
+    for (int t0 = 0; t0 < n; t0 += 16) {
+        const int j = t0 + lane % 16;
+        const bool ok = j < n;
+        const int64_t tok = ok ? list[j] / a.topk : 0;
+        // this lane's 32 bf16 of its row at K tile kt: 64 bytes at ap + kt*256
+        const uint8_t* ap = reinterpret_cast<const uint8_t*>(a.hidden + tok * D) + (lane / 16) * 64;
+
+        v4f acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        auto steps = [&](auto u_const, int kt) {
+            constexpr int UU = decltype(u_const)::value;
+            uint32_t sw[UU];
+            uint4 b[UU][4], x[UU][4];
+#pragma unroll
+            for (int u = 0; u < UU; ++u) {
+                sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) b[u][q] = ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024);
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    x[u][p] = ok ? ld16(ap + int64_t(kt + u) * 256 + p * 16) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UU; ++u) {
+                uint32_t sa;
+                const uint4 av = mx_quant_lane_block(x[u], sa);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[q] = mfma_fp4_16x16x128(av, b[u][q], acc[q], sa, (sw[u] >> (8 * q)) & 0xFFu);
+            }
+        };
+        int kt = kt_begin;
+        for (; kt + U <= kt_end; kt += U) steps(std::integral_constant<int, U>{}, kt);
+        for (; kt < kt_end; ++kt) steps(std::integral_constant<int, 1>{}, kt);
+
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][q][i][lane] = acc[q][i];
+        __syncthreads();
+
+        // wave w finishes element i = w of every lane: row 4*(lane/16) + w of the tile
+        {
+            const int i = wave;
+            float s4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                s4[q] = red[0][q][i][lane] + red[1][q][i][lane] + red[2][q][i][lane] +
+                        red[3][q][i][lane];
+            // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
+            const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
+            const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
+            const int jr = t0 + 4 * (lane / 16) + i;
+            const bool row_ok = jr < n;
+            const int64_t r = row_ok ? list[jr] : 0;
+            if (a.h_dbg && row_ok) {
+                a.h_dbg[r * I + c * 32 + lane % 16] = uint16_t(h0);
+                a.h_dbg[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
+            }
+            // the row's MXFP4 group = columns c*32..+31, held by the 16 lanes of a DPP row
+            const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
+            const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
+            const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
+            const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
+            const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
+            if (row_ok && lane % 16 == 0) {
+                *reinterpret_cast<uint4*>(a.a2q + r * (I / 2) + c * 16) = make_uint4(qlo, d1, qhi, d3);
+                a.a2s[r * (I / 32) + c] = uint8_t(s);
+            }
+        }
+        __syncthreads();          // red is rewritten by the next row tile
+    }
+}
+
+// ---------------------------------------------------------------- stage 2 --
+//
+// Workgroup x: output columns x*16*NS .. +16*NS (NS adjacent 16-row slices
+// of one 64-row group of the prepared down weight) for every token; RT row
+// tiles of 16 tokens.  Its 16 waves split the active slots (wave w takes
+// slots w, w + 16, ...); per slot and K tile a wave loads the NS slices'
+// weight fragments (NS x 1 KiB, contiguous), one scale word (the slices'
+// scale bytes) and, for MFMA row t, the h fragment of token t's route to the
+// slot's expert (zero when there is none), shared by the NS slices.  G slots
+// x 2 K tiles are loaded before their MFMAs: G x 2 x NS KiB of weights in
+// flight per wave, 16 waves per CU (one workgroup per CU, 128 VGPRs each).
+#ifndef MOE_OS_SLOTS_IN_FLIGHT
+#define MOE_OS_SLOTS_IN_FLIGHT 2
+#endif
+constexpr int kOsThreads = 1024;
+constexpr int kOsWaves = kOsThreads / kWave;
+constexpr int kOsSlices = 2;
+constexpr int kOsMaxSlots = kDirectMaxTokens * kMaxTopkDirect;
+
+template <int RT, int G, int NS>
+__global__ void __launch_bounds__(kOsThreads)
+gemm2_direct_kernel(DirectArgs a)
+{
+    __shared__ int32_t s_e[kOsMaxSlots];
+    __shared__ int32_t s_layers[kOsMaxSlots];
+    __shared__ int16_t s_route[kOsMaxSlots * 16 * RT];     // layer 0: [slot][token]
+    __shared__ float s_tw[kOsMaxSlots];                    // topk_w by route
+    __shared__ float red[kOsWaves][NS][RT][4][kWave];
+    __shared__ int32_t s_active;
+    const int n16_0 = blockIdx.x * NS;          // first slice; NS | 4, so one 64-row group
+    const int n64 = n16_0 / 4, q0 = n16_0 % 4;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int M = a.M, D = a.D, I = a.I, topk = a.topk;
+    const int R = M * topk;
+    const int slots = direct_slots(M, a.E, topk);
+    const int KT = I / 128;                   // even
+
+    if (threadIdx.x == 0) s_active = *a.n_active;
+    for (int y = threadIdx.x; y < slots; y += kOsThreads) {
+        s_e[y] = a.slot_expert[y];
+        s_layers[y] = a.slot_layers[y];
+    }
+    for (int i = threadIdx.x; i < slots * M; i += kOsThreads) {
+        const int y = i / M, t = i % M;
+        s_route[y * 16 * RT + t] = int16_t(a.route_of[i]);
+    }
+    for (int r = threadIdx.x; r < R; r += kOsThreads) s_tw[r] = a.tw[r];
+    __syncthreads();
+    const int active = s_active;
+
+    const int64_t w_stride = int64_t(D) * (I / 2), s_stride = int64_t(D) * (I / 32);
+    // slice s of K tile kt of expert e: wcol + e*w_stride + kt*4096 + s*1024
+    const uint8_t* wcol = a.w2p + (int64_t(n64) * KT * 4 + q0) * 1024 + lane * 16;
+    const uint8_t* scol = a.w2sp + int64_t(n64) * KT * 256 + lane * 4;      // + e*s_stride + kt*256
+    const int row = lane % 16, kq = lane / 16;
+
+    v4f acc[NS][RT];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[sl][rt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+    for (int y0 = wave; y0 < active; y0 += kOsWaves * G) {
+        v4f tmp[G][NS][RT];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) tmp[g][sl][rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int kt = 0; kt < KT; kt += 2) {
+            uint4 b[G][2][NS], av[G][2][RT];
+            uint32_t sw[G][2], sa[G][2][RT];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int y = y0 + g * kOsWaves;
+                const bool on = y < active;
+                const int64_t e = on ? s_e[y] : 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl)
+                        b[g][h][sl] = on ? ld16_nt(wcol + e * w_stride + int64_t(kt + h) * 4096 + sl * 1024)
+                                         : make_uint4(0, 0, 0, 0);
+                    sw[g][h] = on ? *reinterpret_cast<const uint32_t*>(scol + e * s_stride +
+                                                                       (kt + h) * 256)
+                                  : 0u;
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int t = rt * 16 + row;
+                    const int r = (on && t < M) ? s_route[y * 16 * RT + t] : -1;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        av[g][h][rt] = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + (kt + h) * 64 + kq * 16)
+                                              : make_uint4(0, 0, 0, 0);
+                        sa[g][h][rt] = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + (kt + h) * 4 + kq] : 0u;
+                    }
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            tmp[g][sl][rt] = mfma_fp4_16x16x128(av[g][h][rt], b[g][h][sl], tmp[g][sl][rt],
+                                                                sa[g][h][rt],
+                                                                (sw[g][h] >> (8 * (q0 + sl))) & 0xFFu);
+        }
+        // weight each token's row by its routing weight and accumulate
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int y = y0 + g * kOsWaves;
+            if (y >= active) break;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = rt * 16 + 4 * kq + i;
+                    const int r = t < M ? s_route[y * 16 * RT + t] : -1;
+                    const float w = r >= 0 ? s_tw[r] : 0.0f;
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) acc[sl][rt][i] += w * tmp[g][sl][rt][i];
+                }
+        }
+    }
+
+    // further layers (a token naming one expert in several slots): rare,
+    // one slot and K tile at a time, routes from the global table
+#pragma unroll 1
+    for (int y = wave; y < active; y += kOsWaves) {
+        const int layers = s_layers[y];
+        const int64_t e = s_e[y];
+#pragma unroll 1
+        for (int l = 1; l < layers; ++l) {
+            const int32_t* tab = a.route_of + (int64_t(l) * slots + y) * M;
+            v4f tmp[NS][RT];
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) tmp[sl][rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int kt = 0; kt < KT; ++kt) {
+                const uint32_t sw = *reinterpret_cast<const uint32_t*>(scol + e * s_stride + kt * 256);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int t = rt * 16 + row;
+                    const int r = t < M ? tab[t] : -1;
+                    const uint4 av = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + kt * 64 + kq * 16)
+                                            : make_uint4(0, 0, 0, 0);
+                    const uint32_t sa = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + kt * 4 + kq] : 0u;
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) {
+                        const uint4 b = ld16(wcol + e * w_stride + int64_t(kt) * 4096 + sl * 1024);
+                        tmp[sl][rt] = mfma_fp4_16x16x128(av, b, tmp[sl][rt], sa,
+                                                         (sw >> (8 * (q0 + sl))) & 0xFFu);
+                    }
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = rt * 16 + 4 * kq + i;
+                    const int r = t < M ? tab[t] : -1;
+                    const float w = r >= 0 ? s_tw[r] : 0.0f;
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) acc[sl][rt][i] += w * tmp[sl][rt][i];
+                }
+        }
+    }
+
+    // the waves' sums, in wave order; one bf16 rounding
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][sl][rt][i][lane] = acc[sl][rt][i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < M * 16 * NS; o += kOsThreads) {
+        const int t = o / (16 * NS), c = o % (16 * NS);
+        const int sl = c / 16, col = c % 16;
+        const int rt = t / 16, tt = t % 16;
+        const int L = col + 16 * (tt / 4), i = tt % 4;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kOsWaves; ++w) sum += red[w][sl][rt][i][L];
+        a.out[int64_t(t) * D + n16_0 * 16 + c] = uint16_t(f32_to_bf16_rne(sum));
+    }
+}
+
+static bool direct_shape_ok(const DirectArgs& a)
+{
+    return a.M <= kDirectMaxTokens && a.topk <= kMaxTopkDirect &&
+           int64_t(a.M) * a.topk <= kDirectMaxRoutes && a.E <= kDirectMaxE;
+}
+
+hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream)
+{
+    if (!direct_shape_ok(a)) return hipErrorInvalidValue;
+    if (a.M == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm1_direct_kernel<4>), dim3(a.I / 32, direct_slots(a.M, a.E, a.topk)),
+                       dim3(kDirThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream)
+{
+    if (!direct_shape_ok(a)) return hipErrorInvalidValue;
+    if (a.M == 0) return hipSuccess;
+    const dim3 grid(a.D / (16 * kOsSlices));
+    if (a.M <= 16)
+        hipLaunchKernelGGL((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices>), grid,
+                           dim3(kOsThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm2_direct_kernel<2, 1, kOsSlices>), grid, dim3(kOsThreads), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+// Debug view of the route-indexed rows: row r holds route r when its id is
+// valid, else the sentinel M*topk; num_valid = {M*topk, valid routes}.
+__global__ void direct_rows_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                   int32_t* __restrict__ row_route, int32_t* __restrict__ num_valid)
+{
+    __shared__ int32_t count;
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int r = threadIdx.x; r < R; r += blockDim.x) {
+        const bool v = ids[r] >= 0 && ids[r] < E;
+        if (row_route) row_route[r] = v ? r : R;
+        mine += v;
+    }
+    atomicAdd(&count, mine);
+    __syncthreads();
+    if (threadIdx.x == 0 && num_valid) {
+        num_valid[0] = R;
+        num_valid[1] = count;
+    }
+}
+
+hipError_t launch_direct_rows(const int32_t* ids, int R, int E, int32_t* row_route,
+                              int32_t* num_valid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(direct_rows_kernel, dim3(1), dim3(256), 0, stream, ids, R, E, row_route,
+                       num_valid);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -271,46 +271,82 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream)
 }
 
 // out[t, :] = bf16( sum_{s < topk, 0 <= ids[t,s] < E} partial[t*topk + s, :] ),
-// fp32 sum in slot order; 8 columns per thread.
+// fp32 sum in slot order.  A thread owns VEC columns of one token; the slots
+// are taken eight at a time with all eight loads issued before the adds, so a
+// token costs two memory round trips (ids, then partial rows) per eight slots
+// instead of one per slot.
+template <int VEC>
 __global__ void __launch_bounds__(256)
 reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restrict__ ids, int M,
                     int D, int E, int topk, uint16_t* __restrict__ out)
 {
-    const int64_t n8 = int64_t(M) * (D / 8);
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
+    constexpr int W = VEC / 2;          // 32-bit words per thread and row
+    const int64_t per_row = D / VEC;
+    const int64_t nv = int64_t(M) * per_row;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nv;
          i += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t t = i / (D / 8);
-        const int64_t c8 = i % (D / 8);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < topk; ++s) {
-            const int e = ids[t * topk + s];
-            if (e < 0 || e >= E) continue;
-            const uint4 v = ld16(reinterpret_cast<const uint8_t*>(partial + (t * topk + s) * D + c8 * 8));
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const int64_t t = i / per_row;
+        const int64_t col = (i % per_row) * VEC;
+        float acc[VEC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] += bf16_to_f32(w[j] & 0xFFFFu);
-                acc[2 * j + 1] += bf16_to_f32(w[j] >> 16);
+        for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
+#pragma unroll 1
+        for (int s0 = 0; s0 < topk; s0 += 8) {
+            bool use[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u;
+                const int e = s < topk ? ids[t * topk + s] : -1;
+                use[u] = e >= 0 && e < E;
+            }
+            uint32_t v[8][W];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint16_t* src = partial + (t * topk + s0 + u) * D + col;
+                if constexpr (W == 1) {
+                    v[u][0] = use[u] ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+                } else {
+                    const uint4 x = use[u] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+                    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (!use[u]) continue;
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    acc[2 * j] += bf16_to_f32(v[u][j] & 0xFFFFu);
+                    acc[2 * j + 1] += bf16_to_f32(v[u][j] >> 16);
+                }
             }
         }
-        uint4 o;
-        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-        o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-        o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-        *reinterpret_cast<uint4*>(out + t * D + c8 * 8) = o;
+        uint32_t o[W];
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+            o[j] = f32_to_bf16_rne(acc[2 * j]) | (f32_to_bf16_rne(acc[2 * j + 1]) << 16);
+        if constexpr (W == 1)
+            *reinterpret_cast<uint32_t*>(out + t * D + col) = o[0];
+        else
+            *reinterpret_cast<uint4*>(out + t * D + col) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
+// Few tokens: two columns per thread (enough threads to cover the latency);
+// many tokens: eight columns per thread (16-byte accesses).
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
                                int topk, uint16_t* out, int n_cu, hipStream_t stream)
 {
-    const int64_t n8 = int64_t(M) * (D / 8);
-    if (n8 == 0) return hipSuccess;
-    int64_t blocks = (n8 + 255) / 256;
+    if (int64_t(M) * D == 0) return hipSuccess;
+    const bool narrow = int64_t(M) * (D / 2) <= int64_t(n_cu) * 1024;
+    const int64_t nv = int64_t(M) * (D / (narrow ? 2 : 8));
+    int64_t blocks = (nv + 255) / 256;
     if (blocks > int64_t(n_cu) * 16) blocks = int64_t(n_cu) * 16;
-    hipLaunchKernelGGL(reduce_slots_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, partial,
-                       ids, M, D, E, topk, out);
+    if (narrow)
+        hipLaunchKernelGGL(reduce_slots_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           partial, ids, M, D, E, topk, out);
+    else
+        hipLaunchKernelGGL(reduce_slots_kernel<8>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           partial, ids, M, D, E, topk, out);
     return hipGetLastError();
 }
 

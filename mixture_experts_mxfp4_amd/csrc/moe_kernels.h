@@ -73,6 +73,36 @@ hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernel
 hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream);
 hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream);
 
+// Route-indexed path (small batches): no route sort, no quantization or
+// reduction pass; a2 rows and h rows are indexed by the route r = t*topk + s.
+constexpr int kDirectMaxTokens = 32;
+constexpr int kMaxTopkDirect = 16;
+constexpr int kDirectMaxRoutes = 1024;
+constexpr int kDirectMaxE = 1024;
+// expert slots: min(E, M*topk), an upper bound of the active experts
+__host__ __device__ inline int direct_slots(int M, int E, int topk)
+{
+    return M * topk < E ? M * topk : E;
+}
+struct DirectArgs {
+    const uint16_t* hidden;
+    const uint8_t *w13p, *w13sp, *w2p, *w2sp;
+    const int32_t* ids;
+    const float* tw;
+    uint8_t *a2q, *a2s;            // [M*topk][I/2], [M*topk][I/32]
+    int32_t* slot_expert;          // [slots] expert of slot y (descending ids), or -1
+    int32_t* slot_layers;          // [slots] layers of slot y's token -> route table
+    int32_t* route_of;             // [topk][slots][M] route of token t to slot y's expert, or -1
+    int32_t* n_active;             // [1] number of active experts
+    uint16_t* out;                 // bf16 [M][D]
+    uint16_t* h_dbg;
+    int M, D, I, E, topk;
+};
+hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream);
+hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream);
+hipError_t launch_direct_rows(const int32_t* ids, int R, int E, int32_t* row_route,
+                              int32_t* num_valid, hipStream_t stream);
+
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
                                int topk, uint16_t* out, int n_cu, hipStream_t stream);
 

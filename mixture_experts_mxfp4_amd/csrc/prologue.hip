@@ -49,6 +49,23 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int id, bool valid, int nb
     return peers;
 }
 
+// Every slot of the route list starts as padding (route M*topk, weight 0) and
+// every block as unused (expert -1), written by the whole workgroup before its
+// barrier; the sort then only stores the real routes and the used blocks'
+// experts (the padding is never written per expert, one slot at a time).
+__device__ __forceinline__ void fill_padding(int R, int bm, int nb_cap,
+                                             int32_t* __restrict__ sorted_route,
+                                             float* __restrict__ sorted_w,
+                                             int32_t* __restrict__ block_expert)
+{
+    const int64_t cap = int64_t(nb_cap) * bm;
+    for (int64_t p = threadIdx.x; p < cap; p += kPrologueThreads) {
+        sorted_route[p] = R;
+        sorted_w[p] = 0.0f;
+    }
+    for (int b = threadIdx.x; b < nb_cap; b += kPrologueThreads) block_expert[b] = -1;
+}
+
 template <int U>
 __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
                                 int M, int topk, int E, int bm, int nb_cap,
@@ -64,6 +81,7 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int i = tid; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
+    fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert);
     __syncthreads();
 
     const int per_wave = (R + kRouteWaves - 1) / kRouteWaves;
@@ -123,18 +141,12 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
                 run += c;
             }
 #pragma unroll 1
-            for (int p = base_e + total; p < base_e + padded; ++p) {
-                sorted_route[p] = R;
-                sorted_w[p] = 0.0f;
-            }
-#pragma unroll 1
             for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
         }
         carry += all;
         valid_total += vall;
         __syncthreads();
     }
-    for (int b = carry / bm + tid; b < nb_cap; b += kPrologueThreads) block_expert[b] = -1;
     if (tid == 0) {
         num_valid[0] = carry;
         num_valid[1] = valid_total;
@@ -188,6 +200,7 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
         ids[r] = ids_g[r];
         tw[r] = tw_g[r];
     }
+    fill_padding(M * topk, bm, nb_cap, sorted_route, sorted_w, block_expert);
     __syncthreads();
     if (threadIdx.x >= kWave) return;
     const int lane = threadIdx.x;
@@ -221,18 +234,12 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
         if (e < E) {
             cnt[e] = base_e;
 #pragma unroll 1
-            for (int p = base_e + total; p < base_e + padded; ++p) {
-                sorted_route[p] = R;
-                sorted_w[p] = 0.0f;
-            }
-#pragma unroll 1
             for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
         }
         carry += __builtin_amdgcn_readlane(inc, kWave - 1);
         vcarry += __builtin_amdgcn_readlane(vinc, kWave - 1);
         __builtin_amdgcn_wave_barrier();
     }
-    for (int b = carry / bm + lane; b < nb_cap; b += kWave) block_expert[b] = -1;
     if (lane == 0) {
         num_valid[0] = carry;
         num_valid[1] = vcarry;

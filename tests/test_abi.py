@@ -67,8 +67,21 @@ def test_block_m_and_capacity(binding):
     assert binding.moe_mxfp4_route_capacity(0, 8, 2, 16) == 0
 
 
+def test_path_choice(binding):
+    assert binding.moe_mxfp4_path(16, 7168, 256, 257, 9) == binding.PATH_DIRECT
+    assert binding.moe_mxfp4_path(8, 512, 256, 9, 3) == binding.PATH_DIRECT
+    assert binding.moe_mxfp4_path(64, 7168, 2048, 33, 9) == binding.PATH_STREAM
+    assert binding.moe_mxfp4_path(1024, 7168, 256, 257, 9) == binding.PATH_STREAM
+    assert binding.moe_mxfp4_path(200, 512, 256, 257, 9) == binding.PATH_STREAM
+    assert binding.moe_mxfp4_path(4096, 7168, 2048, 33, 9) == binding.PATH_TILED
+    assert binding.moe_mxfp4_path(16, 7000, 256, 257, 9) == 0
+
+
 def test_workspace_bytes(binding):
-    assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 257, 9) > 16 * 7168 * 4
+    # route-indexed path: at least h in MXFP4 for every route
+    assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 257, 9) >= 16 * 9 * (128 + 8)
+    # sorted paths: at least the bf16 contribution of every route
+    assert binding.moe_mxfp4_workspace_bytes(64, 7168, 2048, 33, 9) >= 64 * 9 * 7168 * 2
     assert binding.moe_mxfp4_workspace_bytes(16, 7000, 256, 257, 9) == 0
     assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 2000, 9) == 0     # E > 1024
 

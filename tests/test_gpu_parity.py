@@ -202,14 +202,22 @@ def test_prepare_layout_and_round_trip(binding, E, D, I):
 # --------------------------------------------------------------- forward ---
 
 def _check_intermediates(case, dbg):
+    from mixture_experts_mxfp4_amd import binding
     """h per sorted row against the oracle's h; the fused requant bit-exact
     against the oracle quantizer applied to the GPU's own h."""
     sr = dbg["sorted_route"].cpu().numpy()
     n = int(dbg["num_valid"].cpu().numpy()[0])
     bm = dbg["block_m"]
-    want_route = oracle.route(case.ids, case.tw, case.E, bm)
-    np.testing.assert_array_equal(sr[:n], want_route["sorted_route"])
-    valid = np.nonzero(sr[:n] < case.M * case.topk)[0]
+    R = case.M * case.topk
+    if dbg["path"] == binding.PATH_DIRECT:
+        # rows indexed by route: row r = route r, invalid ids -> sentinel R
+        ok = (case.ids.reshape(-1) >= 0) & (case.ids.reshape(-1) < case.E)
+        np.testing.assert_array_equal(sr[:n], np.where(ok, np.arange(R), R))
+        assert n == R and int(dbg["num_valid"].cpu().numpy()[1]) == int(ok.sum())
+    else:
+        want_route = oracle.route(case.ids, case.tw, case.E, bm)
+        np.testing.assert_array_equal(sr[:n], want_route["sorted_route"])
+    valid = np.nonzero(sr[:n] < R)[0]
     h_gpu = dbg["h"].cpu().view(torch.int16).numpy().view(np.uint16)[valid]
     _, h_or = case.run_oracle(want_h=True)
     r = sr[valid]
@@ -250,7 +258,9 @@ def test_forward_workload_sampled(binding, name, n_sample):
 
 
 @pytest.mark.parametrize("M,D,I,E,n_routed,seed", [
-    (1, 512, 256, 9, 2, 21),          # single token
+    (1, 512, 256, 9, 2, 21),          # single token (route-indexed path)
+    (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
+    (200, 512, 256, 257, 8, 28),      # sorted streaming path with block_m 16
     (37, 768, 768, 5, 3, 22),         # ragged M, D and I not multiples of 512
     (130, 1024, 512, 33, 8, 23),      # several blocks per expert
     (3, 256, 256, 2, 1, 24),          # smallest dims
@@ -266,8 +276,9 @@ def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     _check_intermediates(case, dbg)
 
 
-def test_forward_invalid_and_duplicate_ids(binding):
-    M, D, I, E = 20, 512, 256, 6
+@pytest.mark.parametrize("M,E", [(20, 6), (8, 40)])      # sorted and route-indexed paths
+def test_forward_invalid_and_duplicate_ids(binding, M, E):
+    D, I = 512, 256
     rng = np.random.default_rng(5)
     ids = rng.integers(0, E, (M, 4)).astype(np.int32)
     ids[:, 1] = ids[:, 0]            # duplicate slot
