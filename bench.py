@@ -3,9 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
-One step = one full forward (prologue = route sort + activation quant, stage 1,
-stage 2, per-token slot reduction) through the C ABI on a seeded synthetic DeepSeek-R1-shaped batch
-whose inputs are already resident in HBM.  Prepared weights are kept in
+One step = one full forward through the C ABI on a seeded synthetic
+DeepSeek-R1-shaped batch whose inputs are already resident in HBM: on the
+route-indexed path (few tokens) stage 1 (own route scan + activation quant +
+gate_up + SwiGLU + requant) and stage 2 (down projection x routing weight,
+per-token sum); on the sorted paths the prologue (route sort + activation
+quant), stage 1, stage 2 and the per-token slot reduction.  Prepared weights are kept in
 several copies and rotated step by step, so that every forward streams its
 experts' weights from HBM rather than from the 256 MB Infinity Cache.
 
@@ -38,9 +41,16 @@ METRIC = "µs/forward + HBM GB/s (M≤16) / MXFP4 MFMA TFLOPS (M≥1024), D=7168
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA
 MALL_BYTES = 256 << 20
-STAGE1_KERNEL = "gemm1_swiglu_quant_kernel"
-STAGE1_SOURCES = ("mixture_experts_mxfp4_amd/csrc/gemm1.hip",
-                  "mixture_experts_mxfp4_amd/csrc/moe_common.h")
+# the stage-1 (dominant) kernel and the sources that define it, per path
+_CSRC = "mixture_experts_mxfp4_amd/csrc/"
+STAGE1 = {
+    "direct": ("gemm1_direct_kernel", (_CSRC + "direct.hip", _CSRC + "moe_common.h",
+                                       _CSRC + "moe_kernels.h")),
+    "stream": ("gemm1_swiglu_quant_kernel", (_CSRC + "gemm1.hip", _CSRC + "moe_common.h",
+                                             _CSRC + "moe_kernels.h")),
+    "tiled": ("gemm1_tile_kernel", (_CSRC + "gemm_tile.hip", _CSRC + "moe_common.h",
+                                    _CSRC + "moe_kernels.h")),
+}
 
 
 # ---------------------------------------------------------------- helpers ---
@@ -61,21 +71,17 @@ def _hip():
     return lib
 
 
-HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
-
-
 class Events:
-    """Raw hipEvent_t handles created through the HIP runtime.  They are
-    created without the system-scope fence, which otherwise adds several
-    microseconds of idle time at every record between two kernels."""
+    """Raw hipEvent_t handles created through the HIP runtime, for the
+    library's kernel-attached timing (moe_mxfp4_forward_profiled), which
+    records them on the stream the kernels are launched on."""
 
     def __init__(self, n):
         self.hip = _hip()
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h),
-                                                    HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h), 0) == 0
             self.ev.append(h.value)
 
     def ms(self, a, b):
@@ -120,10 +126,11 @@ def algorithmic(w, ids_np, tokens=None):
     }
 
 
-def load_traffic(workload):
+def load_traffic(workload, path_name):
     """HBM traffic of the stage-1 kernel from the committed rocprofv3 counter
     summary, if it was taken on the current stage-1 source; else None."""
-    path = os.path.join(ROOT, "profiles", f"stage1_{workload}_hbm_traffic.txt")
+    kernel, sources = STAGE1[path_name]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -132,7 +139,7 @@ def load_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("stage1_source_sha256_16") != source_hash(STAGE1_SOURCES):
+    if vals.get("stage1_source_sha256_16") != source_hash(sources):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -214,16 +221,20 @@ def run(args):
     ws = binding.alloc_workspace(w.M, w.D, w.I, w.E, w.topk, dev)
     torch.cuda.synchronize()
 
-    # untimed warm-up; the last warm-up pass also records every stage boundary
-    stage_ev = Events(5)
+    path = binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)
+    path_name = binding.PATH_NAMES[path]
+    launches = binding.PATH_LAUNCHES[path]
+
+    # untimed warm-up; the last warm-up pass also times every launch
+    stage_ev = Events(8)
     for i in range(args.warmup):
-        ev = stage_ev.ev if i == args.warmup - 1 else [None] * 5
+        ev = stage_ev.ev if i == args.warmup - 1 else [None] * 8
         binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
     torch.cuda.synchronize()
     stages_us = None
     if args.warmup > 0:
-        names = ["prologue", "stage1", "stage2", "reduce"]
-        stages_us = {n: round(1000 * stage_ev.ms(j, j + 1), 2) for j, n in enumerate(names)}
+        stages_us = {binding.LAUNCHES[j]: round(1000 * stage_ev.ms(2 * j, 2 * j + 1), 2)
+                     for j in launches}
 
     # timed region: exactly K forwards, nothing else on the stream
     torch.cuda.synchronize()
@@ -234,13 +245,15 @@ def run(args):
     t1 = time.perf_counter()
     ms_per_step = 1000.0 * (t1 - t0) / args.steps
 
-    # kernel-timing pass: the same K forwards again, with HIP events recorded
-    # on the launch stream right before and after stage 1 (the dominant
-    # kernel).  An event record between two kernels adds a few microseconds
-    # of idle time, so these forwards are not part of the timed region.
+    # kernel-timing pass: the same K forwards again, with HIP events attached
+    # to the dispatch of stage 1 (the dominant kernel) on its launch stream
+    # (hipExtLaunchKernel start/stop: the kernel's own execution).  Launches
+    # that carry events are not the plain timed ones, so this is a pass of
+    # its own after the timed region.
     step_ev = Events(2 * args.steps)
     for i in range(args.steps):
-        ev = [None, step_ev.ev[2 * i], step_ev.ev[2 * i + 1], None, None]
+        ev = [None] * 8
+        ev[2], ev[3] = step_ev.ev[2 * i], step_ev.ev[2 * i + 1]
         binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
     torch.cuda.synchronize()
     stage1_ms = sum(step_ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
@@ -260,8 +273,9 @@ def run(args):
         achieved = alg["stage1_flops"] / (stage1_ms / 1000.0) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(args.workload)
-    roof["kernel"] = STAGE1_KERNEL
+    roof["traffic"] = load_traffic(args.workload, path_name)
+    roof["kernel"] = STAGE1[path_name][0]
+    roof["source_sha256_16"] = source_hash(STAGE1[path_name][1])
     roof["kernel_us"] = round(stage1_ms * 1000.0, 2)
 
     cpu = None
@@ -290,8 +304,9 @@ def run(args):
                                f"({w.n_routed} routed {w.routing} + shared expert {w.E - 1})",
                    "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
                    "routing": w.routing, "seed": w.seed, "global_batch": w.M,
-                   "parallelism": "single GPU", "block_m": binding.moe_mxfp4_block_m(
-                       w.M, w.D, w.I, w.E, w.topk), "weight_copies": copies},
+                   "parallelism": "single GPU", "path": path_name,
+                   "block_m": binding.moe_mxfp4_block_m(w.M, w.D, w.I, w.E, w.topk),
+                   "weight_copies": copies},
         "us_per_forward": round(ms_per_step * 1000.0, 2),
         "tokens_per_s": round(w.M / sec, 1),
         "hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
@@ -299,7 +314,7 @@ def run(args):
         "roofline_frac_forward": round(max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
                                            alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)) / sec, 4),
         "active_experts": alg["n_active"],
-        "stage_us_warmup": stages_us,
+        "kernel_us_warmup": stages_us,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -191,14 +191,20 @@ int moe_mxfp4_forward_debug(const uint16_t* hidden,
                             uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
                             hipStream_t stream);
 
-/* Forward that records caller-created HIP events on `stream` at the stage
- * boundaries, for timing: stage_events[0] before the prologue (route sort and
- * activation quant, one launch; none on the DIRECT path, whose stage 1
- * quantizes the activations itself), [1] after it, [2] after stage 1 (gate_up +
- * SwiGLU + requant), [3] after stage 2 (down projection x routing weight),
- * [4] after the per-token sum over slots.  Any entry (or the array) may be
- * NULL.  The events are only recorded; the caller reads them after
- * synchronizing. */
+/* Forward that times its own kernels, for benchmarks: caller-created HIP
+ * events are attached to the dispatches of the forward's launches
+ * (hipExtLaunchKernel), so each pair brackets exactly that kernel's
+ * execution.  kernel_events[2*i] / [2*i+1] = start / stop of launch i:
+ *   0  prologue (route sort + activation quant; on the TILED path also the
+ *      sorted copy of the activations: start on the first kernel, stop on
+ *      the second)
+ *   1  stage 1 (gate_up GEMM + SwiGLU + MXFP4 requant; on the DIRECT path
+ *      also the route scan and the activation quant)
+ *   2  stage 2 (down GEMM x routing weight; on the DIRECT path also the
+ *      per-token sum)
+ *   3  per-token sum over slots (sorted paths)
+ * Events of launches a path does not make are not recorded.  Any entry (or
+ * the array) may be NULL.  The caller reads the events after synchronizing. */
 int moe_mxfp4_forward_profiled(const uint16_t* hidden,
                                const uint8_t* w13, const uint8_t* w13_scale,
                                const uint8_t* w2, const uint8_t* w2_scale,
@@ -206,7 +212,7 @@ int moe_mxfp4_forward_profiled(const uint16_t* hidden,
                                uint16_t* out,
                                int M, int D, int I, int E, int topk,
                                void* workspace, size_t workspace_bytes,
-                               hipEvent_t* stage_events, hipStream_t stream);
+                               hipEvent_t* kernel_events, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -173,14 +173,21 @@ def moe_mxfp4_forward(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ou
     return out
 
 
+LAUNCHES = ("prologue", "stage1", "stage2", "reduce")
+PATH_LAUNCHES = {PATH_DIRECT: (1, 2), PATH_STREAM: (0, 1, 2, 3), PATH_TILED: (0, 1, 2, 3)}
+
+
 def moe_mxfp4_forward_profiled(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out,
-                               workspace, stage_events, stream=None):
-    """Forward recording HIP events (raw hipEvent_t handles, ints or None) at the
-    five stage boundaries; see include/moe_mxfp4.h."""
+                               workspace, kernel_events, stream=None):
+    """Forward whose launches carry HIP events (raw hipEvent_t handles, ints or
+    None): kernel_events[2*i], [2*i+1] = start, stop of launch i (LAUNCHES);
+    see include/moe_mxfp4.h.  Launches a path does not make (PATH_LAUNCHES)
+    leave their events unrecorded."""
     args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
-    if len(stage_events) != 5:
-        raise ValueError("stage_events: expected 5 entries")
-    ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+    if len(kernel_events) != 2 * len(LAUNCHES):
+        raise ValueError(f"kernel_events: expected {2 * len(LAUNCHES)} entries")
+    ev = (ctypes.c_void_p * len(kernel_events))(
+        *[ctypes.c_void_p(e) if e else None for e in kernel_events])
     _check("moe_mxfp4_forward_profiled",
            _lib.moe_mxfp4_forward_profiled(*args, ev, _stream(stream)))
     return out

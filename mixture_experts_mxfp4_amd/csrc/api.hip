@@ -158,13 +158,20 @@ struct DebugOut {
     uint16_t* h;
     uint8_t* a2_codes;
     uint8_t* a2_scales;
-    hipEvent_t* events;     // 5 stage-boundary events (entries may be null)
+    hipEvent_t* events;     // kernel events: start/stop of launches 0..3 (entries may be null)
 };
 
-bool mark(const DebugOut* d, int i, hipStream_t stream)
+// Events of launch i (0 prologue, 1 stage 1, 2 stage 2, 3 slot reduction),
+// attached to the kernels' own dispatches.  The prologue's pair spans its
+// two kernels on the tiled path (the stop event goes to the second).
+moe::KernelEvents kernel_events(const DebugOut* d, int i)
 {
-    if (!d || !d->events || !d->events[i]) return true;
-    return hipEventRecord(d->events[i], stream) == hipSuccess;
+    moe::KernelEvents ev;
+    if (d && d->events) {
+        ev.start = d->events[2 * i];
+        ev.stop = d->events[2 * i + 1];
+    }
+    return ev;
 }
 
 int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
@@ -179,14 +186,11 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
                       reinterpret_cast<int32_t*>(ws + L.n_active), out,
                       dbg ? dbg->h : nullptr, M, D, I, E, topk};
     (void)n_cu;
-    // no prologue on this path (events 0 and 1 bracket nothing) and the slot
-    // sum is part of stage 2 (events 3 and 4 likewise)
-    if (!mark(dbg, 0, stream) || !mark(dbg, 1, stream)) return MOE_MXFP4_ERR_HIP;
-    hipError_t e = moe::launch_gemm1_direct(a, stream);
-    if (e != hipSuccess || !mark(dbg, 2, stream)) return MOE_MXFP4_ERR_HIP;
-    e = moe::launch_gemm2_direct(a, stream);
-    if (e != hipSuccess || !mark(dbg, 3, stream) || !mark(dbg, 4, stream))
-        return MOE_MXFP4_ERR_HIP;
+    // two launches: no prologue, and the slot sum is part of stage 2
+    hipError_t e = moe::launch_gemm1_direct(a, stream, kernel_events(dbg, 1));
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_gemm2_direct(a, stream, kernel_events(dbg, 2));
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
     if (dbg) {
         const int R = M * topk;
         if ((dbg->sorted_route || dbg->num_valid) &&
@@ -239,29 +243,33 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     uint16_t* partial = reinterpret_cast<uint16_t*>(ws + L.partial);
     const int nb = int(L.nb);
 
-    if (!mark(dbg, 0, stream)) return MOE_MXFP4_ERR_HIP;
     // block_m 256 selects the LDS-tiled kernels (many routes per expert);
     // smaller blocks the weight-streaming kernels.
     const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
                          block_expert, num_valid, hidden, D, a1q, a1s};
-    hipError_t e = moe::launch_prologue(pa, n_cu, stream);
+    const moe::KernelEvents ev0 = kernel_events(dbg, 0);
+    hipError_t e = moe::launch_prologue(pa, n_cu, stream,
+                                        tile ? moe::KernelEvents{ev0.start, nullptr} : ev0);
     if (e == hipSuccess && tile)
         e = moe::launch_gather_a1(a1q, a1s, sorted_route, num_valid, M, D, topk, L.cap, a1f, a1fs,
-                                  n_cu, stream);
-    if (e != hipSuccess || !mark(dbg, 1, stream)) return MOE_MXFP4_ERR_HIP;
+                                  n_cu, stream, moe::KernelEvents{nullptr, ev0.stop});
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
                       a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap};
-    e = tile ? moe::launch_gemm1_tile(g1, stream) : moe::launch_gemm1(g1, stream);
-    if (e != hipSuccess || !mark(dbg, 2, stream)) return MOE_MXFP4_ERR_HIP;
+    const moe::KernelEvents ev1 = kernel_events(dbg, 1);
+    e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
                       partial, M, D, I, topk, L.bm, nb, L.cap};
-    e = tile ? moe::launch_gemm2_tile(g2, stream) : moe::launch_gemm2(g2, stream);
-    if (e != hipSuccess || !mark(dbg, 3, stream)) return MOE_MXFP4_ERR_HIP;
-    e = moe::launch_reduce_slots(partial, topk_ids, M, D, E, topk, out, n_cu, stream);
-    if (e != hipSuccess || !mark(dbg, 4, stream)) return MOE_MXFP4_ERR_HIP;
+    const moe::KernelEvents ev2 = kernel_events(dbg, 2);
+    e = tile ? moe::launch_gemm2_tile(g2, stream, ev2) : moe::launch_gemm2(g2, stream, ev2);
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    e = moe::launch_reduce_slots(partial, topk_ids, M, D, E, topk, out, n_cu, stream,
+                                 kernel_events(dbg, 3));
+    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     if (dbg) {
         if (dbg->sorted_route &&
@@ -422,9 +430,9 @@ MOE_API int moe_mxfp4_forward_profiled(const uint16_t* hidden, const uint8_t* w1
                                        const uint8_t* w2_scale, const int32_t* topk_ids,
                                        const float* topk_w, uint16_t* out, int M, int D, int I,
                                        int E, int topk, void* workspace, size_t workspace_bytes,
-                                       hipEvent_t* stage_events, hipStream_t stream)
+                                       hipEvent_t* kernel_events, hipStream_t stream)
 {
-    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, stage_events};
+    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, kernel_events};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream);
 }

@@ -43,6 +43,9 @@
 namespace moe {
 
 constexpr int kDirThreads = 256;
+#ifndef MOE_G1_UNROLL
+#define MOE_G1_UNROLL 2          // K tiles of weight loads issued ahead per wave (x NG x 4 KiB)
+#endif
 
 // Picks this workgroup's expert and its routes; run by one whole wave.
 // Pass 1 marks the experts that have a route in an LDS bitmap; the y-th
@@ -183,18 +186,20 @@ __device__ __forceinline__ void publish_slot(const DirectArgs& a, int y, const i
 
 // ---------------------------------------------------------------- stage 1 --
 //
-// Workgroup (c, y): 64-row group c of the prepared gate_up weight of the
-// y-th active expert e (gate columns c*32..+31 and the matching up columns),
-// all K = D, four waves splitting K as in the sorted streaming kernel.
-template <int U>
+// Workgroup (x, y): NG consecutive 64-row groups c = x*NG + j of the prepared
+// gate_up weight of the y-th active expert e (gate columns c*32..+31 and the
+// matching up columns), all K = D, four waves splitting K as in the sorted
+// streaming kernel.  The NG groups share the route scan and each K tile's
+// activation fragment (loaded as bf16 and quantized once).
+template <int U, int NG>
 __global__ void __launch_bounds__(kDirThreads)
 gemm1_direct_kernel(DirectArgs a)
 {
     __shared__ int32_t list[kDirectMaxRoutes];
     __shared__ uint32_t bitmap[kDirectMaxE / 32];
     __shared__ int32_t n_list, e_sel;
-    __shared__ float red[4][4][4][kWave];      // [wave][slice][i][lane]
-    const int c = blockIdx.x, y = blockIdx.y;
+    __shared__ float red[4][NG][4][4][kWave];      // [wave][group][slice][i][lane]
+    const int x = blockIdx.x, y = blockIdx.y;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = a.M * a.topk;
     const int D = a.D, I = a.I;
@@ -205,15 +210,16 @@ gemm1_direct_kernel(DirectArgs a)
             n_list = nw;
             e_sel = ew;
         }
-        if (c == 0) publish_slot(a, y, list, nw, ew, active);
+        if (x == 0) publish_slot(a, y, list, nw, ew, active);
     }
     __syncthreads();
     const int n = n_list, e = e_sel;
     if (e < 0) return;
 
     const int KT = D / 128;
-    const uint8_t* wb = a.w13p + int64_t(e) * I * D + int64_t(c) * KT * 4096 + lane * 16;
-    const uint8_t* sb = a.w13sp + int64_t(e) * I * D / 16 + int64_t(c) * KT * 256 + lane * 4;
+    const int64_t gstride = int64_t(KT) * 4096, sgstride = int64_t(KT) * 256;   // per 64-row group
+    const uint8_t* wb = a.w13p + int64_t(e) * I * D + int64_t(x) * NG * gstride + lane * 16;
+    const uint8_t* sb = a.w13sp + int64_t(e) * I * D / 16 + int64_t(x) * NG * sgstride + lane * 4;
     const int kt_begin = wave * KT / 4, kt_end = (wave + 1) * KT / 4;
 
 #pragma unroll 1
@@ -224,30 +230,41 @@ gemm1_direct_kernel(DirectArgs a)
         // this lane's 32 bf16 of its row at K tile kt: 64 bytes at ap + kt*256
         const uint8_t* ap = reinterpret_cast<const uint8_t*>(a.hidden + tok * D) + (lane / 16) * 64;
 
-        v4f acc[4];
+        v4f acc[NG][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[g][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
+        // U K tiles of loads (NG x 4 KiB of weights per tile) are issued before
+        // their quantization and MFMAs
         auto steps = [&](auto u_const, int kt) {
             constexpr int UU = decltype(u_const)::value;
-            uint32_t sw[UU];
-            uint4 b[UU][4], x[UU][4];
+            uint32_t sw[UU][NG];
+            uint4 b[UU][NG][4], xa[UU][4];
 #pragma unroll
             for (int u = 0; u < UU; ++u) {
-                sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) b[u][q] = ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024);
+                for (int g = 0; g < NG; ++g) {
+                    sw[u][g] = *reinterpret_cast<const uint32_t*>(sb + g * sgstride + (kt + u) * 256);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        b[u][g][q] = ld16_nt(wb + g * gstride + int64_t((kt + u) * 4 + q) * 1024);
+                }
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    x[u][p] = ok ? ld16(ap + int64_t(kt + u) * 256 + p * 16) : make_uint4(0, 0, 0, 0);
+                    xa[u][p] = ok ? ld16(ap + int64_t(kt + u) * 256 + p * 16) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UU; ++u) {
                 uint32_t sa;
-                const uint4 av = mx_quant_lane_block(x[u], sa);
+                const uint4 av = mx_quant_lane_block(xa[u], sa);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[q] = mfma_fp4_16x16x128(av, b[u][q], acc[q], sa, (sw[u] >> (8 * q)) & 0xFFu);
+                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[g][q] = mfma_fp4_16x16x128(av, b[u][g][q], acc[g][q], sa,
+                                                       (sw[u][g] >> (8 * q)) & 0xFFu);
             }
         };
         int kt = kt_begin;
@@ -255,25 +272,29 @@ gemm1_direct_kernel(DirectArgs a)
         for (; kt < kt_end; ++kt) steps(std::integral_constant<int, 1>{}, kt);
 
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][q][i][lane] = acc[q][i];
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[wave][g][q][i][lane] = acc[g][q][i];
         __syncthreads();
 
         // wave w finishes element i = w of every lane: row 4*(lane/16) + w of the tile
-        {
-            const int i = wave;
+        const int i = wave;
+        const int jr = t0 + 4 * (lane / 16) + i;
+        const bool row_ok = jr < n;
+        const int64_t r = row_ok ? list[jr] : 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int c = x * NG + g;
             float s4[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                s4[q] = red[0][q][i][lane] + red[1][q][i][lane] + red[2][q][i][lane] +
-                        red[3][q][i][lane];
+                s4[q] = red[0][g][q][i][lane] + red[1][g][q][i][lane] + red[2][g][q][i][lane] +
+                        red[3][g][q][i][lane];
             // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
             const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
             const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
-            const int jr = t0 + 4 * (lane / 16) + i;
-            const bool row_ok = jr < n;
-            const int64_t r = row_ok ? list[jr] : 0;
             if (a.h_dbg && row_ok) {
                 a.h_dbg[r * I + c * 32 + lane % 16] = uint16_t(h0);
                 a.h_dbg[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
@@ -496,26 +517,27 @@ static bool direct_shape_ok(const DirectArgs& a)
            int64_t(a.M) * a.topk <= kDirectMaxRoutes && a.E <= kDirectMaxE;
 }
 
-hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream)
+hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm1_direct_kernel<4>), dim3(a.I / 32, direct_slots(a.M, a.E, a.topk)),
-                       dim3(kDirThreads), 0, stream, a);
+    // two 64-row groups per workgroup (I is a multiple of 256: I/32 is even)
+    MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2>),
+               dim3(a.I / 64, direct_slots(a.M, a.E, a.topk)), dim3(kDirThreads), 0, stream, ev, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream)
+hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
     const dim3 grid(a.D / (16 * kOsSlices));
     if (a.M <= 16)
-        hipLaunchKernelGGL((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices>), grid,
-                           dim3(kOsThreads), 0, stream, a);
+        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices>), grid,
+                   dim3(kOsThreads), 0, stream, ev, a);
     else
-        hipLaunchKernelGGL((gemm2_direct_kernel<2, 1, kOsSlices>), grid, dim3(kOsThreads), 0,
-                           stream, a);
+        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices>), grid, dim3(kOsThreads), 0, stream, ev,
+                   a);
     return hipGetLastError();
 }
 

@@ -147,22 +147,21 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 }
 
 template <int RT>
-static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream)
+static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<RT>), dim3(a.I / 32, a.nb_cap),
-                       dim3(kGemmThreads), 0, stream, a.a1q, a.a1s, a.w13p, a.w13sp,
-                       a.sorted_route, a.block_expert, a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M,
-                       a.D, a.I, a.topk, a.cap);
+    MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT>), dim3(a.I / 32, a.nb_cap), dim3(kGemmThreads), 0,
+               stream, ev, a.a1q, a.a1s, a.w13p, a.w13sp, a.sorted_route, a.block_expert,
+               a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M, a.D, a.I, a.topk, a.cap);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream)
+hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (a.nb_cap == 0) return hipSuccess;
     switch (a.block_m) {
-    case 16: return launch_g1<1>(a, stream);
-    case 32: return launch_g1<2>(a, stream);
-    case 64: return launch_g1<4>(a, stream);
+    case 16: return launch_g1<1>(a, stream, ev);
+    case 32: return launch_g1<2>(a, stream, ev);
+    case 64: return launch_g1<4>(a, stream, ev);
     default: return hipErrorInvalidValue;
     }
 }

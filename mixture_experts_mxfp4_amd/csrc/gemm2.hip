@@ -237,21 +237,20 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
 }
 
 template <int RT, int U, int NG>
-static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream)
+static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    hipLaunchKernelGGL((gemm2_weighted_kernel<RT, U, NG>), dim3(a.D / (256 * NG), a.nb_cap),
-                       dim3(kGemmThreads), 0, stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
-                       a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk,
-                       a.cap);
+    MOE_LAUNCH((gemm2_weighted_kernel<RT, U, NG>), dim3(a.D / (256 * NG), a.nb_cap),
+               dim3(kGemmThreads), 0, stream, ev, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
+               a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
     return hipGetLastError();
 }
 
 template <int RT>
-static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream)
+static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    hipLaunchKernelGGL((gemm2_simple_kernel<RT>), dim3(a.D / 256, a.nb_cap), dim3(kGemmThreads), 0,
-                       stream, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w,
-                       a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
+    MOE_LAUNCH((gemm2_simple_kernel<RT>), dim3(a.D / 256, a.nb_cap), dim3(kGemmThreads), 0,
+               stream, ev, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w,
+               a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
     return hipGetLastError();
 }
 
@@ -259,13 +258,15 @@ static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream)
 // with double-buffered loads, which keeps enough weight bytes in flight with
 // half the workgroups.  Larger blocks keep one group per wave (their
 // register budget goes to the extra row tiles).
-hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream)
+hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (a.nb_cap == 0) return hipSuccess;
     switch (a.block_m) {
-    case 16: return (a.D / 256) % 2 == 0 ? launch_g2<1, 2, 2>(a, stream) : launch_g2<1, 2, 1>(a, stream);
-    case 32: return launch_g2_simple<2>(a, stream);
-    case 64: return launch_g2_simple<4>(a, stream);
+    case 16:
+        return (a.D / 256) % 2 == 0 ? launch_g2<1, 2, 2>(a, stream, ev)
+                                    : launch_g2<1, 2, 1>(a, stream, ev);
+    case 32: return launch_g2_simple<2>(a, stream, ev);
+    case 64: return launch_g2_simple<4>(a, stream, ev);
     default: return hipErrorInvalidValue;
     }
 }
@@ -334,7 +335,8 @@ reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restr
 // Few tokens: two columns per thread (enough threads to cover the latency);
 // many tokens: eight columns per thread (16-byte accesses).
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
-                               int topk, uint16_t* out, int n_cu, hipStream_t stream)
+                               int topk, uint16_t* out, int n_cu, hipStream_t stream,
+                               const KernelEvents& ev)
 {
     if (int64_t(M) * D == 0) return hipSuccess;
     const bool narrow = int64_t(M) * (D / 2) <= int64_t(n_cu) * 1024;
@@ -342,11 +344,11 @@ hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int 
     int64_t blocks = (nv + 255) / 256;
     if (blocks > int64_t(n_cu) * 16) blocks = int64_t(n_cu) * 16;
     if (narrow)
-        hipLaunchKernelGGL(reduce_slots_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                           partial, ids, M, D, E, topk, out);
+        MOE_LAUNCH(reduce_slots_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, stream, ev,
+                   partial, ids, M, D, E, topk, out);
     else
-        hipLaunchKernelGGL(reduce_slots_kernel<8>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                           partial, ids, M, D, E, topk, out);
+        MOE_LAUNCH(reduce_slots_kernel<8>, dim3(unsigned(blocks)), dim3(256), 0, stream, ev,
+                   partial, ids, M, D, E, topk, out);
     return hipGetLastError();
 }
 

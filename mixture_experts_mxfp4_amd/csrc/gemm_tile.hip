@@ -326,25 +326,25 @@ hipError_t tile_allow_lds()
                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream)
+hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || (2 * a.I) % kTN != 0) return hipErrorInvalidValue;
     TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.block_expert,
                a.num_valid, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s, a.h_dbg, nullptr};
-    hipLaunchKernelGGL(gemm1_tile_kernel, dim3(2 * a.I / kTN, a.nb_cap), dim3(kTThreads),
-                       tile_lds_bytes(), stream, p, a.I);
+    MOE_LAUNCH(gemm1_tile_kernel, dim3(2 * a.I / kTN, a.nb_cap), dim3(kTThreads),
+               uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream)
+hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || a.D % kTN != 0) return hipErrorInvalidValue;
     TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.block_expert,
                a.num_valid, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr, nullptr, a.partial};
-    hipLaunchKernelGGL(gemm2_tile_kernel, dim3(a.D / kTN, a.nb_cap), dim3(kTThreads),
-                       tile_lds_bytes(), stream, p);
+    MOE_LAUNCH(gemm2_tile_kernel, dim3(a.D / kTN, a.nb_cap), dim3(kTThreads),
+               uint32_t(tile_lds_bytes()), stream, ev, p);
     return hipGetLastError();
 }
 

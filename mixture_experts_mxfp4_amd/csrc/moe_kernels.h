@@ -1,11 +1,28 @@
 // Host-side launchers of the gfx950 kernels (internal to libmoe_mxfp4.so).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Optional timestamps of one forward launch: events attached to the kernel's
+// own dispatch (hipExtLaunchKernel), so they time the kernel and nothing else
+// (an event record between two kernels adds microseconds of idle time).
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ev, ...)                                   \
+    do {                                                                                        \
+        if ((ev).start || (ev).stop)                                                            \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (ev).start, (ev).stop, 0, \
+                                  __VA_ARGS__);                                                 \
+        else                                                                                    \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
+    } while (0)
 
 size_t route_lds_bytes(int E);
 hipError_t route_allow_lds(int bytes);   // lift the 64 KiB dynamic-LDS default
@@ -28,7 +45,8 @@ struct PrologueArgs {
     int D;
     uint8_t *a1q, *a1s;
 };
-hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream);
+hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
+                           const KernelEvents& ev = {});
 
 hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
                           uint8_t* dst_scales, int E, int N, int K, int gate_up_I, int inverse,
@@ -38,7 +56,8 @@ hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, u
 // (tiled path), padding rows zeroed.
 hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_t* sorted_route,
                             const int32_t* num_valid, int M, int D, int topk, int64_t cap,
-                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream);
+                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream,
+                            const KernelEvents& ev = {});
 
 // a2 (fragment layout) -> canonical row-major codes [cap][I/2] and scales [cap][I/32].
 hipError_t launch_a2_to_canonical(const uint8_t* a2q, const uint8_t* a2s, int64_t cap, int I,
@@ -54,7 +73,7 @@ struct Gemm1Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
 };
-hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
+hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
 
 struct Gemm2Args {
@@ -66,12 +85,12 @@ struct Gemm2Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
 };
-hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
+hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
 // LDS-tiled variants for block_m = 256.
 hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
-hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream);
-hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream);
+hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
+hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
 // Route-indexed path (small batches): no route sort, no quantization or
 // reduction pass; a2 rows and h rows are indexed by the route r = t*topk + s.
@@ -98,12 +117,13 @@ struct DirectArgs {
     uint16_t* h_dbg;
     int M, D, I, E, topk;
 };
-hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream);
-hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream);
+hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
+hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_direct_rows(const int32_t* ids, int R, int E, int32_t* row_route,
                               int32_t* num_valid, hipStream_t stream);
 
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
-                               int topk, uint16_t* out, int n_cu, hipStream_t stream);
+                               int topk, uint16_t* out, int n_cu, hipStream_t stream,
+                               const KernelEvents& ev = {});
 
 }  // namespace moe

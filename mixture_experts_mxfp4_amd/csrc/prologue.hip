@@ -382,14 +382,15 @@ gather_a1_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1
 
 hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_t* sorted_route,
                             const int32_t* num_valid, int M, int D, int topk, int64_t cap,
-                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream)
+                            uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream,
+                            const KernelEvents& ev)
 {
     const int64_t n = cap * (D / 128);
     if (n == 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
     if (blocks > int64_t(n_cu) * 8) blocks = int64_t(n_cu) * 8;
-    hipLaunchKernelGGL(gather_a1_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a1q, a1s,
-                       sorted_route, num_valid, M, D, topk, cap, a1f, a1fs);
+    MOE_LAUNCH(gather_a1_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, ev, a1q, a1s,
+               sorted_route, num_valid, M, D, topk, cap, a1f, a1fs);
     return hipGetLastError();
 }
 
@@ -447,15 +448,17 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint
     return hipGetLastError();
 }
 
-hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream)
+hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
+                           const KernelEvents& ev)
 {
     const int64_t blocks = 1 + quant_blocks(a.M, a.D, n_cu);
+    const uint32_t lds = uint32_t(route_lds_bytes(a.E));
     if (long_list(a.M, a.topk))
-        hipLaunchKernelGGL(prologue_kernel<4>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
-                           route_lds_bytes(a.E), stream, a);
+        MOE_LAUNCH(prologue_kernel<4>, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds, stream,
+                   ev, a);
     else
-        hipLaunchKernelGGL(prologue_kernel<0>, dim3(unsigned(blocks)), dim3(kPrologueThreads),
-                           route_lds_bytes(a.E), stream, a);
+        MOE_LAUNCH(prologue_kernel<0>, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds, stream,
+                   ev, a);
     return hipGetLastError();
 }
 

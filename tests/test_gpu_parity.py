@@ -330,18 +330,24 @@ def test_forward_deterministic(binding):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_forward_profiled_matches_forward(binding):
+@pytest.mark.parametrize("name,M", [("tiny", None), ("small_batch", 40), ("prefill", 1100)])
+def test_forward_profiled_matches_forward(binding, name, M):
+    """The timed forward gives the same bits as the plain one, and records
+    exactly the launches of its path (events attached to the kernels)."""
     import bench
-    case = workload_case("tiny")
+    case = workload_case(name, M=M)
     d = case.device_inputs()
     ref = case.run_gpu()
-    ev = bench.Events(5)
+    ev = bench.Events(8)
     out = torch.empty_like(d["hidden"])
     ws = binding.alloc_workspace(case.M, case.D, case.I, case.E, case.topk)
     binding.moe_mxfp4_forward_profiled(d["hidden"], *d["prepared"], d["ids"], d["tw"], out, ws,
                                        ev.ev)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
-    for j in range(4):
-        assert ev.ms(j, j + 1) >= 0.0
+    path = binding.moe_mxfp4_path(case.M, case.D, case.I, case.E, case.topk)
+    for i in binding.PATH_LAUNCHES[path]:
+        ms = ev.ms(2 * i, 2 * i + 1)
+        log(f"{name} M={case.M} launch {binding.LAUNCHES[i]}: {1000 * ms:.2f} us")
+        assert ms > 0.0
     ev.close()
