@@ -44,7 +44,7 @@ namespace moe {
 
 constexpr int kDirThreads = 256;
 #ifndef MOE_G1_UNROLL
-#define MOE_G1_UNROLL 2          // K tiles of weight loads issued ahead per wave (x NG x 4 KiB)
+#define MOE_G1_UNROLL 1          // K tiles per double-buffered chunk (x NG x 4 KiB of weights)
 #endif
 
 // Picks this workgroup's expert and its routes; run by one whole wave.
@@ -114,6 +114,28 @@ __device__ __forceinline__ void active_expert_routes(const int32_t* __restrict__
     active_out = __builtin_amdgcn_readlane(inc, kWave - 1);
 }
 
+// Raw buffer loads: a wave-uniform base and size in a buffer resource
+// (SGPRs), a 32-bit per-lane offset, a uniform offset and an immediate, so a
+// wave keeps one address register per stream instead of one 64-bit address
+// per load in flight; offsets at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
+                                             0x00020000);
+}
+constexpr int kCacheStream = 2;            // non-temporal (single-use weight streams)
+template <int IMM, int AUX = 0>
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff + IMM), int(soff), AUX);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), 0);
+}
+
 // One 32-element MX block held by one lane as 64 bytes of bf16 (x[0] =
 // elements 0..7, ...): returns its 16 code bytes (byte b = elements 2b, 2b+1)
 // and the e8m0 scale byte.
@@ -132,13 +154,7 @@ __device__ __forceinline__ uint4 mx_quant_lane_block(const uint4 (&x)[4], uint32
     scale = s;
     uint32_t out[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
-        uint32_t d = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) d |= mx_code2(w[j] & 0xFFFFu, w[j] >> 16, s) << (8 * j);
-        out[p] = d;
-    }
+    for (int p = 0; p < 4; ++p) out[p] = mx_pack8(x[p].x, x[p].y, x[p].z, x[p].w, s);
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
@@ -200,7 +216,7 @@ gemm1_direct_kernel(DirectArgs a)
     __shared__ int32_t n_list, e_sel;
     __shared__ float red[4][NG][4][4][kWave];      // [wave][group][slice][i][lane]
     const int x = blockIdx.x, y = blockIdx.y;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int R = a.M * a.topk;
     const int D = a.D, I = a.I;
     if (wave == 0) {
@@ -217,18 +233,22 @@ gemm1_direct_kernel(DirectArgs a)
     if (e < 0) return;
 
     const int KT = D / 128;
-    const int64_t gstride = int64_t(KT) * 4096, sgstride = int64_t(KT) * 256;   // per 64-row group
-    const uint8_t* wb = a.w13p + int64_t(e) * I * D + int64_t(x) * NG * gstride + lane * 16;
-    const uint8_t* sb = a.w13sp + int64_t(e) * I * D / 16 + int64_t(x) * NG * sgstride + lane * 4;
+    const uint32_t gstride = uint32_t(KT) * 4096, sgstride = uint32_t(KT) * 256;   // per 64-row group
+    // this workgroup's NG groups of codes and scales, and the hidden rows
+    const auto wres = buffer_rsrc(a.w13p + int64_t(e) * I * D + int64_t(x) * NG * gstride,
+                                  NG * gstride);
+    const auto sres = buffer_rsrc(a.w13sp + int64_t(e) * I * D / 16 + int64_t(x) * NG * sgstride,
+                                  NG * sgstride);
+    const uint32_t hbytes = uint32_t(a.M) * D * 2;
+    const auto hres = buffer_rsrc(a.hidden, hbytes);
     const int kt_begin = wave * KT / 4, kt_end = (wave + 1) * KT / 4;
 
 #pragma unroll 1
     for (int t0 = 0; t0 < n; t0 += 16) {
         const int j = t0 + lane % 16;
-        const bool ok = j < n;
-        const int64_t tok = ok ? list[j] / a.topk : 0;
-        // this lane's 32 bf16 of its row at K tile kt: 64 bytes at ap + kt*256
-        const uint8_t* ap = reinterpret_cast<const uint8_t*>(a.hidden + tok * D) + (lane / 16) * 64;
+        // this lane's 32 bf16 of its row at K tile kt: 64 bytes at hoff + kt*256
+        // (rows past the expert's routes read as zero)
+        const uint32_t hoff = j < n ? uint32_t(list[j] / a.topk) * D * 2 + (lane / 16) * 64 : hbytes;
 
         v4f acc[NG][4];
 #pragma unroll
@@ -236,27 +256,37 @@ gemm1_direct_kernel(DirectArgs a)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[g][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // U K tiles of loads (NG x 4 KiB of weights per tile) are issued before
-        // their quantization and MFMAs
-        auto steps = [&](auto u_const, int kt) {
-            constexpr int UU = decltype(u_const)::value;
-            uint32_t sw[UU][NG];
-            uint4 b[UU][NG][4], xa[UU][4];
+        // chunks of U K tiles; the loads of the next chunk are issued before
+        // the quantization and MFMAs of the current one (register double
+        // buffering); tiles past the wave's K range load nothing and add zero
+        uint4 b0[U][NG][4], b1[U][NG][4], x0[U][4], x1[U][4];
+        uint32_t s0[U][NG], s1[U][NG];
+        auto load = [&](uint4 (&b)[U][NG][4], uint4 (&xa)[U][4], uint32_t (&sw)[U][NG], int kt0) {
 #pragma unroll
-            for (int u = 0; u < UU; ++u) {
+            for (int u = 0; u < U; ++u) {
+                const int kt = kt0 + u;
+                const bool in = kt < kt_end;
+                const uint32_t wo = in ? lane * 16 + uint32_t(kt) * 4096 : NG * gstride;
+                const uint32_t so = in ? lane * 4 + uint32_t(kt) * 256 : NG * sgstride;
+                const uint32_t ho = in ? hoff + uint32_t(kt) * 256 : hbytes;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    sw[u][g] = *reinterpret_cast<const uint32_t*>(sb + g * sgstride + (kt + u) * 256);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        b[u][g][q] = ld16_nt(wb + g * gstride + int64_t((kt + u) * 4 + q) * 1024);
+                    sw[u][g] = bld4(sres, so, g * sgstride);
+                    b[u][g][0] = bld16<0, kCacheStream>(wres, wo, g * gstride);
+                    b[u][g][1] = bld16<1024, kCacheStream>(wres, wo, g * gstride);
+                    b[u][g][2] = bld16<2048, kCacheStream>(wres, wo, g * gstride);
+                    b[u][g][3] = bld16<3072, kCacheStream>(wres, wo, g * gstride);
                 }
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    xa[u][p] = ok ? ld16(ap + int64_t(kt + u) * 256 + p * 16) : make_uint4(0, 0, 0, 0);
+                xa[u][0] = bld16<0>(hres, ho, 0);
+                xa[u][1] = bld16<16>(hres, ho, 0);
+                xa[u][2] = bld16<32>(hres, ho, 0);
+                xa[u][3] = bld16<48>(hres, ho, 0);
             }
+        };
+        auto compute = [&](const uint4 (&b)[U][NG][4], const uint4 (&xa)[U][4],
+                           const uint32_t (&sw)[U][NG]) {
 #pragma unroll
-            for (int u = 0; u < UU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 uint32_t sa;
                 const uint4 av = mx_quant_lane_block(xa[u], sa);
 #pragma unroll
@@ -267,9 +297,15 @@ gemm1_direct_kernel(DirectArgs a)
                                                        (sw[u][g] >> (8 * q)) & 0xFFu);
             }
         };
-        int kt = kt_begin;
-        for (; kt + U <= kt_end; kt += U) steps(std::integral_constant<int, U>{}, kt);
-        for (; kt < kt_end; ++kt) steps(std::integral_constant<int, 1>{}, kt);
+        const int nchunks = (kt_end - kt_begin + U - 1) / U;
+        if (nchunks > 0) load(b0, x0, s0, kt_begin);
+        for (int ci = 0; ci < nchunks; ci += 2) {
+            if (ci + 1 < nchunks) load(b1, x1, s1, kt_begin + (ci + 1) * U);
+            compute(b0, x0, s0);
+            if (ci + 1 >= nchunks) break;
+            if (ci + 2 < nchunks) load(b0, x0, s0, kt_begin + (ci + 2) * U);
+            compute(b1, x1, s1);
+        }
 
 #pragma unroll
         for (int g = 0; g < NG; ++g)

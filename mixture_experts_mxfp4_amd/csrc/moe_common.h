@@ -46,21 +46,41 @@ __device__ __forceinline__ uint32_t mx_scale_from_amax(uint32_t amax_mag)
 }
 
 // E2M1 codes under scale byte s with gfx950's scaled conversion
-// v_cvt_scalef32_pk_fp4_f32: it divides by the power of two 2^(s-127) held in
-// the scale operand's exponent field, rounds to nearest even and saturates at
-// 6, keeping the sign.  For every finite bf16 input with |x| / 2^(s-127) < 8
+// v_cvt_scalef32_pk_fp4_bf16: it takes two bf16 values as they are stored,
+// divides by the power of two 2^(s-127) held in the scale operand's exponent
+// field, rounds to nearest even and saturates at 6, keeping the sign, and
+// writes the two codes into the selected byte of its destination (the other
+// bytes pass through).  For every finite bf16 input with |x| / 2^(s-127) < 8
 // (always the case when s comes from the block maximum) and every scale byte
 // 0..254 its codes equal the OCP rule above bit for bit (checked exhaustively
-// on the device; the GPU tests compare the quantizer with the CPU reference).
+// on the device against the rule and against the f32-source form of the same
+// conversion; the GPU tests compare the quantizer with the CPU reference).
 __device__ __forceinline__ float mx_scale_operand(uint32_t s)
 {
     return __builtin_bit_cast(float, s << 23);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// byte `SEL` of `old` <- codes of the bf16 pair `pair` (low half -> low nibble)
+template <int SEL>
+__device__ __forceinline__ uint32_t mx_code_pair(uint32_t old, uint32_t pair, float scale_op)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2_t, pair),
+                                                     scale_op, SEL);
+}
+// four bf16 pairs (8 consecutive elements) -> one dword of codes
+__device__ __forceinline__ uint32_t mx_pack8(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
+                                             uint32_t s)
+{
+    const float so = mx_scale_operand(s);
+    uint32_t d = mx_code_pair<0>(0u, p0, so);
+    d = mx_code_pair<1>(d, p1, so);
+    d = mx_code_pair<2>(d, p2, so);
+    return mx_code_pair<3>(d, p3, so);
+}
 // two elements -> one byte: x0 in the low nibble, x1 in the high nibble
 __device__ __forceinline__ uint32_t mx_code2(uint32_t bits0, uint32_t bits1, uint32_t s)
 {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, bf16_to_f32(bits0), bf16_to_f32(bits1),
-                                                    mx_scale_operand(s), 0) & 0xFFu;
+    return mx_code_pair<0>(0u, (bits0 & 0xFFFFu) | (bits1 << 16), mx_scale_operand(s)) & 0xFFu;
 }
 __device__ __forceinline__ uint32_t mx_code(uint32_t bits16, uint32_t s)
 {

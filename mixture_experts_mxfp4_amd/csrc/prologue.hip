@@ -287,9 +287,7 @@ __device__ void quant_rows_body(const uint16_t* __restrict__ x, int64_t rows, in
         amax = max(amax, dpp<kDppXor1>(amax));      // the block's four lanes
         amax = max(amax, dpp<kDppXor2>(amax));
         const uint32_t s = mx_scale_from_amax(amax);
-        uint32_t packed = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) packed |= mx_code2(w[j] & 0xFFFFu, w[j] >> 16, s) << (8 * j);
+        const uint32_t packed = mx_pack8(w[0], w[1], w[2], w[3], s);
         if (in) {
             reinterpret_cast<uint32_t*>(codes)[i] = packed;
             if ((i & 3) == 0) {
