@@ -22,6 +22,11 @@ Helper modes (used to make the committed rocprofv3 summaries):
     --copy-calibration         run a plain 1 GiB device copy (counter scale)
     --summarize-stats DIR      print the kernel-time summary of a rocprofv3 run
     --summarize-pmc DIR        print per-kernel counter means of a --pmc run
+    --traffic-summary WORKLOAD FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+                               print the stage-1 HBM traffic summary (the
+                               profiles/<kernel>_<workload>_hbm_traffic.txt
+                               format) from FETCH_SIZE / WRITE_SIZE passes of
+                               the workload and of --copy-calibration
 """
 import argparse
 import csv
@@ -245,18 +250,37 @@ def run(args):
     t1 = time.perf_counter()
     ms_per_step = 1000.0 * (t1 - t0) / args.steps
 
-    # kernel-timing pass: the same K forwards again, with HIP events attached
-    # to the dispatch of stage 1 (the dominant kernel) on its launch stream
-    # (hipExtLaunchKernel start/stop: the kernel's own execution).  Launches
-    # that carry events are not the plain timed ones, so this is a pass of
-    # its own after the timed region.
-    step_ev = Events(2 * args.steps)
-    for i in range(args.steps):
-        ev = [None] * 8
-        ev[2], ev[3] = step_ev.ev[2 * i], step_ev.ev[2 * i + 1]
-        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
+    # kernel-timing pass: the same K forwards again, on the same stream, each
+    # with (a) stage 1's span on the device clock (its earliest workgroup
+    # start to its latest workgroup end, recorded by the kernel itself) and (b)
+    # HIP stop events attached to the dispatches of stage 1 and of the launch
+    # before it.  Back-to-back launches start as the previous one ends, so
+    # stop minus previous stop is stage 1's time as the queue sees it; the
+    # runtime's marker for a launch carrying events adds a few microseconds
+    # in front of it, which the span excludes.  Launches with events or spans
+    # are not the plain timed ones, so this is a pass of its own.
+    prev = 0 if 0 in launches else launches[-1]          # launch before stage 1
+    same_forward = prev < 1
+    khz = binding.moe_mxfp4_wall_clock_khz()
+    n_wg = binding.moe_mxfp4_stage1_workgroups(w.M, w.D, w.I, w.E, w.topk)
+    spans = torch.zeros((args.steps + 1, 2 * n_wg), dtype=torch.int64, device=dev)
+    step_ev = Events(2 * (args.steps + 1))
     torch.cuda.synchronize()
-    stage1_ms = sum(step_ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+    for i in range(args.steps + 1):
+        ev = [None] * 8
+        ev[2 * prev + 1] = step_ev.ev[2 * i]
+        ev[3] = step_ev.ev[2 * i + 1]
+        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev,
+                                           spans[i])
+    torch.cuda.synchronize()
+    if same_forward:
+        ev_times = [step_ev.ms(2 * i, 2 * i + 1) for i in range(1, args.steps + 1)]
+    else:
+        ev_times = [step_ev.ms(2 * (i - 1), 2 * i + 1) for i in range(1, args.steps + 1)]
+    sp = spans[1:].cpu()
+    span_ms = [binding.stage1_span_ms(sp[i], khz) for i in range(args.steps)]
+    stage1_ms = sum(span_ms) / len(span_ms)
+    stage1_event_ms = sum(ev_times) / len(ev_times)
     step_ev.close()
     stage_ev.close()
 
@@ -277,6 +301,9 @@ def run(args):
     roof["kernel"] = STAGE1[path_name][0]
     roof["source_sha256_16"] = source_hash(STAGE1[path_name][1])
     roof["kernel_us"] = round(stage1_ms * 1000.0, 2)
+    roof["kernel_us_events"] = round(stage1_event_ms * 1000.0, 2)
+    roof["kernel_timing"] = ("kernel span on the device clock; events: stop-to-stop "
+                             "with the runtime's launch marker")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,6 +393,46 @@ def summarize_pmc(d):
         print(f"{k:80s} {c:>12s} {len(v):10d} {sum(v) / len(v):18.1f}")
 
 
+def _pmc_mean(d, kernel_prefix):
+    """Mean per dispatch of the one counter of a --pmc run, over the kernels
+    whose name (template arguments included) starts with `kernel_prefix`."""
+    vals = []
+    for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+        name = r.get("Kernel_Name", "").replace("void ", "")
+        if name.startswith(kernel_prefix):
+            vals.append(float(r.get("Counter_Value", 0)))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_prefix} in {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    from mixture_experts_mxfp4_amd import binding, inputs
+    w = inputs.WORKLOADS[workload]
+    path_name = binding.PATH_NAMES[binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)]
+    kernel, sources = STAGE1[path_name]
+    copy_kib = float(1 << 30) / 1024.0
+    cf, _ = _pmc_mean(copy_fetch_dir, "__amd_rocclr_copyBuffer")
+    cw, _ = _pmc_mean(copy_write_dir, "__amd_rocclr_copyBuffer")
+    f, nf = _pmc_mean(fetch_dir, "moe::" + kernel)
+    wr, nw = _pmc_mean(write_dir, "moe::" + kernel)
+    ff, fw = copy_kib / cf, copy_kib / cw
+    traffic = (f * ff + wr * fw) * 1024.0
+    print(f"# HBM traffic of {kernel} on the {workload} workload (path {path_name})")
+    print(f"# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same counters")
+    print(f"# read for a plain 1 GiB device copy (bench.py --copy-calibration)")
+    print(f"workload: {workload}")
+    print(f"kernel: {kernel}")
+    print(f"stage1_source_sha256_16: {source_hash(sources)}")
+    print(f"fetch_size_kib_per_dispatch: {f:.1f}  ({nf} dispatches)")
+    print(f"write_size_kib_per_dispatch: {wr:.1f}  ({nw} dispatches)")
+    print(f"copy_fetch_size_kib: {cf:.1f}  (1 GiB = {copy_kib:.0f} KiB)")
+    print(f"copy_write_size_kib: {cw:.1f}")
+    print(f"fetch_scale: {ff:.4f}")
+    print(f"write_scale: {fw:.4f}")
+    print(f"traffic_bytes_per_launch: {traffic:.0f}")
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -380,7 +447,11 @@ def main():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--summarize-stats", metavar="DIR")
     p.add_argument("--summarize-pmc", metavar="DIR")
+    p.add_argument("--traffic-summary", nargs=5,
+                   metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = p.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats)
     if args.summarize_pmc:

@@ -191,10 +191,12 @@ int moe_mxfp4_forward_debug(const uint16_t* hidden,
                             uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
                             hipStream_t stream);
 
-/* Forward that times its own kernels, for benchmarks: caller-created HIP
- * events are attached to the dispatches of the forward's launches
- * (hipExtLaunchKernel), so each pair brackets exactly that kernel's
- * execution.  kernel_events[2*i] / [2*i+1] = start / stop of launch i:
+/* Forward that times its own kernels, for benchmarks.
+ *
+ * kernel_events (array of 8, entries may be NULL, or NULL): caller-created
+ * HIP events attached to the dispatches of the forward's launches
+ * (hipExtLaunchKernel); kernel_events[2*i] / [2*i+1] = start / stop of
+ * launch i:
  *   0  prologue (route sort + activation quant; on the TILED path also the
  *      sorted copy of the activations: start on the first kernel, stop on
  *      the second)
@@ -203,8 +205,18 @@ int moe_mxfp4_forward_debug(const uint16_t* hidden,
  *   2  stage 2 (down GEMM x routing weight; on the DIRECT path also the
  *      per-token sum)
  *   3  per-token sum over slots (sorted paths)
- * Events of launches a path does not make are not recorded.  Any entry (or
- * the array) may be NULL.  The caller reads the events after synchronizing. */
+ * Events of launches a path does not make are not recorded.  The runtime
+ * puts a marker in front of each launch that carries events, which delays
+ * that kernel's start by a few microseconds; the spans below have no such
+ * effect.
+ *
+ * stage1_clock (device pointer to 2 * moe_mxfp4_stage1_workgroups(...)
+ * uint64, 8-byte aligned, or NULL): stage-1 workgroup w stores its start in
+ * [2w] and, when all its waves are done, its end in [2w+1], in ticks of the
+ * device's constant-rate clock (moe_mxfp4_wall_clock_khz); the kernel's span
+ * is the smallest start to the largest end.  Every workgroup writes both.
+ *
+ * The caller reads events and spans after synchronizing. */
 int moe_mxfp4_forward_profiled(const uint16_t* hidden,
                                const uint8_t* w13, const uint8_t* w13_scale,
                                const uint8_t* w2, const uint8_t* w2_scale,
@@ -212,7 +224,16 @@ int moe_mxfp4_forward_profiled(const uint16_t* hidden,
                                uint16_t* out,
                                int M, int D, int I, int E, int topk,
                                void* workspace, size_t workspace_bytes,
-                               hipEvent_t* kernel_events, hipStream_t stream);
+                               hipEvent_t* kernel_events, uint64_t* stage1_clock,
+                               hipStream_t stream);
+
+/* Frequency (kHz) of the clock of stage1_clock records on the current
+ * device; 0 on error. */
+int moe_mxfp4_wall_clock_khz(void);
+
+/* Number of workgroups of the stage-1 launch for this shape (0 for an
+ * invalid shape or M = 0). */
+int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk);
 
 #ifdef __cplusplus
 }

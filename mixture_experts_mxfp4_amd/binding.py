@@ -34,7 +34,10 @@ _lib.moe_mxfp4_forward.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
 _lib.moe_mxfp4_forward.restype = _I
 _lib.moe_mxfp4_forward_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
 _lib.moe_mxfp4_forward_debug.restype = _I
-_lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P]
+_lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P, _P]
+_lib.moe_mxfp4_wall_clock_khz.argtypes, _lib.moe_mxfp4_wall_clock_khz.restype = [], _I
+_lib.moe_mxfp4_stage1_workgroups.argtypes = [_I] * 5
+_lib.moe_mxfp4_stage1_workgroups.restype = _I64
 _lib.moe_mxfp4_forward_profiled.restype = _I
 _lib.moe_mxfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.moe_mxfp4_quantize.restype = _I
@@ -45,7 +48,8 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_bl
            "moe_mxfp4_path",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
            "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
-           "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled")
+           "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled",
+           "moe_mxfp4_wall_clock_khz", "moe_mxfp4_stage1_workgroups")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -177,19 +181,45 @@ LAUNCHES = ("prologue", "stage1", "stage2", "reduce")
 PATH_LAUNCHES = {PATH_DIRECT: (1, 2), PATH_STREAM: (0, 1, 2, 3), PATH_TILED: (0, 1, 2, 3)}
 
 
+def moe_mxfp4_wall_clock_khz() -> int:
+    """Frequency of the device clock that stage-1 spans are counted in."""
+    return int(_lib.moe_mxfp4_wall_clock_khz())
+
+
+def moe_mxfp4_stage1_workgroups(M, D, I, E, topk) -> int:
+    return int(_lib.moe_mxfp4_stage1_workgroups(M, D, I, E, topk))
+
+
+def stage1_span_ms(records, khz):
+    """Span (ms) of stage 1 from its per-workgroup [start, end] clock records."""
+    r = records.reshape(-1, 2)
+    return float((r[:, 1].max() - r[:, 0].min()).item()) / khz
+
+
 def moe_mxfp4_forward_profiled(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out,
-                               workspace, kernel_events, stream=None):
+                               workspace, kernel_events, stage1_clock=None, stream=None):
     """Forward whose launches carry HIP events (raw hipEvent_t handles, ints or
     None): kernel_events[2*i], [2*i+1] = start, stop of launch i (LAUNCHES);
     see include/moe_mxfp4.h.  Launches a path does not make (PATH_LAUNCHES)
-    leave their events unrecorded."""
+    leave their events unrecorded.  stage1_clock: None or a contiguous device
+    int64 tensor of 2 * moe_mxfp4_stage1_workgroups(...) elements that
+    receives every stage-1 workgroup's [start, end] clock (stage1_span_ms)."""
     args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
     if len(kernel_events) != 2 * len(LAUNCHES):
         raise ValueError(f"kernel_events: expected {2 * len(LAUNCHES)} entries")
     ev = (ctypes.c_void_p * len(kernel_events))(
         *[ctypes.c_void_p(e) if e else None for e in kernel_events])
+    clk = None
+    if stage1_clock is not None:
+        M, topk = topk_ids.shape
+        E, D, I = _weight_dims(w13, w2)
+        need = 2 * moe_mxfp4_stage1_workgroups(M, D, I, E, topk)
+        if (stage1_clock.dtype != torch.int64 or stage1_clock.numel() < need
+                or not stage1_clock.is_cuda or not stage1_clock.is_contiguous()):
+            raise TypeError(f"stage1_clock: expected a contiguous device int64 tensor of {need}")
+        clk = ctypes.c_void_p(stage1_clock.data_ptr())
     _check("moe_mxfp4_forward_profiled",
-           _lib.moe_mxfp4_forward_profiled(*args, ev, _stream(stream)))
+           _lib.moe_mxfp4_forward_profiled(*args, ev, clk, _stream(stream)))
     return out
 
 

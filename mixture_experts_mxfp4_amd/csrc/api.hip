@@ -159,6 +159,7 @@ struct DebugOut {
     uint8_t* a2_codes;
     uint8_t* a2_scales;
     hipEvent_t* events;     // kernel events: start/stop of launches 0..3 (entries may be null)
+    uint64_t* stage1_clock; // device [2 x stage-1 workgroups]: their start/end clocks (may be null)
 };
 
 // Events of launch i (0 prologue, 1 stage 1, 2 stage 2, 3 slot reduction),
@@ -184,7 +185,8 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
                       reinterpret_cast<int32_t*>(ws + L.slot_layers),
                       reinterpret_cast<int32_t*>(ws + L.route_of),
                       reinterpret_cast<int32_t*>(ws + L.n_active), out,
-                      dbg ? dbg->h : nullptr, M, D, I, E, topk};
+                      dbg ? dbg->h : nullptr, M, D, I, E, topk,
+                      dbg ? dbg->stage1_clock : nullptr};
     (void)n_cu;
     // two launches: no prologue, and the slot sum is part of stage 2
     hipError_t e = moe::launch_gemm1_direct(a, stream, kernel_events(dbg, 1));
@@ -257,7 +259,8 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
-                      a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap};
+                      a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap,
+                      dbg ? dbg->stage1_clock : nullptr};
     const moe::KernelEvents ev1 = kernel_events(dbg, 1);
     e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
@@ -305,6 +308,24 @@ MOE_API int moe_mxfp4_block_m(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk)) return 0;
     return choose_block_m(M, E, topk);
+}
+
+MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk) || M == 0) return 0;
+    const Layout L = layout(M, D, I, E, topk);
+    if (L.path == MOE_MXFP4_PATH_DIRECT) return int64_t(I / 64) * moe::direct_slots(M, E, topk);
+    if (L.path == MOE_MXFP4_PATH_TILED) return int64_t(2 * I / 256) * L.nb;
+    return int64_t(I / 32) * L.nb;
+}
+
+MOE_API int moe_mxfp4_wall_clock_khz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return 0;
+    return khz;
 }
 
 MOE_API int moe_mxfp4_path(int M, int D, int I, int E, int topk)
@@ -387,7 +408,7 @@ MOE_API int moe_mxfp4_forward_debug(const uint16_t* hidden, const uint8_t* w13,
     const void* opt[] = {sorted_route, num_valid, h, a2_codes, a2_scales};
     for (const void* p : opt)
         if (p && !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
-    DebugOut d{sorted_route, num_valid, h, a2_codes, a2_scales, nullptr};
+    DebugOut d{sorted_route, num_valid, h, a2_codes, a2_scales, nullptr, nullptr};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream);
 }
@@ -430,9 +451,11 @@ MOE_API int moe_mxfp4_forward_profiled(const uint16_t* hidden, const uint8_t* w1
                                        const uint8_t* w2_scale, const int32_t* topk_ids,
                                        const float* topk_w, uint16_t* out, int M, int D, int I,
                                        int E, int topk, void* workspace, size_t workspace_bytes,
-                                       hipEvent_t* kernel_events, hipStream_t stream)
+                                       hipEvent_t* kernel_events, uint64_t* stage1_clock,
+                                       hipStream_t stream)
 {
-    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, kernel_events};
+    if (stage1_clock && !aligned(stage1_clock, 8)) return MOE_MXFP4_ERR_INVALID_ARG;
+    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, kernel_events, stage1_clock};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream);
 }

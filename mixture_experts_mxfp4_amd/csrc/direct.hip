@@ -219,6 +219,7 @@ gemm1_direct_kernel(DirectArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int R = a.M * a.topk;
     const int D = a.D, I = a.I;
+    span_begin(a.clk);
     if (wave == 0) {
         int nw, ew, active;
         active_expert_routes(a.ids, R, a.E, y, bitmap, list, nw, ew, active);
@@ -230,7 +231,10 @@ gemm1_direct_kernel(DirectArgs a)
     }
     __syncthreads();
     const int n = n_list, e = e_sel;
-    if (e < 0) return;
+    if (e < 0) {
+        span_end(a.clk);
+        return;
+    }
 
     const int KT = D / 128;
     const uint32_t gstride = uint32_t(KT) * 4096, sgstride = uint32_t(KT) * 256;   // per 64-row group
@@ -348,6 +352,7 @@ gemm1_direct_kernel(DirectArgs a)
         }
         __syncthreads();          // red is rewritten by the next row tile
     }
+    span_end(a.clk);
 }
 
 // ---------------------------------------------------------------- stage 2 --

@@ -39,7 +39,7 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                           const int32_t* __restrict__ block_expert,
                           const int32_t* __restrict__ num_valid, uint8_t* __restrict__ a2q,
                           uint8_t* __restrict__ a2s, uint16_t* __restrict__ h_dbg, int M, int D,
-                          int I, int topk, int64_t cap)
+                          int I, int topk, int64_t cap, uint64_t* clk)
 {
     constexpr int BM = 16 * RT;
     constexpr int U = g1_unroll<RT>();
@@ -47,7 +47,11 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 
     const int c = blockIdx.x;          // MXFP4 group of h = 64-row group of w13p
     const int blk = blockIdx.y;
-    if (blk * BM >= num_valid[0]) return;
+    span_begin(clk);
+    if (blk * BM >= num_valid[0]) {
+        span_end(clk);
+        return;
+    }
     const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
@@ -144,6 +148,7 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
             }
         }
     }
+    span_end(clk);
 }
 
 template <int RT>
@@ -151,7 +156,7 @@ static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream, const Kernel
 {
     MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT>), dim3(a.I / 32, a.nb_cap), dim3(kGemmThreads), 0,
                stream, ev, a.a1q, a.a1s, a.w13p, a.w13sp, a.sorted_route, a.block_expert,
-               a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M, a.D, a.I, a.topk, a.cap);
+               a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M, a.D, a.I, a.topk, a.cap, a.clk);
     return hipGetLastError();
 }
 

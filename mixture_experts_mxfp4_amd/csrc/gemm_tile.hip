@@ -98,6 +98,7 @@ struct TileArgs {
     uint8_t* a2s;
     uint16_t* h_dbg;
     uint16_t* partial;         // stage 2 output [M*topk][N]
+    uint64_t* clk;             // optional kernel span (stage 1)
 };
 
 // The per-wave source pointers of one stage's five loads; every load is a
@@ -223,7 +224,11 @@ gemm1_tile_kernel(TileArgs p, int I)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int ntile = blockIdx.x, blk = blockIdx.y;
-    if (blk * kTM >= p.num_valid[0]) return;
+    span_begin(p.clk);
+    if (blk * kTM >= p.num_valid[0]) {
+        span_end(p.clk);
+        return;
+    }
     const int e = p.block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
@@ -267,6 +272,7 @@ gemm1_tile_kernel(TileArgs p, int I)
             }
         }
     }
+    span_end(p.clk);
 }
 
 // ------------------------------------------------------------ stage 2 ----
@@ -331,7 +337,7 @@ hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const Kerne
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || (2 * a.I) % kTN != 0) return hipErrorInvalidValue;
     TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.block_expert,
-               a.num_valid, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s, a.h_dbg, nullptr};
+               a.num_valid, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s, a.h_dbg, nullptr, a.clk};
     MOE_LAUNCH(gemm1_tile_kernel, dim3(2 * a.I / kTN, a.nb_cap), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
     return hipGetLastError();
@@ -342,7 +348,8 @@ hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const Kerne
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || a.D % kTN != 0) return hipErrorInvalidValue;
     TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.block_expert,
-               a.num_valid, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr, nullptr, a.partial};
+               a.num_valid, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr, nullptr, a.partial,
+               nullptr};
     MOE_LAUNCH(gemm2_tile_kernel, dim3(a.D / kTN, a.nb_cap), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p);
     return hipGetLastError();

@@ -138,6 +138,33 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
 
 __device__ __forceinline__ float silu_fast(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }
 
+// ------------------------------------------------------ kernel span -----
+//
+// Optional record of one kernel's execution on the device's constant-rate
+// real-time clock (wall_clock64, hipDeviceAttributeWallClockRate): workgroup
+// w = blockIdx.x + gridDim.x * blockIdx.y stores its start in clk[2w] and,
+// once all its waves are done, its end in clk[2w + 1] (plain stores to slots
+// of its own: no contention).  The kernel's span is the earliest start to
+// the latest end; it times the kernel from inside, without the queue
+// packets that events attached to a launch add in front of it.  A null clk
+// records nothing (clk is a kernel argument: the branches are uniform).
+__device__ __forceinline__ int64_t span_slot()
+{
+    return 2 * (int64_t(blockIdx.y) * gridDim.x + blockIdx.x);
+}
+__device__ __forceinline__ void span_begin(uint64_t* clk)
+{
+    if (clk && threadIdx.x == 0) clk[span_slot()] = uint64_t(wall_clock64());
+}
+// every thread of the workgroup calls it (it holds a workgroup barrier)
+__device__ __forceinline__ void span_end(uint64_t* clk)
+{
+    if (clk) {
+        __syncthreads();
+        if (threadIdx.x == 0) clk[span_slot() + 1] = uint64_t(wall_clock64());
+    }
+}
+
 // ------------------------------------------------------------- MFMA -----
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 (format code 4).

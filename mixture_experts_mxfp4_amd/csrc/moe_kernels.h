@@ -72,6 +72,7 @@ struct Gemm1Args {
     uint16_t* h_dbg;
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
+    uint64_t* clk = nullptr;       // optional kernel span (span_begin / span_end)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
@@ -116,6 +117,7 @@ struct DirectArgs {
     uint16_t* out;                 // bf16 [M][D]
     uint16_t* h_dbg;
     int M, D, I, E, topk;
+    uint64_t* clk = nullptr;       // optional stage-1 span (span_begin / span_end)
 };
 hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});

@@ -341,10 +341,18 @@ def test_forward_profiled_matches_forward(binding, name, M):
     ev = bench.Events(8)
     out = torch.empty_like(d["hidden"])
     ws = binding.alloc_workspace(case.M, case.D, case.I, case.E, case.topk)
+    n_wg = binding.moe_mxfp4_stage1_workgroups(case.M, case.D, case.I, case.E, case.topk)
+    span = torch.zeros(2 * n_wg, dtype=torch.int64, device="cuda")
     binding.moe_mxfp4_forward_profiled(d["hidden"], *d["prepared"], d["ids"], d["tw"], out, ws,
-                                       ev.ev)
+                                       ev.ev, span)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    rec = span.cpu().reshape(-1, 2)
+    khz = binding.moe_mxfp4_wall_clock_khz()
+    assert khz > 0 and bool((rec > 0).all()) and bool((rec[:, 1] >= rec[:, 0]).all())
+    ms = binding.stage1_span_ms(rec, khz)
+    log(f"{name} M={case.M} stage-1 span {1000.0 * ms:.2f} us over {n_wg} workgroups")
+    assert 0.0 < ms < 1000.0
     path = binding.moe_mxfp4_path(case.M, case.D, case.I, case.E, case.topk)
     for i in binding.PATH_LAUNCHES[path]:
         ms = ev.ms(2 * i, 2 * i + 1)
