@@ -180,6 +180,7 @@ def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0):
     wq = (w13.reshape(Eu, 2 * w.I, w.D // 2), w13s.reshape(Eu, 2 * w.I, w.D // 32),
           w2.reshape(Eu, w.D, w.I // 2), w2s.reshape(Eu, w.D, w.I // 32))
     hb = inputs.bf16_bits(hidden)
+    threads = min(threads, n)          # the oracle runs one token per thread
     t0 = time.perf_counter()
     oracle.forward(hb, *wq, sub_ids, tw.numpy(), tokens=toks, nthreads=threads)
     dt = time.perf_counter() - t0
