@@ -96,7 +96,7 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, total;
 };
 
 Layout layout(int M, int D, int I, int E, int topk)
@@ -108,7 +108,7 @@ Layout layout(int M, int D, int I, int E, int topk)
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    L.slot_expert = L.slot_layers = L.route_of = L.n_active = 0;
+    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = 0;
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
         // rows indexed by route: a2 codes and scales row-major; the expert
         // slots with their token -> route tables
@@ -125,6 +125,7 @@ Layout layout(int M, int D, int I, int E, int topk)
         L.total = off;
         return L;
     }
+    L.chunk_counts = take(sizeof(int32_t) * size_t(moe::route_chunks(M, topk)) * E);
     L.sorted_route = take(sizeof(int32_t) * size_t(L.cap));
     L.sorted_w = take(sizeof(float) * size_t(L.cap));
     L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
@@ -249,7 +250,8 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     // smaller blocks the weight-streaming kernels.
     const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
-                         block_expert, num_valid, hidden, D, a1q, a1s};
+                         block_expert, num_valid, hidden, D, a1q, a1s,
+                         reinterpret_cast<int32_t*>(ws + L.chunk_counts)};
     const moe::KernelEvents ev0 = kernel_events(dbg, 0);
     hipError_t e = moe::launch_prologue(pa, n_cu, stream,
                                         tile ? moe::KernelEvents{ev0.start, nullptr} : ev0);

@@ -48,11 +48,11 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     const int c = blockIdx.x;          // MXFP4 group of h = 64-row group of w13p
     const int blk = blockIdx.y;
     span_begin(clk);
-    if (blk * BM >= num_valid[0]) {
+    const int e = block_expert[blk];       // -1 past the used blocks
+    if (e < 0) {
         span_end(clk);
         return;
     }
-    const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
     const int KT = D / 128;

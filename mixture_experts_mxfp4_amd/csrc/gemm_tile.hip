@@ -225,11 +225,11 @@ gemm1_tile_kernel(TileArgs p, int I)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int ntile = blockIdx.x, blk = blockIdx.y;
     span_begin(p.clk);
-    if (blk * kTM >= p.num_valid[0]) {
+    const int e = p.block_expert[blk];     // -1 past the used blocks
+    if (e < 0) {
         span_end(p.clk);
         return;
     }
-    const int e = p.block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
 
@@ -284,8 +284,8 @@ gemm2_tile_kernel(TileArgs p)
     __shared__ int32_t s_route[kTM];
     __shared__ float s_w[kTM];
     const int ntile = blockIdx.x, blk = blockIdx.y;
-    if (blk * kTM >= p.num_valid[0]) return;
-    const int e = p.block_expert[blk];
+    const int e = p.block_expert[blk];     // -1 past the used blocks
+    if (e < 0) return;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const int R = p.M * p.topk;

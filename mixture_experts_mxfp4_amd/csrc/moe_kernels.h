@@ -33,7 +33,9 @@ hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int top
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                              uint8_t* scales, int n_cu, hipStream_t stream);
 
-// Route sort (workgroup 0) + activation quantization (the other workgroups).
+// Route sort + activation quantization: one launch (workgroup 0 sorts, the
+// others quantize), or for long lists two (counting + quantization, then the
+// chunked scatter).
 struct PrologueArgs {
     const int32_t* ids;
     const float* tw;
@@ -44,7 +46,10 @@ struct PrologueArgs {
     const uint16_t* hidden;
     int D;
     uint8_t *a1q, *a1s;
+    int32_t* chunk_counts;         // [route_chunks][E] for long lists (else unused)
 };
+// Chunks of the two-launch route sort for this many routes (0: one workgroup).
+int route_chunks(int M, int topk);
 hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
                            const KernelEvents& ev = {});
 

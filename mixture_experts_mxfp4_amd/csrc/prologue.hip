@@ -35,6 +35,7 @@ namespace moe {
 
 constexpr int kPrologueThreads = 1024;
 constexpr int kRouteWaves = kPrologueThreads / kWave;
+constexpr int kRouteChunk = 4 * kPrologueThreads;   // routes per workgroup of the chunked sort
 
 // Lanes of this wave whose (valid) expert id equals mine.
 __device__ __forceinline__ uint64_t same_expert_lanes(int id, bool valid, int nbits)
@@ -50,44 +51,39 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int id, bool valid, int nb
 }
 
 // Every slot of the route list starts as padding (route M*topk, weight 0) and
-// every block as unused (expert -1), written by the whole workgroup before its
-// barrier; the sort then only stores the real routes and the used blocks'
-// experts (the padding is never written per expert, one slot at a time).
+// every block as unused (expert -1); the sort then only stores the real
+// routes and the used blocks' experts (the padding is never written per
+// expert, one slot at a time).  `part`/`parts` split the fill among the
+// workgroups of a launch; the fill is ordered before the sort's own stores
+// by a barrier (one workgroup) or by the launch boundary (chunked sort).
 __device__ __forceinline__ void fill_padding(int R, int bm, int nb_cap,
                                              int32_t* __restrict__ sorted_route,
                                              float* __restrict__ sorted_w,
-                                             int32_t* __restrict__ block_expert)
+                                             int32_t* __restrict__ block_expert, int part = 0,
+                                             int parts = 1)
 {
     const int64_t cap = int64_t(nb_cap) * bm;
-    for (int64_t p = threadIdx.x; p < cap; p += kPrologueThreads) {
+    const int64_t p0 = cap * part / parts, p1 = cap * (part + 1) / parts;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += kPrologueThreads) {
         sorted_route[p] = R;
         sorted_w[p] = 0.0f;
     }
-    for (int b = threadIdx.x; b < nb_cap; b += kPrologueThreads) block_expert[b] = -1;
+    const int b0 = int(int64_t(nb_cap) * part / parts), b1 = int(int64_t(nb_cap) * (part + 1) / parts);
+    for (int b = b0 + threadIdx.x; b < b1; b += kPrologueThreads) block_expert[b] = -1;
 }
 
+// Per-wave histograms of the routes [c0, c1): each wave takes a contiguous
+// sub-range, 64 routes at a time; lanes holding the same expert are found
+// with ballots over the bits of the id, and the lowest such lane adds their
+// number to the wave's row cnt[wave * E + id] (no atomics).
 template <int U>
-__device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
-                                int M, int topk, int E, int bm, int nb_cap,
-                                int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
-                                int32_t* __restrict__ block_expert,
-                                int32_t* __restrict__ num_valid, int32_t* lds)
+__device__ __forceinline__ void wave_histograms(const int32_t* __restrict__ ids, int c0, int c1,
+                                                int E, int nbits, int32_t* cnt)
 {
-    int32_t* cnt = lds;                                   // [waves][E]
-    int32_t* wave_sum = lds + kRouteWaves * E;            // [2][waves] scan scratch
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int R = M * topk;
-    const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    for (int i = tid; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
-    fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert);
-    __syncthreads();
-
-    const int per_wave = (R + kRouteWaves - 1) / kRouteWaves;
-    const int w_begin = min(R, wave * per_wave), w_end = min(R, w_begin + per_wave);
-
-    // pass 1: per-wave histogram
+    const int per_wave = (c1 - c0 + kRouteWaves - 1) / kRouteWaves;
+    const int w_begin = min(c1, c0 + wave * per_wave), w_end = min(c1, w_begin + per_wave);
 #pragma unroll 1
     for (int base = w_begin; base < w_end; base += kWave * U) {
         int id[U];
@@ -103,17 +99,60 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
             if (valid && (peers & lanes_below) == 0) cnt[wave * E + id[u]] += __popcll(peers);
         }
     }
+}
+
+// Sorts the routes [c0, c1) (one chunk of the list, or all of it) into their
+// final places.  With chunk_counts (the per-expert counts of all G chunks,
+// [G][E], from the counting launch) the expert segments' bases come from the
+// totals of every chunk and this chunk's routes go after those of chunks
+// 0..g-1; without, the chunk is the whole list.  Chunk 0 (or the only one)
+// writes block_expert and num_valid.  The order inside an expert's segment
+// is ascending route: chunk, then wave, then lane order.
+template <int U>
+__device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
+                                int M, int topk, int E, int bm, int nb_cap,
+                                int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
+                                int32_t* __restrict__ block_expert,
+                                int32_t* __restrict__ num_valid, int32_t* lds,
+                                int c0 = 0, int c1 = -1,
+                                const int32_t* __restrict__ chunk_counts = nullptr, int G = 1,
+                                int g = 0)
+{
+    int32_t* cnt = lds;                                   // [waves][E]
+    int32_t* wave_sum = lds + kRouteWaves * E;            // [2][waves] scan scratch
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int R = M * topk;
+    if (c1 < 0) c1 = R;
+    const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int i = tid; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
+    if (!chunk_counts) fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert);
     __syncthreads();
 
-    // scan over experts of the padded counts (one expert per thread per round)
+    // pass 1: per-wave histogram of this chunk
+    wave_histograms<U>(ids, c0, c1, E, nbits, cnt);
+    __syncthreads();
+
+    // scan over experts of the padded totals (one expert per thread per round)
     int carry = 0, valid_total = 0;
 #pragma unroll 1
     for (int e0 = 0; e0 < E; e0 += kPrologueThreads) {
         const int e = e0 + tid;
-        int total = 0;
-        if (e < E)
+        int total = 0, earlier = 0;       // all routes of e; those of chunks before this one
+        if (e < E) {
+            if (chunk_counts) {
 #pragma unroll 1
-            for (int w = 0; w < kRouteWaves; ++w) total += cnt[w * E + e];
+                for (int c = 0; c < G; ++c) {
+                    const int n = chunk_counts[int64_t(c) * E + e];
+                    total += n;
+                    earlier += c < g ? n : 0;
+                }
+            } else {
+#pragma unroll 1
+                for (int w = 0; w < kRouteWaves; ++w) total += cnt[w * E + e];
+            }
+        }
         const int padded = (total + bm - 1) / bm * bm;
         int inc = padded, vinc = total;               // inclusive scans within the wave
 #pragma unroll 1
@@ -133,26 +172,29 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
         }
         const int base_e = carry + before + inc - padded;
         if (e < E) {
-            int run = base_e;
+            int run = base_e + earlier;
 #pragma unroll 1
             for (int w = 0; w < kRouteWaves; ++w) {
                 int c = cnt[w * E + e];
                 cnt[w * E + e] = run;
                 run += c;
             }
+            if (g == 0)
 #pragma unroll 1
-            for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
+                for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
         }
         carry += all;
         valid_total += vall;
         __syncthreads();
     }
-    if (tid == 0) {
+    if (tid == 0 && g == 0) {
         num_valid[0] = carry;
         num_valid[1] = valid_total;
     }
 
     // pass 2: stable scatter (each wave only touches its own histogram row)
+    const int per_wave = (c1 - c0 + kRouteWaves - 1) / kRouteWaves;
+    const int w_begin = min(c1, c0 + wave * per_wave), w_end = min(c1, w_begin + per_wave);
 #pragma unroll 1
     for (int base = w_begin; base < w_end; base += kWave * U) {
         int id[U];
@@ -178,6 +220,28 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
             }
             __builtin_amdgcn_wave_barrier();
         }
+    }
+}
+
+// Counting launch of the chunked sort (chunk g of kRouteChunk routes): the
+// chunk's per-expert counts, and part g of the padding fill.
+__device__ void route_count_body(const int32_t* __restrict__ ids, int R, int E, int bm, int nb_cap,
+                                 int g, int G, int32_t* __restrict__ chunk_counts,
+                                 int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
+                                 int32_t* __restrict__ block_expert, int32_t* lds)
+{
+    int32_t* cnt = lds;                                   // [waves][E]
+    const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    for (int i = threadIdx.x; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
+    fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert, g, G);
+    __syncthreads();
+    const int c0 = g * kRouteChunk, c1 = min(R, c0 + kRouteChunk);
+    wave_histograms<4>(ids, c0, c1, E, nbits, cnt);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kPrologueThreads) {
+        int total = 0;
+        for (int w = 0; w < kRouteWaves; ++w) total += cnt[w * E + e];
+        chunk_counts[int64_t(g) * E + e] = total;
     }
 }
 
@@ -341,6 +405,35 @@ prologue_kernel(PrologueArgs a)
     }
 }
 
+// Long route lists: the sort is split over chunks of kRouteChunk routes.
+// Launch 1 (prologue_count_kernel): workgroups 0..G-1 count their chunk's
+// routes per expert (and fill their part of the padding), the others
+// quantize the activations.  Launch 2 (route_scatter_kernel): workgroup g
+// rebuilds the expert bases from all chunks' counts and scatters its chunk.
+__global__ void __launch_bounds__(kPrologueThreads)
+prologue_count_kernel(PrologueArgs a, int G)
+{
+    extern __shared__ int32_t lds[];
+    if (int(blockIdx.x) < G) {
+        route_count_body(a.ids, a.M * a.topk, a.E, a.bm, a.nb_cap, blockIdx.x, G, a.chunk_counts,
+                         a.sorted_route, a.sorted_w, a.block_expert, lds);
+    } else {
+        quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, blockIdx.x - G, gridDim.x - G,
+                        kPrologueThreads);
+    }
+}
+
+__global__ void __launch_bounds__(kPrologueThreads)
+route_scatter_kernel(PrologueArgs a, int G)
+{
+    extern __shared__ int32_t lds[];
+    const int g = blockIdx.x;
+    const int R = a.M * a.topk;
+    route_sort_body<4>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route, a.sorted_w,
+                       a.block_expert, a.num_valid, lds, g * kRouteChunk,
+                       min(R, (g + 1) * kRouteChunk), a.chunk_counts, G, g);
+}
+
 // Sorted-row fragment copy of the quantized activations for the tiled
 // kernels: one thread per (sorted row, K tile), 64 code bytes + one scale word.
 // Consecutive threads take consecutive rows of a 16-row slice, so each store
@@ -401,12 +494,19 @@ size_t route_lds_bytes(int E)
 
 static bool long_list(int M, int topk) { return int64_t(M) * topk > kShortList; }
 
+int route_chunks(int M, int topk)
+{
+    return long_list(M, topk) ? int((int64_t(M) * topk + kRouteChunk - 1) / kRouteChunk) : 0;
+}
+
 hipError_t route_allow_lds(int bytes)
 {
     const void* k[] = {reinterpret_cast<const void*>(&route_sort_kernel<0>),
                        reinterpret_cast<const void*>(&route_sort_kernel<4>),
                        reinterpret_cast<const void*>(&prologue_kernel<0>),
-                       reinterpret_cast<const void*>(&prologue_kernel<4>)};
+                       reinterpret_cast<const void*>(&prologue_kernel<4>),
+                       reinterpret_cast<const void*>(&prologue_count_kernel),
+                       reinterpret_cast<const void*>(&route_scatter_kernel)};
     for (const void* f : k) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (e != hipSuccess) return e;
@@ -449,8 +549,20 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint
 hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
                            const KernelEvents& ev)
 {
-    const int64_t blocks = 1 + quant_blocks(a.M, a.D, n_cu);
     const uint32_t lds = uint32_t(route_lds_bytes(a.E));
+    const int G = route_chunks(a.M, a.topk);
+    if (G > 0) {
+        if (!a.chunk_counts) return hipErrorInvalidValue;
+        const int64_t blocks = G + quant_blocks(a.M, a.D, n_cu);
+        MOE_LAUNCH(prologue_count_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds,
+                   stream, (KernelEvents{ev.start, nullptr}), a, G);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        MOE_LAUNCH(route_scatter_kernel, dim3(unsigned(G)), dim3(kPrologueThreads), lds, stream,
+                   (KernelEvents{nullptr, ev.stop}), a, G);
+        return hipGetLastError();
+    }
+    const int64_t blocks = 1 + quant_blocks(a.M, a.D, n_cu);
     if (long_list(a.M, a.topk))
         MOE_LAUNCH(prologue_kernel<4>, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds, stream,
                    ev, a);

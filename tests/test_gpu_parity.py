@@ -257,6 +257,26 @@ def test_forward_workload_sampled(binding, name, n_sample):
     assert torch.isfinite(full).all()
 
 
+@pytest.mark.parametrize("name", ["prefill", "large_prefill"])
+def test_forward_route_list_long(binding, name):
+    """Long route lists are sorted in chunks over several workgroups inside the
+    forward; the list the forward used is the oracle's, bit for bit."""
+    w = inputs.WORKLOADS[name]
+    hidden, ids, tw = inputs.make_activations(w.M, w.D, w.E, w.n_routed, w.routing, w.seed)
+    E, D, I = w.E, w.D, w.I
+    # weights only need the right shapes here (the route list does not depend on them)
+    prep = binding.moe_mxfp4_prepare_weights(
+        *[torch.zeros(s, dtype=torch.uint8, device="cuda")
+          for s in ((E, 2 * I, D // 2), (E, 2 * I, D // 32), (E, D, I // 2), (E, D, I // 32))])
+    dbg = binding.moe_mxfp4_forward_debug(hidden.cuda(), *prep, ids.cuda(), tw.cuda())
+    torch.cuda.synchronize()
+    want = oracle.route(ids.numpy(), tw.numpy(), E, dbg["block_m"])
+    n = int(want["num_valid"][0])
+    log(f"{name}: {w.M * w.topk} routes, block_m {dbg['block_m']}, {n} sorted rows")
+    np.testing.assert_array_equal(dbg["num_valid"].cpu().numpy(), want["num_valid"])
+    np.testing.assert_array_equal(dbg["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+
+
 @pytest.mark.parametrize("M,D,I,E,n_routed,seed", [
     (1, 512, 256, 9, 2, 21),          # single token (route-indexed path)
     (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
