@@ -96,7 +96,7 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, expert_block0, total;
 };
 
 Layout layout(int M, int D, int I, int E, int topk)
@@ -108,7 +108,7 @@ Layout layout(int M, int D, int I, int E, int topk)
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = 0;
+    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.expert_block0 = 0;
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
         // rows indexed by route: a2 codes and scales row-major; the expert
         // slots with their token -> route tables
@@ -130,6 +130,7 @@ Layout layout(int M, int D, int I, int E, int topk)
     L.sorted_w = take(sizeof(float) * size_t(L.cap));
     L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
     L.num_valid = take(sizeof(int32_t) * 4);
+    L.expert_block0 = take(sizeof(int32_t) * (size_t(E) + 1));
     L.a1q = take(size_t(M) * D / 2);
     L.a1s = take(size_t(M) * D / 32);
     // sorted fragment-layout copy of a1, only for the tiled kernels
@@ -237,6 +238,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
     int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
     int32_t* num_valid = reinterpret_cast<int32_t*>(ws + L.num_valid);
+    int32_t* expert_block0 = reinterpret_cast<int32_t*>(ws + L.expert_block0);
     uint8_t* a1q = ws + L.a1q;
     uint8_t* a1s = ws + L.a1s;
     uint8_t* a1f = ws + L.a1f;
@@ -251,7 +253,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
                          block_expert, num_valid, hidden, D, a1q, a1s,
-                         reinterpret_cast<int32_t*>(ws + L.chunk_counts)};
+                         reinterpret_cast<int32_t*>(ws + L.chunk_counts), expert_block0};
     const moe::KernelEvents ev0 = kernel_events(dbg, 0);
     hipError_t e = moe::launch_prologue(pa, n_cu, stream,
                                         tile ? moe::KernelEvents{ev0.start, nullptr} : ev0);
@@ -262,13 +264,13 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
                       a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap,
-                      dbg ? dbg->stage1_clock : nullptr};
+                      dbg ? dbg->stage1_clock : nullptr, expert_block0};
     const moe::KernelEvents ev1 = kernel_events(dbg, 1);
     e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      partial, M, D, I, topk, L.bm, nb, L.cap};
+                      partial, M, D, I, topk, L.bm, nb, L.cap, expert_block0};
     const moe::KernelEvents ev2 = kernel_events(dbg, 2);
     e = tile ? moe::launch_gemm2_tile(g2, stream, ev2) : moe::launch_gemm2(g2, stream, ev2);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
@@ -317,7 +319,7 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
     if (check_shape(M, D, I, E, topk) || M == 0) return 0;
     const Layout L = layout(M, D, I, E, topk);
     if (L.path == MOE_MXFP4_PATH_DIRECT) return int64_t(I / 64) * moe::direct_slots(M, E, topk);
-    if (L.path == MOE_MXFP4_PATH_TILED) return int64_t(2 * I / 256) * L.nb;
+    if (L.path == MOE_MXFP4_PATH_TILED) return moe::tile_grid(2 * I / 256, int(L.nb));
     return int64_t(I / 32) * L.nb;
 }
 

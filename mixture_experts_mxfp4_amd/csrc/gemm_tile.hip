@@ -92,6 +92,7 @@ struct TileArgs {
     const float* sorted_w;
     const int32_t* block_expert;
     const int32_t* num_valid;
+    const int32_t* expert_block0;   // [E+1] first block of each expert, then the used blocks
     int M, topk, N, K;         // N, K of one expert's weight matrix
     int64_t cap;               // rows of the sorted fragment-layout operands
     uint8_t* a2q;              // stage 1 outputs
@@ -217,16 +218,43 @@ __device__ __forceinline__ void a_sources(const TileArgs& p, int blk, StageSrc& 
     }
 }
 
+// Tile order.  The dispatcher deals workgroups to the XCDs round-robin by id
+// and each XCD has its own L2, so workgroup w runs on XCD w % 8 as that
+// XCD's (w / 8)-th.  Each XCD takes an equal contiguous share of the used
+// tiles, ordered expert by expert and, inside an expert, column tile by
+// column tile across the expert's row blocks: the workgroups resident on
+// one XCD at a time share an expert's weight tiles and activation blocks
+// in their L2 instead of every XCD fetching every block.  The grid is
+// rounded up to a multiple of 8 (tile_grid), so every share fits.
+
+// Column tile, block and expert of this workgroup; false past the used tiles.
+__device__ __forceinline__ bool tile_of(const TileArgs& p, int n_tiles, int& ntile, int& blk,
+                                        int& e)
+{
+    const int w = blockIdx.x;
+    const int xcd = w % kXcds, j = w / kXcds;
+    const int64_t used = int64_t(n_tiles) * (p.num_valid[0] / kTM);
+    const int64_t lo = used * xcd / kXcds, hi = used * (xcd + 1) / kXcds;
+    const int64_t t = lo + j;
+    if (t >= hi) return false;
+    e = p.block_expert[t / n_tiles];
+    const int first = p.expert_block0[e];
+    const int nb = p.expert_block0[e + 1] - first;
+    const int local = int(t - int64_t(n_tiles) * first);
+    ntile = local / nb;
+    blk = first + local % nb;
+    return true;
+}
+
 // ------------------------------------------------------------ stage 1 ----
 
 __global__ void __launch_bounds__(kTThreads, 1)
 gemm1_tile_kernel(TileArgs p, int I)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int ntile = blockIdx.x, blk = blockIdx.y;
     span_begin(p.clk);
-    const int e = p.block_expert[blk];     // -1 past the used blocks
-    if (e < 0) {
+    int ntile, blk, e;
+    if (!tile_of(p, p.N / kTN, ntile, blk, e)) {
         span_end(p.clk);
         return;
     }
@@ -283,9 +311,8 @@ gemm2_tile_kernel(TileArgs p)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ int32_t s_route[kTM];
     __shared__ float s_w[kTM];
-    const int ntile = blockIdx.x, blk = blockIdx.y;
-    const int e = p.block_expert[blk];     // -1 past the used blocks
-    if (e < 0) return;
+    int ntile, blk, e;
+    if (!tile_of(p, p.N / kTN, ntile, blk, e)) return;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const int R = p.M * p.topk;
@@ -336,9 +363,11 @@ hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const Kerne
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || (2 * a.I) % kTN != 0) return hipErrorInvalidValue;
+    if (!a.expert_block0) return hipErrorInvalidValue;
     TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.block_expert,
-               a.num_valid, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s, a.h_dbg, nullptr, a.clk};
-    MOE_LAUNCH(gemm1_tile_kernel, dim3(2 * a.I / kTN, a.nb_cap), dim3(kTThreads),
+               a.num_valid, a.expert_block0, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s,
+               a.h_dbg, nullptr, a.clk};
+    MOE_LAUNCH(gemm1_tile_kernel, dim3(tile_grid(2 * a.I / kTN, a.nb_cap)), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
     return hipGetLastError();
 }
@@ -347,10 +376,11 @@ hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const Kerne
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || a.D % kTN != 0) return hipErrorInvalidValue;
+    if (!a.expert_block0) return hipErrorInvalidValue;
     TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.block_expert,
-               a.num_valid, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr, nullptr, a.partial,
-               nullptr};
-    MOE_LAUNCH(gemm2_tile_kernel, dim3(a.D / kTN, a.nb_cap), dim3(kTThreads),
+               a.num_valid, a.expert_block0, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr,
+               nullptr, a.partial, nullptr};
+    MOE_LAUNCH(gemm2_tile_kernel, dim3(tile_grid(a.D / kTN, a.nb_cap)), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p);
     return hipGetLastError();
 }

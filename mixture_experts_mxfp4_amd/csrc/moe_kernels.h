@@ -47,6 +47,7 @@ struct PrologueArgs {
     int D;
     uint8_t *a1q, *a1s;
     int32_t* chunk_counts;         // [route_chunks][E] for long lists (else unused)
+    int32_t* expert_block0;        // [E+1]: first block of each expert, then the used blocks
 };
 // Chunks of the two-launch route sort for this many routes (0: one workgroup).
 int route_chunks(int M, int topk);
@@ -78,6 +79,7 @@ struct Gemm1Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
     uint64_t* clk = nullptr;       // optional kernel span (span_begin / span_end)
+    const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
@@ -90,10 +92,17 @@ struct Gemm2Args {
     uint16_t* partial;          // bf16 [M*topk][D], weighted contribution per route
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
+    const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
-// LDS-tiled variants for block_m = 256.
+// LDS-tiled variants for block_m = 256.  Their grids are one-dimensional:
+// n_tiles column tiles x nb_cap blocks, rounded up to whole rounds of the 8 XCDs.
+constexpr int kXcds = 8;
+inline unsigned tile_grid(int n_tiles, int nb_cap)
+{
+    return unsigned((int64_t(n_tiles) * nb_cap + kXcds - 1) / kXcds * kXcds);
+}
 hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
 hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});

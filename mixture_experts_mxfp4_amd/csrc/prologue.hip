@@ -106,14 +106,16 @@ __device__ __forceinline__ void wave_histograms(const int32_t* __restrict__ ids,
 // [G][E], from the counting launch) the expert segments' bases come from the
 // totals of every chunk and this chunk's routes go after those of chunks
 // 0..g-1; without, the chunk is the whole list.  Chunk 0 (or the only one)
-// writes block_expert and num_valid.  The order inside an expert's segment
+// writes block_expert, num_valid and, when given, expert_block0 (each
+// expert's first block, then the number of used blocks).  The order inside an expert's segment
 // is ascending route: chunk, then wave, then lane order.
 template <int U>
 __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
                                 int M, int topk, int E, int bm, int nb_cap,
                                 int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
                                 int32_t* __restrict__ block_expert,
-                                int32_t* __restrict__ num_valid, int32_t* lds,
+                                int32_t* __restrict__ num_valid,
+                                int32_t* __restrict__ expert_block0, int32_t* lds,
                                 int c0 = 0, int c1 = -1,
                                 const int32_t* __restrict__ chunk_counts = nullptr, int G = 1,
                                 int g = 0)
@@ -179,9 +181,11 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
                 cnt[w * E + e] = run;
                 run += c;
             }
-            if (g == 0)
+            if (g == 0) {
 #pragma unroll 1
                 for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
+                if (expert_block0) expert_block0[e] = base_e / bm;
+            }
         }
         carry += all;
         valid_total += vall;
@@ -190,6 +194,7 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     if (tid == 0 && g == 0) {
         num_valid[0] = carry;
         num_valid[1] = valid_total;
+        if (expert_block0) expert_block0[E] = carry / bm;
     }
 
     // pass 2: stable scatter (each wave only touches its own histogram row)
@@ -255,7 +260,8 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
                                 int M, int topk, int E, int bm, int nb_cap,
                                 int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
                                 int32_t* __restrict__ block_expert,
-                                int32_t* __restrict__ num_valid, int32_t* lds)
+                                int32_t* __restrict__ num_valid,
+                                int32_t* __restrict__ expert_block0, int32_t* lds)
 {
     int32_t* ids = lds;                                          // [R]
     float* tw = reinterpret_cast<float*>(lds + kShortList);      // [R]
@@ -299,6 +305,7 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
             cnt[e] = base_e;
 #pragma unroll 1
             for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
+            if (expert_block0) expert_block0[e] = base_e / bm;
         }
         carry += __builtin_amdgcn_readlane(inc, kWave - 1);
         vcarry += __builtin_amdgcn_readlane(vinc, kWave - 1);
@@ -307,6 +314,7 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
     if (lane == 0) {
         num_valid[0] = carry;
         num_valid[1] = vcarry;
+        if (expert_block0) expert_block0[E] = carry / bm;
     }
     // pass 2: stable scatter
 #pragma unroll 1
@@ -372,10 +380,10 @@ route_sort_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw,
     extern __shared__ int32_t lds[];
     if constexpr (U == 0) {
         route_sort_wave(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w, block_expert,
-                        num_valid, lds);
+                        num_valid, nullptr, lds);
     } else {
         route_sort_body<U>(ids, tw, M, topk, E, bm, nb_cap, sorted_route, sorted_w,
-                           block_expert, num_valid, lds);
+                           block_expert, num_valid, nullptr, lds);
     }
 }
 
@@ -394,10 +402,10 @@ prologue_kernel(PrologueArgs a)
     if (blockIdx.x == 0) {
         if constexpr (U == 0) {
             route_sort_wave(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
-                            a.sorted_w, a.block_expert, a.num_valid, lds);
+                            a.sorted_w, a.block_expert, a.num_valid, a.expert_block0, lds);
         } else {
             route_sort_body<U>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route,
-                               a.sorted_w, a.block_expert, a.num_valid, lds);
+                               a.sorted_w, a.block_expert, a.num_valid, a.expert_block0, lds);
         }
     } else {
         quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, blockIdx.x - 1, gridDim.x - 1,
@@ -430,7 +438,7 @@ route_scatter_kernel(PrologueArgs a, int G)
     const int g = blockIdx.x;
     const int R = a.M * a.topk;
     route_sort_body<4>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route, a.sorted_w,
-                       a.block_expert, a.num_valid, lds, g * kRouteChunk,
+                       a.block_expert, a.num_valid, a.expert_block0, lds, g * kRouteChunk,
                        min(R, (g + 1) * kRouteChunk), a.chunk_counts, G, g);
 }
 
