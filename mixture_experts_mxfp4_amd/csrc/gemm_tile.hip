@@ -10,9 +10,11 @@
 //                   per lane);
 //   K pipeline      K advances 128 elements per stage; 4 stages live in LDS
 //                   (34 KiB each: A and B codes, A and B scales) and are filled
-//                   by direct global->LDS loads (global_load_lds), so three
-//                   stages are in flight while one is consumed, without
-//                   staging registers;
+//                   by direct global->LDS loads (global_load_lds) issued three
+//                   stages ahead, without staging registers;
+//   schedule        each stage's loads, LDS fragment reads and barrier sit
+//                   between its MFMAs in a fixed order (tile_step), so the
+//                   matrix cores are never left waiting on them;
 //   LDS layout      codes as [16-row slice][32-element chunk][row%16][16 B]:
 //                   a quarter-wave reads 256 contiguous bytes per fragment (no
 //                   bank conflicts), and the prepared weight fragments already
@@ -28,15 +30,18 @@ namespace moe {
 constexpr int kTThreads = 512;
 constexpr int kTM = 256;                 // rows per tile (= block_m of this path)
 constexpr int kTN = 256;                 // columns per tile
-#ifndef MOE_TILE_STAGES
-#define MOE_TILE_STAGES 4
-#endif
-constexpr int kStages = MOE_TILE_STAGES;
+constexpr int kStages = 4;
 constexpr int kOffB = kTM * 64;          // A codes 16 KiB, then B codes 16 KiB
 constexpr int kOffAS = kOffB + kTN * 64; // A scales: [row][4 B]
 constexpr int kOffBS = kOffAS + kTM * 4; // B scales: [n64 group][lane][4 slices]
 constexpr int kStageBytes = kOffBS + kTN * 4;
 constexpr int kLoadsPerStage = 5;        // global_load_lds per wave per stage
+// Epilogue staging in the (then idle) ring: rows padded by 16 B so that
+// consecutive rows start 4 banks apart.
+constexpr int kHStride = 128 * 2 + 16;   // stage 1: 128 bf16 h columns per row
+constexpr int kPStride = kTN * 2 + 16;   // stage 2: 256 bf16 output columns per row
+static_assert(kTM * kPStride <= kStages * kStageBytes && kTM * kHStride <= kStages * kStageBytes,
+              "epilogue staging must fit in the ring");
 
 size_t tile_lds_bytes() { return size_t(kStages) * kStageBytes; }
 
@@ -71,13 +76,14 @@ __device__ __forceinline__ void wait_barrier()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ v16f mfma_fp4_32x32x64(uint4 a, uint4 b, v16f c, uint32_t sa,
-                                                   uint32_t sb)
+// Block-scaled FP4 MFMA whose scale bytes are picked from 32-bit words by the
+// instruction's byte selects (SA, SB: byte 0..3 of sa, sb).
+template <int SA, int SB>
+__device__ __forceinline__ v16f mfma_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb)
 {
     v8i A = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
     v8i B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, int(sa), 0,
-                                                            int(sb));
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, SA, int(sa), SB, int(sb));
 }
 
 // Byte offset of (row, 32-element chunk c) in a [slice][chunk][row%16][16 B] tile.
@@ -111,67 +117,149 @@ struct StageSrc {
     int64_t scale_step;        // bytes per K tile of `scale`
 };
 
-// buf: LDS address of the stage buffer; wave: wave-uniform wave index.
-__device__ __forceinline__ void issue_stage(const StageSrc& s, int kt, uint32_t buf, int wave)
+// Load d (0-4) of this wave for K tile kt into the stage buffer at LDS address
+// `buf`; wave: wave-uniform wave index.
+__device__ __forceinline__ void issue_load(const StageSrc& s, int kt, int d, uint32_t buf, int wave)
 {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) dma16(s.a_code[h] + int64_t(kt) * 1024, buf + (2 * wave + h) * 1024);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) dma16(s.b_code[h] + int64_t(kt) * 4096, buf + kOffB + (2 * wave + h) * 1024);
-    if (wave < 4) dma4(s.scale + kt * s.scale_step, buf + kOffAS + wave * 256);
+    if (d < 2) dma16(s.a_code[d] + int64_t(kt) * 1024, buf + (2 * wave + d) * 1024);
+    else if (d < 4) dma16(s.b_code[d - 2] + int64_t(kt) * 4096, buf + kOffB + (2 * wave + d - 2) * 1024);
+    else if (wave < 4) dma4(s.scale + kt * s.scale_step, buf + kOffAS + wave * 256);
     else dma4(s.scale + kt * s.scale_step, buf + kOffBS + (wave - 4) * 256);
 }
 
+// MFMA operands of one 64-deep K half for a wave's 64 x 128 tile.
+struct HalfFrags {
+    uint4 a[2], b[4];
+};
+
+// Fragment i (0-1: A tile i, 2-5: B tile i-2) of K half jj from stage buffer buf.
+__device__ __forceinline__ void read_frag(const uint8_t* buf, int jj, int wave_m, int wave_n, int lane,
+                                          HalfFrags& f, int i)
+{
+    const int c = 2 * jj + (lane >> 5);
+    if (i < 2) f.a[i] = *reinterpret_cast<const uint4*>(buf + tile_off(wave_m * 64 + i * 32 + (lane & 31), c));
+    else f.b[i - 2] = *reinterpret_cast<const uint4*>(buf + kOffB + tile_off(wave_n * 128 + (i - 2) * 32 + (lane & 31), c));
+}
+
+// Scale words.  A: the four chunk scales of row wave_m*64 + mt*32 + lane%32 (byte c
+// = chunk).  B: the prepared word of group wave_n*2 + g for chunk 2jj + lane/32 and
+// row lane%16, which holds the scales of the group's four 16-row slices; MFMA tile nt
+// of this lane uses slice 2(nt%2) + (lane/16)%2 of group wave_n*2 + nt/2.
+__device__ __forceinline__ uint32_t read_sa(const uint8_t* buf, int wave_m, int lane, int mt)
+{
+    return *reinterpret_cast<const uint32_t*>(buf + kOffAS + (wave_m * 64 + mt * 32 + (lane & 31)) * 4);
+}
+__device__ __forceinline__ uint32_t read_sb(const uint8_t* buf, int wave_n, int lane, int jj, int g)
+{
+    const int c = 2 * jj + (lane >> 5);
+    return *reinterpret_cast<const uint32_t*>(buf + kOffBS + (wave_n * 2 + g) * 256 + (c * 16 + (lane & 15)) * 4);
+}
+
 // acc[mt][nt] += A[256 x K] . W[e][tile columns]^T over the whole K.
+//
+// One K tile (stage) per step, in two halves of eight MFMAs.  The instruction
+// stream of a step is fixed (sched_barrier fences): between the MFMAs of half 0
+// the wave issues its five loads of stage kt+3 (whose ring slot was last read
+// before the previous step's barrier) and reads half 1's fragments; then it
+// waits for its loads of stage kt+1 and joins the barrier; between the MFMAs of
+// half 1 it reads half 0 of stage kt+1.  So the matrix cores always have the
+// next MFMA queued while loads, LDS reads and the barrier are in flight.  The
+// scale words are shifted once per stage to this lane's byte pair and the MFMA
+// byte selects pick chunk and slice.
+template <bool kLoad>
+__device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, uint8_t* lds,
+                                          uint32_t lds0, int wave, int lane, v16f acc[2][4],
+                                          HalfFrags& f0, HalfFrags& f1, uint32_t sa[2],
+                                          uint32_t sb0[2])
+{
+    const int wave_m = wave >> 1, wave_n = wave & 1;
+    const uint8_t* cur = lds + (kt % kStages) * kStageBytes;
+    const uint8_t* nxt = lds + ((kt + 1) % kStages) * kStageBytes;
+    const uint32_t load_buf = lds0 + ((kt + kStages - 1) % kStages) * kStageBytes;
+    uint32_t sb1[2], sa_next[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) sa[m] >>= 8 * (lane >> 5);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sb0[g] >>= 8 * ((lane >> 4) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int mt = i >> 2, nt = i & 3;
+        acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<0, 2>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1])
+                               : mfma_fp4_sel<0, 0>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1]);
+        if (kLoad && i < kLoadsPerStage) issue_load(src, kt + kStages - 1, i, load_buf, wave);
+        if (i >= 1 && i < 7) read_frag(cur, 1, wave_m, wave_n, lane, f1, i - 1);
+        if (i == 7) {
+            sb1[0] = read_sb(cur, wave_n, lane, 1, 0);
+            sb1[1] = read_sb(cur, wave_n, lane, 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // this wave's LDS reads are done, and its loads of stage kt+1 have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (kLoad) {
+        wait_barrier<2 * kLoadsPerStage>();          // stages kt+2, kt+3 may be in flight
+    } else if (kt + 2 < KT) {
+        wait_barrier<kLoadsPerStage>();              // stage kt+2 may be in flight
+    } else {
+        wait_barrier<0>();
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sb1[g] >>= 8 * ((lane >> 4) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int mt = i >> 2, nt = i & 3;
+        acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
+                               : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
+        // (after the last stage these read a ring slot whose contents go unused)
+        if (i < 6) read_frag(nxt, 0, wave_m, wave_n, lane, f0, i);
+        if (i == 6) {
+            sa_next[0] = read_sa(nxt, wave_m, lane, 0);
+            sa_next[1] = read_sa(nxt, wave_m, lane, 1);
+        }
+        if (i == 7) {
+            sb0[0] = read_sb(nxt, wave_n, lane, 0, 0);
+            sb0[1] = read_sb(nxt, wave_n, lane, 0, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    sa[0] = sa_next[0];
+    sa[1] = sa_next[1];
+}
+
 __device__ __forceinline__ void tile_mainloop(const StageSrc& src, int KT, uint8_t* lds,
                                               v16f acc[2][4])
 {
+    static_assert(kStages == 4, "the waits below assume three stages in flight");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < KT) issue_stage(src, s, lds0 + s * kStageBytes, wave);
+    const int pre = min(KT, kStages - 1);
+    for (int s = 0; s < pre; ++s)
+        for (int d = 0; d < kLoadsPerStage; ++d) issue_load(src, s, d, lds0 + s * kStageBytes, wave);
+    // stage 0 has landed once at most pre - 1 later stages are pending
+    if (pre == 3) wait_barrier<2 * kLoadsPerStage>();
+    else if (pre == 2) wait_barrier<kLoadsPerStage>();
+    else wait_barrier<0>();
 
-    for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed once at most `ahead` later stages are pending
-        const int ahead = min(KT - 1 - kt, kStages - 2);
-        if (ahead >= 3) wait_barrier<3 * kLoadsPerStage>();
-        else if (ahead == 2) wait_barrier<2 * kLoadsPerStage>();
-        else if (ahead == 1) wait_barrier<kLoadsPerStage>();
-        else wait_barrier<0>();
-        if (kt + kStages - 1 < KT)
-            issue_stage(src, kt + kStages - 1, lds0 + ((kt + kStages - 1) % kStages) * kStageBytes, wave);
+    HalfFrags f0, f1;
+    uint32_t sa[2], sb0[2];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) read_frag(lds, 0, wave_m, wave_n, lane, f0, i);
+    sa[0] = read_sa(lds, wave_m, lane, 0);
+    sa[1] = read_sa(lds, wave_m, lane, 1);
+    sb0[0] = read_sb(lds, wave_n, lane, 0, 0);
+    sb0[1] = read_sb(lds, wave_n, lane, 0, 1);
 
-        const uint8_t* buf = lds + (kt % kStages) * kStageBytes;
-        uint32_t sa_word[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            sa_word[mt] = *reinterpret_cast<const uint32_t*>(buf + kOffAS + (wave_m * 64 + mt * 32 + (lane & 31)) * 4);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = 2 * jj + (lane >> 5);
-            uint4 af[2], bf[4];
-            uint32_t sb[4];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                af[mt] = *reinterpret_cast<const uint4*>(buf + tile_off(wave_m * 64 + mt * 32 + (lane & 31), c));
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int prow = wave_n * 128 + nt * 32 + (lane & 31);
-                bf[nt] = *reinterpret_cast<const uint4*>(buf + kOffB + tile_off(prow, c));
-                sb[nt] = buf[kOffBS + (prow >> 6) * 256 + (c * 16 + (prow & 15)) * 4 + ((prow >> 4) & 3)];
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint32_t sa = (sa_word[mt] >> (8 * c)) & 0xFFu;
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = mfma_fp4_32x32x64(af[mt], bf[nt], acc[mt][nt], sa, sb[nt]);
-            }
-        }
-    }
+    int kt = 0;
+#pragma unroll 1
+    for (; kt + kStages - 1 < KT; ++kt)
+        tile_step<true>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
+#pragma unroll 1
+    for (; kt < KT; ++kt)
+        tile_step<false>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
 }
 
 __device__ __forceinline__ void zero_acc(v16f acc[2][4])
@@ -270,35 +358,59 @@ gemm1_tile_kernel(TileArgs p, int I)
     zero_acc(acc);
     tile_mainloop(src, p.K / 128, lds, acc);
 
-    // Epilogue: the wave's N tiles are (gate, up) of h groups hg0 and hg0 + 1
-    // (prepared 64-row group = 32 gate rows then 32 up rows).
-    const int hg0 = ntile * 4 + wave_n * 2;
+    // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
+    // wave_n*2 + 1 of the tile (prepared 64-row group = 32 gate rows then 32 up
+    // rows); the tile's 128 h columns are K tile `ntile` of stage 2.  h goes
+    // through LDS (the ring is free once every wave is past the main loop) so
+    // that each thread then holds two whole MXFP4 blocks of one row: thread t
+    // quantizes row t/2, chunks 2(t%2) and 2(t%2)+1, and stores 32 code bytes
+    // and two scale bytes.
+    uint8_t* hs = lds;                                   // [256 rows][kHStride]
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int hg = hg0 + gi;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = wave_m * 64 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                const int64_t srow = int64_t(blk) * kTM + row;
+                const int col = (wave_n * 2 + gi) * 32 + (lane & 31);
                 const uint32_t h = f32_to_bf16_rne(silu_fast(acc[mt][2 * gi][i]) * acc[mt][2 * gi + 1][i]);
-                if (p.h_dbg) p.h_dbg[srow * I + hg * 32 + (lane & 31)] = uint16_t(h);
-                // MXFP4 group: the 32 columns of this row held by one half-wave
-                // (DPP rows 0-1 or 2-3); the two row maxima meet via readlane
-                const uint32_t rmax = row16_max(h & 0x7FFFu);
-                const uint32_t m01 = max(uint32_t(__builtin_amdgcn_readlane(int(rmax), 0)),
-                                         uint32_t(__builtin_amdgcn_readlane(int(rmax), 16)));
-                const uint32_t m23 = max(uint32_t(__builtin_amdgcn_readlane(int(rmax), 32)),
-                                         uint32_t(__builtin_amdgcn_readlane(int(rmax), 48)));
-                const uint32_t s = mx_scale_from_amax(lane < 32 ? m01 : m23);
-                const uint32_t p4 = pack8_codes(mx_code(h, s));
-                if ((lane & 7) == 0)
-                    *reinterpret_cast<uint32_t*>(p.a2q + frag_code_off(srow, hg / 4, hg % 4, I / 128) +
-                                                 ((lane & 31) >> 3) * 4) = p4;
-                if ((lane & 31) == 0) p.a2s[frag_scale_off(srow, hg / 4, p.cap) + hg % 4] = uint8_t(s);
+                *reinterpret_cast<uint16_t*>(hs + row * kHStride + col * 2) = uint16_t(h);
             }
         }
+    }
+    __syncthreads();
+    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int64_t srow = int64_t(blk) * kTM + row;
+    const uint4* hrow = reinterpret_cast<const uint4*>(hs + row * kHStride + half * 128);
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = hrow[j];
+    uint32_t sc = 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 4 * b; j < 4 * b + 4; ++j) {
+            const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) amax = max(amax, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
+        }
+        const uint32_t s = mx_scale_from_amax(amax);
+        uint4 codes;
+        codes.x = mx_pack8(v[4 * b].x, v[4 * b].y, v[4 * b].z, v[4 * b].w, s);
+        codes.y = mx_pack8(v[4 * b + 1].x, v[4 * b + 1].y, v[4 * b + 1].z, v[4 * b + 1].w, s);
+        codes.z = mx_pack8(v[4 * b + 2].x, v[4 * b + 2].y, v[4 * b + 2].z, v[4 * b + 2].w, s);
+        codes.w = mx_pack8(v[4 * b + 3].x, v[4 * b + 3].y, v[4 * b + 3].z, v[4 * b + 3].w, s);
+        *reinterpret_cast<uint4*>(p.a2q + frag_code_off(srow, ntile, 2 * half + b, I / 128)) = codes;
+        sc |= s << (8 * b);
+    }
+    *reinterpret_cast<uint16_t*>(p.a2s + frag_scale_off(srow, ntile, p.cap) + 2 * half) = uint16_t(sc);
+    if (p.h_dbg) {
+        uint4* dst = reinterpret_cast<uint4*>(p.h_dbg + srow * I + ntile * 128 + half * 64);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[j] = v[j];
     }
     span_end(p.clk);
 }
@@ -330,22 +442,33 @@ gemm2_tile_kernel(TileArgs p)
     zero_acc(acc);
     tile_mainloop(src, p.K / 128, lds, acc);
 
+    // Epilogue: the routing weight times the sum, rounded to bf16, goes through
+    // LDS as the 256 x 256 tile; then each half-wave stores one row's 512
+    // contiguous bytes into its route's partial row (padding rows are skipped).
+    uint8_t* ps = lds;                                   // [256 rows][kPStride]
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = wave_m * 64 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            const int sr = s_route[row];
             const float w = s_w[row];
-            uint16_t* dst = p.partial + int64_t(sr) * D + ntile * kTN + wave_n * 128 + (lane & 31);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                // columns lane%32 and lane%32 + 1 as one dword from the even lane
-                const uint32_t v = f32_to_bf16_rne(w * acc[mt][nt][i]);
-                const uint32_t pair = v | (dpp<kDppXor1>(v) << 16);
-                if (sr < R && (lane & 1) == 0) *reinterpret_cast<uint32_t*>(dst + nt * 32) = pair;
+                const int col = wave_n * 128 + nt * 32 + (lane & 31);
+                *reinterpret_cast<uint16_t*>(ps + row * kPStride + col * 2) =
+                    uint16_t(f32_to_bf16_rne(w * acc[mt][nt][i]));
             }
         }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < kTM / 16; ++k) {
+        const int row = wave * (kTM / 8) + 2 * k + (lane >> 5);
+        const int sr = s_route[row];
+        const uint4 v = *reinterpret_cast<const uint4*>(ps + row * kPStride + (lane & 31) * 16);
+        if (sr < R)
+            *reinterpret_cast<uint4*>(p.partial + int64_t(sr) * D + ntile * kTN + (lane & 31) * 8) = v;
     }
 }
 
