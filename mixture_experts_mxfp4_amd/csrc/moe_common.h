@@ -19,12 +19,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
-// float -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+// float -> bf16 bits, round to nearest even (the gfx950 conversion
+// v_cvt_pk_bf16_f32; a NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // ------------------------------------------------------ MXFP4 quantizer ---
@@ -136,7 +135,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
     return x;
 }
 
-__device__ __forceinline__ float silu_fast(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) on the hardware exp2 and reciprocal (about 1 ulp
+// each; the result is rounded to bf16 right after).  Very negative g gives
+// e^-g = inf and a zero reciprocal (silu -> -0); very positive g gives g.
+__device__ __forceinline__ float silu_fast(float g)
+{
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // ------------------------------------------------------ kernel span -----
 //
