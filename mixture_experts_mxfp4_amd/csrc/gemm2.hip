@@ -274,11 +274,12 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEven
 }
 
 // out[t, :] = bf16( sum_{s < topk, 0 <= ids[t,s] < E} partial[t*topk + s, :] ),
-// fp32 sum in slot order.  A thread owns VEC columns of one token; the slots
-// are taken eight at a time with all eight loads issued before the adds, so a
-// token costs two memory round trips (ids, then partial rows) per eight slots
-// instead of one per slot.
-template <int VEC>
+// fp32 sum in slot order.  A thread owns VEC columns of one token and issues
+// the loads of all of the token's slot ids and partial rows at once (KMAX >=
+// topk slots; a slot whose id is out of range was never written by stage 2:
+// its row is loaded but not added), so a token costs one memory round trip.
+// Partial rows are read once: non-temporal loads.
+template <int VEC, int KMAX>
 __global__ void __launch_bounds__(256)
 reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restrict__ ids, int M,
                     int D, int E, int topk, uint16_t* __restrict__ out)
@@ -290,32 +291,27 @@ reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restr
          i += int64_t(gridDim.x) * blockDim.x) {
         const int64_t t = i / per_row;
         const int64_t col = (i % per_row) * VEC;
-        float acc[VEC];
+        int e[KMAX];
+        uint32_t v[KMAX][W];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
-#pragma unroll 1
-        for (int s0 = 0; s0 < topk; s0 += 8) {
-            bool use[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s = s0 + u;
-                const int e = s < topk ? ids[t * topk + s] : -1;
-                use[u] = e >= 0 && e < E;
-            }
-            uint32_t v[8][W];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint16_t* src = partial + (t * topk + s0 + u) * D + col;
+        for (int u = 0; u < KMAX; ++u) {
+            if (u < topk) {
+                e[u] = ids[t * topk + u];
+                const uint16_t* src = partial + (t * topk + u) * D + col;
                 if constexpr (W == 1) {
-                    v[u][0] = use[u] ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+                    v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
                 } else {
-                    const uint4 x = use[u] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+                    const uint4 x = ld16_nt(reinterpret_cast<const uint8_t*>(src));
                     v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
                 }
             }
+        }
+        float acc[VEC];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (!use[u]) continue;
+        for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < KMAX; ++u) {
+            if (u < topk && e[u] >= 0 && e[u] < E) {
 #pragma unroll
                 for (int j = 0; j < W; ++j) {
                     acc[2 * j] += bf16_to_f32(v[u][j] & 0xFFFFu);
@@ -334,6 +330,22 @@ reduce_slots_kernel(const uint16_t* __restrict__ partial, const int32_t* __restr
     }
 }
 
+template <int VEC>
+static void launch_reduce_vec(dim3 grid, hipStream_t stream, const KernelEvents& ev,
+                              const uint16_t* partial, const int32_t* ids, int M, int D, int E,
+                              int topk, uint16_t* out)
+{
+    if (topk <= 8)
+        MOE_LAUNCH((reduce_slots_kernel<VEC, 8>), grid, dim3(256), 0, stream, ev, partial, ids, M,
+                   D, E, topk, out);
+    else if (topk <= 16)
+        MOE_LAUNCH((reduce_slots_kernel<VEC, 16>), grid, dim3(256), 0, stream, ev, partial, ids, M,
+                   D, E, topk, out);
+    else
+        MOE_LAUNCH((reduce_slots_kernel<VEC, 32>), grid, dim3(256), 0, stream, ev, partial, ids, M,
+                   D, E, topk, out);
+}
+
 // Few tokens: two columns per thread (enough threads to cover the latency);
 // many tokens: eight columns per thread (16-byte accesses).
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
@@ -341,16 +353,14 @@ hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int 
                                const KernelEvents& ev)
 {
     if (int64_t(M) * D == 0) return hipSuccess;
+    if (topk < 1 || topk > 32) return hipErrorInvalidValue;
     const bool narrow = int64_t(M) * (D / 2) <= int64_t(n_cu) * 1024;
     const int64_t nv = int64_t(M) * (D / (narrow ? 2 : 8));
     int64_t blocks = (nv + 255) / 256;
     if (blocks > int64_t(n_cu) * 16) blocks = int64_t(n_cu) * 16;
-    if (narrow)
-        MOE_LAUNCH(reduce_slots_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, stream, ev,
-                   partial, ids, M, D, E, topk, out);
-    else
-        MOE_LAUNCH(reduce_slots_kernel<8>, dim3(unsigned(blocks)), dim3(256), 0, stream, ev,
-                   partial, ids, M, D, E, topk, out);
+    const dim3 grid{unsigned(blocks)};
+    if (narrow) launch_reduce_vec<2>(grid, stream, ev, partial, ids, M, D, E, topk, out);
+    else launch_reduce_vec<8>(grid, stream, ev, partial, ids, M, D, E, topk, out);
     return hipGetLastError();
 }
 

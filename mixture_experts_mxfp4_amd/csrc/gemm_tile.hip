@@ -262,6 +262,44 @@ __device__ __forceinline__ void tile_mainloop(const StageSrc& src, int KT, uint8
         tile_step<false>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
 }
 
+// Main loop of a wave whose 64 rows are all padding (an expert's routes come
+// first in its segment, so a block's padding rows are its last ones).  It
+// still issues its share of the B-tile and scale loads (its A slices are
+// rows of its own padding group) and joins every barrier, but reads no
+// fragments and issues no MFMAs, leaving its SIMD's matrix core to the
+// other wave there.  Its sums stay zero.
+constexpr int kIdleLoads = kLoadsPerStage - 2;     // loads 2..4 of issue_load
+__device__ __forceinline__ void tile_mainloop_idle(const StageSrc& src, int KT, uint8_t* lds)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+    const int pre = min(KT, kStages - 1);
+    for (int s = 0; s < pre; ++s)
+        for (int d = 2; d < kLoadsPerStage; ++d) issue_load(src, s, d, lds0 + s * kStageBytes, wave);
+    if (pre == 3) wait_barrier<2 * kIdleLoads>();
+    else if (pre == 2) wait_barrier<kIdleLoads>();
+    else wait_barrier<0>();
+#pragma unroll 1
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + kStages - 1 < KT) {
+            const uint32_t buf = lds0 + ((kt + kStages - 1) % kStages) * kStageBytes;
+            for (int d = 2; d < kLoadsPerStage; ++d) issue_load(src, kt + kStages - 1, d, buf, wave);
+            wait_barrier<2 * kIdleLoads>();
+        } else if (kt + 2 < KT) {
+            wait_barrier<kIdleLoads>();
+        } else {
+            wait_barrier<0>();
+        }
+    }
+}
+
+// Whether this wave's 64 rows of block blk hold any route (wave-uniform).
+__device__ __forceinline__ bool rows_in_use(const TileArgs& p, int blk, int wave_m)
+{
+    const int sr = __builtin_amdgcn_readfirstlane(p.sorted_route[int64_t(blk) * kTM + wave_m * 64]);
+    return sr < p.M * p.topk;
+}
+
 __device__ __forceinline__ void zero_acc(v16f acc[2][4])
 {
 #pragma unroll
@@ -356,7 +394,8 @@ gemm1_tile_kernel(TileArgs p, int I)
 
     v16f acc[2][4];
     zero_acc(acc);
-    tile_mainloop(src, p.K / 128, lds, acc);
+    if (rows_in_use(p, blk, wave_m)) tile_mainloop(src, p.K / 128, lds, acc);
+    else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
     // wave_n*2 + 1 of the tile (prepared 64-row group = 32 gate rows then 32 up
@@ -440,7 +479,8 @@ gemm2_tile_kernel(TileArgs p)
 
     v16f acc[2][4];
     zero_acc(acc);
-    tile_mainloop(src, p.K / 128, lds, acc);
+    if (rows_in_use(p, blk, wave_m)) tile_mainloop(src, p.K / 128, lds, acc);
+    else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue: the routing weight times the sum, rounded to bf16, goes through
     // LDS as the 256 x 256 tile; then each half-wave stores one row's 512
