@@ -47,6 +47,9 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
 {
     constexpr int BM = 16 * RT;
     constexpr int U = g2_unroll<RT>();
+    constexpr int kRow = 256 * 2 + 16;       // staged output row: 256 bf16 + 16 B bank stagger
+    __shared__ __attribute__((aligned(16))) uint8_t stage[BM * kRow];
+    __shared__ int32_t s_route[BM];
     const int blk = blockIdx.y;
     const int e = block_expert[blk];       // -1 past the used blocks
     if (e < 0) return;
@@ -103,22 +106,33 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
     for (; kt + U <= KT; kt += U) steps(std::integral_constant<int, U>{}, kt);
     for (; kt < KT; ++kt) steps(std::integral_constant<int, 1>{}, kt);
 
+    // Epilogue: the routing weight times the sum, rounded to bf16, goes through
+    // LDS as the block's BM x 256 tile; then each half-wave stores one row's
+    // 512 contiguous bytes of its route's partial row (padding rows skipped).
+    if (threadIdx.x < BM) s_route[threadIdx.x] = sorted_route[int64_t(blk) * BM + threadIdx.x];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t srow = int64_t(blk) * BM + rt * 16 + 4 * (lane / 16) + i;
-            const int sr = sorted_route[srow];
-            const float w = sorted_w[srow];
-            uint16_t* dst = partial + int64_t(sr) * D + n64 * 64 + lane % 16;
+            const int row = rt * 16 + 4 * (lane / 16) + i;
+            const float w = sorted_w[int64_t(blk) * BM + row];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                // columns lane%16 and lane%16 + 1 as one dword from the even lane
-                const uint32_t v = f32_to_bf16_rne(w * acc[rt][q][i]);
-                const uint32_t pair = v | (dpp<kDppXor1>(v) << 16);
-                if (sr < R && (lane & 1) == 0) *reinterpret_cast<uint32_t*>(dst + q * 16) = pair;
+                const int col = wave * 64 + q * 16 + lane % 16;
+                *reinterpret_cast<uint16_t*>(stage + row * kRow + col * 2) =
+                    uint16_t(f32_to_bf16_rne(w * acc[rt][q][i]));
             }
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BM / 8; ++k) {
+        const int c = k * kGemmThreads + threadIdx.x;   // 16-byte chunk: row c/32, chunk c%32
+        const int row = c >> 5, ch = c & 31;
+        const int sr = s_route[row];
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kRow + ch * 16);
+        if (sr < R)
+            *reinterpret_cast<uint4*>(partial + int64_t(sr) * D + blockIdx.x * 256 + ch * 8) = v;
     }
 }
 
