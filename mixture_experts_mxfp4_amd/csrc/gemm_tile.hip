@@ -115,6 +115,7 @@ struct StageSrc {
     const uint8_t* b_code[2];  // this lane's 16 B of B pieces 2w, 2w+1 at kt = 0
     const uint8_t* scale;      // waves 0-3: A scale word of row 64w+lane; 4-7: B scale word
     int64_t scale_step;        // bytes per K tile of `scale`
+    uint32_t scale_lds;        // byte offset of this wave's scale words in a stage buffer
 };
 
 // Load d (0-4) of this wave for K tile kt into the stage buffer at LDS address
@@ -123,8 +124,7 @@ __device__ __forceinline__ void issue_load(const StageSrc& s, int kt, int d, uin
 {
     if (d < 2) dma16(s.a_code[d] + int64_t(kt) * 1024, buf + (2 * wave + d) * 1024);
     else if (d < 4) dma16(s.b_code[d - 2] + int64_t(kt) * 4096, buf + kOffB + (2 * wave + d - 2) * 1024);
-    else if (wave < 4) dma4(s.scale + kt * s.scale_step, buf + kOffAS + wave * 256);
-    else dma4(s.scale + kt * s.scale_step, buf + kOffBS + (wave - 4) * 256);
+    else dma4(s.scale + kt * s.scale_step, __builtin_amdgcn_readfirstlane(buf + s.scale_lds));
 }
 
 // MFMA operands of one 64-deep K half for a wave's 64 x 128 tile.
@@ -325,6 +325,7 @@ __device__ __forceinline__ void b_sources(const TileArgs& p, int e, int ntile, S
     if (wave >= 4) {
         s.scale = p.wsp + int64_t(e) * p.N * (p.K / 32) + int64_t(ntile * 4 + wave - 4) * KT * 256 + lane * 4;
         s.scale_step = 256;
+        s.scale_lds = uint32_t(kOffBS + (wave - 4) * 256);
     }
 }
 
@@ -341,6 +342,7 @@ __device__ __forceinline__ void a_sources(const TileArgs& p, int blk, StageSrc& 
     if (wave < 4) {
         s.scale = p.as + frag_scale_off(row0 + wave * 64 + lane, 0, p.cap);
         s.scale_step = p.cap * 4;
+        s.scale_lds = uint32_t(kOffAS + wave * 256);
     }
 }
 
@@ -462,8 +464,12 @@ gemm2_tile_kernel(TileArgs p)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ int32_t s_route[kTM];
     __shared__ float s_w[kTM];
+    span_begin(p.clk);
     int ntile, blk, e;
-    if (!tile_of(p, p.N / kTN, ntile, blk, e)) return;
+    if (!tile_of(p, p.N / kTN, ntile, blk, e)) {
+        span_end(p.clk);
+        return;
+    }
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const int R = p.M * p.topk;
@@ -510,6 +516,7 @@ gemm2_tile_kernel(TileArgs p)
         if (sr < R)
             *reinterpret_cast<uint4*>(p.partial + int64_t(sr) * D + ntile * kTN + (lane & 31) * 8) = v;
     }
+    span_end(p.clk);
 }
 
 hipError_t tile_allow_lds()
@@ -542,7 +549,7 @@ hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const Kerne
     if (!a.expert_block0) return hipErrorInvalidValue;
     TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.block_expert,
                a.num_valid, a.expert_block0, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr,
-               nullptr, a.partial, nullptr};
+               nullptr, a.partial, a.clk};
     MOE_LAUNCH(gemm2_tile_kernel, dim3(tile_grid(a.D / kTN, a.nb_cap)), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p);
     return hipGetLastError();

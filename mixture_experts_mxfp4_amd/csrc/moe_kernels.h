@@ -93,6 +93,7 @@ struct Gemm2Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
     const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
+    uint64_t* clk = nullptr;       // optional workgroup spans (tiled kernel)
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
