@@ -36,12 +36,10 @@ constexpr int kOffAS = kOffB + kTN * 64; // A scales: [row][4 B]
 constexpr int kOffBS = kOffAS + kTM * 4; // B scales: [n64 group][lane][4 slices]
 constexpr int kStageBytes = kOffBS + kTN * 4;
 constexpr int kLoadsPerStage = 5;        // global_load_lds per wave per stage
-// Epilogue staging in the (then idle) ring: rows padded by 16 B so that
-// consecutive rows start 4 banks apart.
-constexpr int kHStride = 128 * 2 + 16;   // stage 1: 128 bf16 h columns per row
-constexpr int kPStride = kTN * 2 + 16;   // stage 2: 256 bf16 output columns per row
-static_assert(kTM * kPStride <= kStages * kStageBytes && kTM * kHStride <= kStages * kStageBytes,
-              "epilogue staging must fit in the ring");
+// Stage-2 epilogue staging in the (then idle) ring: rows padded by 16 B so
+// that consecutive rows start 4 banks apart.
+constexpr int kPStride = kTN * 2 + 16;   // 256 bf16 output columns per row
+static_assert(kTM * kPStride <= kStages * kStageBytes, "epilogue staging must fit in the ring");
 
 size_t tile_lds_bytes() { return size_t(kStages) * kStageBytes; }
 
@@ -166,7 +164,7 @@ __device__ __forceinline__ uint32_t read_sb(const uint8_t* buf, int wave_n, int 
 // next MFMA queued while loads, LDS reads and the barrier are in flight.  The
 // scale words are shifted once per stage to this lane's byte pair and the MFMA
 // byte selects pick chunk and slice.
-template <bool kLoad>
+template <bool kLoad, bool kSwap>
 __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, uint8_t* lds,
                                           uint32_t lds0, int wave, int lane, v16f acc[2][4],
                                           HalfFrags& f0, HalfFrags& f1, uint32_t sa[2],
@@ -185,8 +183,12 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int mt = i >> 2, nt = i & 3;
-        acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<0, 2>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1])
-                               : mfma_fp4_sel<0, 0>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1]);
+        if constexpr (kSwap)
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 0>(f0.b[nt], f0.a[mt], acc[mt][nt], sb0[nt >> 1], sa[mt])
+                                   : mfma_fp4_sel<0, 0>(f0.b[nt], f0.a[mt], acc[mt][nt], sb0[nt >> 1], sa[mt]);
+        else
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<0, 2>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1])
+                                   : mfma_fp4_sel<0, 0>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1]);
         if (kLoad && i < kLoadsPerStage) issue_load(src, kt + kStages - 1, i, load_buf, wave);
         if (i >= 1 && i < 7) read_frag(cur, 1, wave_m, wave_n, lane, f1, i - 1);
         if (i == 7) {
@@ -210,8 +212,12 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int mt = i >> 2, nt = i & 3;
-        acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
-                               : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
+        if constexpr (kSwap)
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt])
+                                   : mfma_fp4_sel<0, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt]);
+        else
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
+                                   : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
         // (after the last stage these read a ring slot whose contents go unused)
         if (i < 6) read_frag(nxt, 0, wave_m, wave_n, lane, f0, i);
         if (i == 6) {
@@ -228,6 +234,10 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
     sa[1] = sa_next[1];
 }
 
+// kSwap: the weights are the MFMA's first operand, so acc[mt][nt] holds the
+// transposed 32x32 tile (lane: row mt*32 + lane%32 of the wave's rows,
+// element i: column (i/4)*8 + (lane/32)*4 + i%4 of N tile nt).
+template <bool kSwap>
 __device__ __forceinline__ void tile_mainloop(const StageSrc& src, int KT, uint8_t* lds,
                                               v16f acc[2][4])
 {
@@ -256,10 +266,10 @@ __device__ __forceinline__ void tile_mainloop(const StageSrc& src, int KT, uint8
     int kt = 0;
 #pragma unroll 1
     for (; kt + kStages - 1 < KT; ++kt)
-        tile_step<true>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
+        tile_step<true, kSwap>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
 #pragma unroll 1
     for (; kt < KT; ++kt)
-        tile_step<false>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
+        tile_step<false, kSwap>(src, KT, kt, lds, lds0, wave, lane, acc, f0, f1, sa, sb0);
 }
 
 // Main loop of a wave whose 64 rows are all padding (an expert's routes come
@@ -396,62 +406,66 @@ gemm1_tile_kernel(TileArgs p, int I)
 
     v16f acc[2][4];
     zero_acc(acc);
-    if (rows_in_use(p, blk, wave_m)) tile_mainloop(src, p.K / 128, lds, acc);
+    if (rows_in_use(p, blk, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
     else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
     // wave_n*2 + 1 of the tile (prepared 64-row group = 32 gate rows then 32 up
-    // rows); the tile's 128 h columns are K tile `ntile` of stage 2.  h goes
-    // through LDS (the ring is free once every wave is past the main loop) so
-    // that each thread then holds two whole MXFP4 blocks of one row: thread t
-    // quantizes row t/2, chunks 2(t%2) and 2(t%2)+1, and stores 32 code bytes
-    // and two scale bytes.
-    uint8_t* hs = lds;                                   // [256 rows][kHStride]
-    __syncthreads();
+    // rows: gate and up of an h column sit at the same place of tiles 2gi and
+    // 2gi+1); the tile's 128 h columns are K tile `ntile` of stage 2.  With the
+    // swapped product a lane holds, for row mt*32 + lane%32, 16 of the 32
+    // columns of an MXFP4 block (columns (i/4)*8 + (lane/32)*4 + i%4) and lane
+    // lane^32 the other 16: the block maximum takes one exchange, and after a
+    // second each half stores 8 contiguous code bytes of the row's 16-byte chunk
+    // (lanes < 32 bytes 0-7, lanes >= 32 bytes 8-15).
+    const bool upper = lane >= 32;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+        const int64_t srow = int64_t(blk) * kTM + wave_m * 64 + mt * 32 + (lane & 31);
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
+            const int c = wave_n * 2 + gi;               // 32-column chunk in K tile `ntile`
+            uint32_t hv[16];
+            uint32_t amax = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = wave_m * 64 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                const int col = (wave_n * 2 + gi) * 32 + (lane & 31);
-                const uint32_t h = f32_to_bf16_rne(silu_fast(acc[mt][2 * gi][i]) * acc[mt][2 * gi + 1][i]);
-                *reinterpret_cast<uint16_t*>(hs + row * kHStride + col * 2) = uint16_t(h);
+                hv[i] = f32_to_bf16_rne(silu_fast(acc[mt][2 * gi][i]) * acc[mt][2 * gi + 1][i]);
+                amax = max(amax, hv[i] & 0x7FFFu);
+            }
+            amax = max(amax, uint32_t(__shfl_xor(int(amax), 32)));
+            const uint32_t s = mx_scale_from_amax(amax);
+            const float so = mx_scale_operand(s);
+            // element pair (2j, 2j+1) of this lane's 16 -> chunk byte
+            // (j/2)*4 + (lane/32)*2 + j%2: bytes of i/4 = 0, 1 in `lo`, of 2, 3 in `hi`
+            uint32_t lo = 0, hi = 0;
+            lo = mx_code_pair<0>(lo, hv[0] | (hv[1] << 16), so);
+            lo = mx_code_pair<1>(lo, hv[2] | (hv[3] << 16), so);
+            lo = mx_code_pair<2>(lo, hv[4] | (hv[5] << 16), so);
+            lo = mx_code_pair<3>(lo, hv[6] | (hv[7] << 16), so);
+            hi = mx_code_pair<0>(hi, hv[8] | (hv[9] << 16), so);
+            hi = mx_code_pair<1>(hi, hv[10] | (hv[11] << 16), so);
+            hi = mx_code_pair<2>(hi, hv[12] | (hv[13] << 16), so);
+            hi = mx_code_pair<3>(hi, hv[14] | (hv[15] << 16), so);
+            // lanes < 32 hold chunk bytes {0,1,4,5} and {8,9,12,13}, lanes >= 32
+            // {2,3,6,7} and {10,11,14,15}
+            const uint32_t recv = uint32_t(__shfl_xor(int(upper ? lo : hi), 32));
+            uint2 out;
+            if (!upper) {
+                out.x = (lo & 0xFFFFu) | (recv << 16);
+                out.y = (lo >> 16) | (recv & 0xFFFF0000u);
+            } else {
+                out.x = (recv & 0xFFFFu) | (hi << 16);
+                out.y = (recv >> 16) | (hi & 0xFFFF0000u);
+            }
+            *reinterpret_cast<uint2*>(p.a2q + frag_code_off(srow, ntile, c, I / 128) + (upper ? 8 : 0)) = out;
+            if (!upper) p.a2s[frag_scale_off(srow, ntile, p.cap) + c] = uint8_t(s);
+            if (p.h_dbg) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    p.h_dbg[srow * I + ntile * 128 + c * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)] =
+                        uint16_t(hv[i]);
             }
         }
-    }
-    __syncthreads();
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t srow = int64_t(blk) * kTM + row;
-    const uint4* hrow = reinterpret_cast<const uint4*>(hs + row * kHStride + half * 128);
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = hrow[j];
-    uint32_t sc = 0;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        uint32_t amax = 0;
-#pragma unroll
-        for (int j = 4 * b; j < 4 * b + 4; ++j) {
-            const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) amax = max(amax, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
-        }
-        const uint32_t s = mx_scale_from_amax(amax);
-        uint4 codes;
-        codes.x = mx_pack8(v[4 * b].x, v[4 * b].y, v[4 * b].z, v[4 * b].w, s);
-        codes.y = mx_pack8(v[4 * b + 1].x, v[4 * b + 1].y, v[4 * b + 1].z, v[4 * b + 1].w, s);
-        codes.z = mx_pack8(v[4 * b + 2].x, v[4 * b + 2].y, v[4 * b + 2].z, v[4 * b + 2].w, s);
-        codes.w = mx_pack8(v[4 * b + 3].x, v[4 * b + 3].y, v[4 * b + 3].z, v[4 * b + 3].w, s);
-        *reinterpret_cast<uint4*>(p.a2q + frag_code_off(srow, ntile, 2 * half + b, I / 128)) = codes;
-        sc |= s << (8 * b);
-    }
-    *reinterpret_cast<uint16_t*>(p.a2s + frag_scale_off(srow, ntile, p.cap) + 2 * half) = uint16_t(sc);
-    if (p.h_dbg) {
-        uint4* dst = reinterpret_cast<uint4*>(p.h_dbg + srow * I + ntile * 128 + half * 64);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[j] = v[j];
     }
     span_end(p.clk);
 }
@@ -485,7 +499,7 @@ gemm2_tile_kernel(TileArgs p)
 
     v16f acc[2][4];
     zero_acc(acc);
-    if (rows_in_use(p, blk, wave_m)) tile_mainloop(src, p.K / 128, lds, acc);
+    if (rows_in_use(p, blk, wave_m)) tile_mainloop<false>(src, p.K / 128, lds, acc);
     else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue: the routing weight times the sum, rounded to bf16, goes through
