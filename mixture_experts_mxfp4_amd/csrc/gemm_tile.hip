@@ -190,11 +190,11 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
             acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<0, 2>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1])
                                    : mfma_fp4_sel<0, 0>(f0.a[mt], f0.b[nt], acc[mt][nt], sa[mt], sb0[nt >> 1]);
         if (kLoad && i < kLoadsPerStage) issue_load(src, kt + kStages - 1, i, load_buf, wave);
-        if (i >= 1 && i < 7) read_frag(cur, 1, wave_m, wave_n, lane, f1, i - 1);
-        if (i == 7) {
+        if (i == 0) {
             sb1[0] = read_sb(cur, wave_n, lane, 1, 0);
             sb1[1] = read_sb(cur, wave_n, lane, 1, 1);
         }
+        if (i >= 1 && i < 7) read_frag(cur, 1, wave_m, wave_n, lane, f1, i - 1);
         __builtin_amdgcn_sched_barrier(0);
     }
     // this wave's LDS reads are done, and its loads of stage kt+1 have landed
@@ -218,16 +218,17 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
         else
             acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
                                    : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
-        // (after the last stage these read a ring slot whose contents go unused)
-        if (i < 6) read_frag(nxt, 0, wave_m, wave_n, lane, f0, i);
-        if (i == 6) {
+        // (after the last stage these read a ring slot whose contents go unused;
+        // the scale words first, so they have landed when the next step shifts them)
+        if (i == 0) {
             sa_next[0] = read_sa(nxt, wave_m, lane, 0);
             sa_next[1] = read_sa(nxt, wave_m, lane, 1);
         }
-        if (i == 7) {
+        if (i == 1) {
             sb0[0] = read_sb(nxt, wave_n, lane, 0, 0);
             sb0[1] = read_sb(nxt, wave_n, lane, 0, 1);
         }
+        if (i >= 2) read_frag(nxt, 0, wave_m, wave_n, lane, f0, i - 2);
         __builtin_amdgcn_sched_barrier(0);
     }
     sa[0] = sa_next[0];
