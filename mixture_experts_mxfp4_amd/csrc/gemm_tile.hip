@@ -43,27 +43,38 @@ static_assert(kTM * kPStride <= kStages * kStageBytes, "epilogue staging must fi
 
 size_t tile_lds_bytes() { return size_t(kStages) * kStageBytes; }
 
-// Direct global->LDS loads.  Lane l's 16 (or 4) bytes land at LDS address
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p)
+{
+    return uint32_t(uintptr_t((__attribute__((address_space(3))) const uint8_t*)(p)));
+}
+
+// A wave-uniform pointer as the compiler's uniform value (SGPR pair).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+
+// Direct global->LDS loads from a wave-uniform 64-bit base (SGPRs) plus a
+// 32-bit per-lane byte offset.  Lane l's 16 (or 4) bytes land at LDS address
 // m0 + l*16 (l*4); `lds_addr` must be wave-uniform.  They are issued from
 // inline assembly so that the compiler does not treat them as LDS writes and
 // drain the whole prefetch pipeline (s_waitcnt vmcnt(0)) before every LDS
 // read; completion is tracked explicitly with wait_barrier<N>() instead.  m0
 // is saved and restored around the load.
-__device__ __forceinline__ uint32_t lds_address(const uint8_t* p)
-{
-    return uint32_t(uintptr_t((__attribute__((address_space(3))) const uint8_t*)(p)));
-}
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr)
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint32_t lds_addr)
 {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(g), "s"(lds_addr) : "memory");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr)
+__device__ __forceinline__ void dma4s(const uint8_t* base, uint32_t off, uint32_t lds_addr)
 {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(g), "s"(lds_addr) : "memory");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr) : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding,
@@ -108,11 +119,15 @@ struct TileArgs {
 
 // The per-wave source pointers of one stage's five loads; every load is a
 // contiguous run (1 KiB of codes or 256 B of scales per wave).
+// Wave-uniform 64-bit bases (held in SGPRs) and 32-bit per-lane offsets.
 struct StageSrc {
-    const uint8_t* a_code[2];  // this lane's 16 B of A slices 2w, 2w+1 at kt = 0
-    const uint8_t* b_code[2];  // this lane's 16 B of B pieces 2w, 2w+1 at kt = 0
-    const uint8_t* scale;      // waves 0-3: A scale word of row 64w+lane; 4-7: B scale word
-    int64_t scale_step;        // bytes per K tile of `scale`
+    const uint8_t* a_base;     // the block's A codes
+    const uint8_t* b_base;     // the expert's prepared weight codes
+    const uint8_t* s_base;     // waves 0-3: the block's A scale words; 4-7: B scale words
+    uint32_t a_off[2];         // this lane's 16 B of A slices 2w, 2w+1 at kt = 0
+    uint32_t b_off[2];         // this lane's 16 B of B pieces 2w, 2w+1 at kt = 0
+    uint32_t s_off;            // this lane's scale word at kt = 0
+    uint32_t s_step;           // bytes per K tile of the scale words
     uint32_t scale_lds;        // byte offset of this wave's scale words in a stage buffer
 };
 
@@ -120,9 +135,10 @@ struct StageSrc {
 // `buf`; wave: wave-uniform wave index.
 __device__ __forceinline__ void issue_load(const StageSrc& s, int kt, int d, uint32_t buf, int wave)
 {
-    if (d < 2) dma16(s.a_code[d] + int64_t(kt) * 1024, buf + (2 * wave + d) * 1024);
-    else if (d < 4) dma16(s.b_code[d - 2] + int64_t(kt) * 4096, buf + kOffB + (2 * wave + d - 2) * 1024);
-    else dma4(s.scale + kt * s.scale_step, __builtin_amdgcn_readfirstlane(buf + s.scale_lds));
+    if (d < 2) dma16s(s.a_base, s.a_off[d] + uint32_t(kt) * 1024u, buf + (2 * wave + d) * 1024);
+    else if (d < 4) dma16s(s.b_base, s.b_off[d - 2] + uint32_t(kt) * 4096u, buf + kOffB + (2 * wave + d - 2) * 1024);
+    else dma4s(uniform_ptr(s.s_base), s.s_off + uint32_t(kt) * s.s_step,
+               __builtin_amdgcn_readfirstlane(buf + s.scale_lds));
 }
 
 // MFMA operands of one 64-deep K half for a wave's 64 x 128 tile.
@@ -325,17 +341,19 @@ __device__ __forceinline__ void zero_acc(v16f acc[2][4])
 // groups n64 = ntile*4 + piece/4 at K tile 0; B scale word of group w-4.
 __device__ __forceinline__ void b_sources(const TileArgs& p, int e, int ntile, StageSrc& s)
 {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
     const int KT = p.K / 128;
-    const uint8_t* wexp = p.wp + int64_t(e) * p.N * (p.K / 2);
+    s.b_base = uniform_ptr(p.wp + int64_t(e) * p.N * (p.K / 2));   // < 2^31 bytes per expert
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int piece = 2 * wave + h;
-        s.b_code[h] = wexp + int64_t(ntile * 4 + piece / 4) * KT * 4096 + (piece % 4) * 1024 + lane * 16;
+        s.b_off[h] = uint32_t((ntile * 4 + piece / 4) * KT * 4096 + (piece % 4) * 1024 + lane * 16);
     }
     if (wave >= 4) {
-        s.scale = p.wsp + int64_t(e) * p.N * (p.K / 32) + int64_t(ntile * 4 + wave - 4) * KT * 256 + lane * 4;
-        s.scale_step = 256;
+        s.s_base = uniform_ptr(p.wsp + int64_t(e) * p.N * (p.K / 32) + int64_t(ntile * 4 + wave - 4) * KT * 256);
+        s.s_off = uint32_t(lane * 4);
+        s.s_step = 256;
         s.scale_lds = uint32_t(kOffBS + (wave - 4) * 256);
     }
 }
@@ -344,15 +362,18 @@ __device__ __forceinline__ void b_sources(const TileArgs& p, int e, int ntile, S
 // rows; A scale words of rows 64w .. 64w+63 (waves 0-3).
 __device__ __forceinline__ void a_sources(const TileArgs& p, int blk, StageSrc& s)
 {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
     const int KT = p.K / 128;
     const int64_t row0 = int64_t(blk) * kTM;
+    s.a_base = uniform_ptr(p.a + frag_code_off(row0, 0, 0, KT));   // the block: 256 * K/2 bytes
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        s.a_code[h] = p.a + frag_code_off(row0 + (2 * wave + h) * 16, 0, 0, KT) + lane * 16;
+        s.a_off[h] = uint32_t(frag_code_off((2 * wave + h) * 16, 0, 0, KT) + lane * 16);
     if (wave < 4) {
-        s.scale = p.as + frag_scale_off(row0 + wave * 64 + lane, 0, p.cap);
-        s.scale_step = p.cap * 4;
+        s.s_base = uniform_ptr(p.as + frag_scale_off(row0, 0, p.cap));
+        s.s_off = uint32_t((wave * 64 + lane) * 4);
+        s.s_step = uint32_t(p.cap * 4);
         s.scale_lds = uint32_t(kOffAS + wave * 256);
     }
 }
@@ -366,22 +387,41 @@ __device__ __forceinline__ void a_sources(const TileArgs& p, int blk, StageSrc& 
 // in their L2 instead of every XCD fetching every block.  The grid is
 // rounded up to a multiple of 8 (tile_grid), so every share fits.
 
-// Column tile, block and expert of this workgroup; false past the used tiles.
-__device__ __forceinline__ bool tile_of(const TileArgs& p, int n_tiles, int& ntile, int& blk,
-                                        int& e)
+// This workgroup's XCD share [lo, hi) of the used tiles and its index j in
+// that XCD.
+__device__ __forceinline__ void xcd_share(const TileArgs& p, int n_tiles, int64_t& lo, int64_t& hi,
+                                          int& j)
 {
     const int w = blockIdx.x;
-    const int xcd = w % kXcds, j = w / kXcds;
+    const int xcd = w % kXcds;
+    j = w / kXcds;
     const int64_t used = int64_t(n_tiles) * (p.num_valid[0] / kTM);
-    const int64_t lo = used * xcd / kXcds, hi = used * (xcd + 1) / kXcds;
-    const int64_t t = lo + j;
-    if (t >= hi) return false;
+    lo = used * xcd / kXcds;
+    hi = used * (xcd + 1) / kXcds;
+}
+
+// Column tile, block and expert of tile t of the order above.
+__device__ __forceinline__ void tile_at(const TileArgs& p, int n_tiles, int64_t t, int& ntile,
+                                        int& blk, int& e)
+{
     e = p.block_expert[t / n_tiles];
     const int first = p.expert_block0[e];
     const int nb = p.expert_block0[e + 1] - first;
     const int local = int(t - int64_t(n_tiles) * first);
     ntile = local / nb;
     blk = first + local % nb;
+}
+
+// Column tile, block and expert of this workgroup (one tile per workgroup);
+// false past the used tiles.
+__device__ __forceinline__ bool tile_of(const TileArgs& p, int n_tiles, int& ntile, int& blk,
+                                        int& e)
+{
+    int64_t lo, hi;
+    int j;
+    xcd_share(p, n_tiles, lo, hi, j);
+    if (lo + j >= hi) return false;
+    tile_at(p, n_tiles, lo + j, ntile, blk, e);
     return true;
 }
 
