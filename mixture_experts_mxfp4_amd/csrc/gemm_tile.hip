@@ -466,27 +466,32 @@ gemm1_tile_kernel(TileArgs p, int I)
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             const int c = wave_n * 2 + gi;               // 32-column chunk in K tile `ntile`
-            uint32_t hv[16];
-            uint32_t amax = 0;
+            // h of element pairs (2j, 2j+1) as packed bf16; block maximum on
+            // the 15-bit magnitudes, two per packed 16-bit max
+            typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+            uint32_t hp[8];
+            u16x2_t m2 = {0, 0};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                hv[i] = f32_to_bf16_rne(silu_fast(acc[mt][2 * gi][i]) * acc[mt][2 * gi + 1][i]);
-                amax = max(amax, hv[i] & 0x7FFFu);
+            for (int j = 0; j < 8; ++j) {
+                hp[j] = f32x2_to_bf16x2(silu_fast(acc[mt][2 * gi][2 * j]) * acc[mt][2 * gi + 1][2 * j],
+                                        silu_fast(acc[mt][2 * gi][2 * j + 1]) * acc[mt][2 * gi + 1][2 * j + 1]);
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, hp[j] & 0x7FFF7FFFu));
             }
+            uint32_t amax = max(uint32_t(m2.x), uint32_t(m2.y));
             amax = max(amax, uint32_t(__shfl_xor(int(amax), 32)));
             const uint32_t s = mx_scale_from_amax(amax);
             const float so = mx_scale_operand(s);
-            // element pair (2j, 2j+1) of this lane's 16 -> chunk byte
-            // (j/2)*4 + (lane/32)*2 + j%2: bytes of i/4 = 0, 1 in `lo`, of 2, 3 in `hi`
+            // element pair j of this lane's 16 -> chunk byte (j/2)*4 + (lane/32)*2 + j%2:
+            // bytes of pairs 0-3 in `lo`, of pairs 4-7 in `hi`
             uint32_t lo = 0, hi = 0;
-            lo = mx_code_pair<0>(lo, hv[0] | (hv[1] << 16), so);
-            lo = mx_code_pair<1>(lo, hv[2] | (hv[3] << 16), so);
-            lo = mx_code_pair<2>(lo, hv[4] | (hv[5] << 16), so);
-            lo = mx_code_pair<3>(lo, hv[6] | (hv[7] << 16), so);
-            hi = mx_code_pair<0>(hi, hv[8] | (hv[9] << 16), so);
-            hi = mx_code_pair<1>(hi, hv[10] | (hv[11] << 16), so);
-            hi = mx_code_pair<2>(hi, hv[12] | (hv[13] << 16), so);
-            hi = mx_code_pair<3>(hi, hv[14] | (hv[15] << 16), so);
+            lo = mx_code_pair<0>(lo, hp[0], so);
+            lo = mx_code_pair<1>(lo, hp[1], so);
+            lo = mx_code_pair<2>(lo, hp[2], so);
+            lo = mx_code_pair<3>(lo, hp[3], so);
+            hi = mx_code_pair<0>(hi, hp[4], so);
+            hi = mx_code_pair<1>(hi, hp[5], so);
+            hi = mx_code_pair<2>(hi, hp[6], so);
+            hi = mx_code_pair<3>(hi, hp[7], so);
             // lanes < 32 hold chunk bytes {0,1,4,5} and {8,9,12,13}, lanes >= 32
             // {2,3,6,7} and {10,11,14,15}
             const uint32_t recv = uint32_t(__shfl_xor(int(upper ? lo : hi), 32));
@@ -504,7 +509,7 @@ gemm1_tile_kernel(TileArgs p, int I)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     p.h_dbg[srow * I + ntile * 128 + c * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)] =
-                        uint16_t(hv[i]);
+                        uint16_t(hp[i >> 1] >> (16 * (i & 1)));
             }
         }
     }
@@ -540,25 +545,30 @@ gemm2_tile_kernel(TileArgs p)
 
     v16f acc[2][4];
     zero_acc(acc);
-    if (rows_in_use(p, blk, wave_m)) tile_mainloop<false>(src, p.K / 128, lds, acc);
+    if (rows_in_use(p, blk, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
     else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue: the routing weight times the sum, rounded to bf16, goes through
     // LDS as the 256 x 256 tile; then each half-wave stores one row's 512
     // contiguous bytes into its route's partial row (padding rows are skipped).
+    // With the swapped product a lane holds one row (mt*32 + lane%32 of the
+    // wave's 64) and, per group of four elements, four consecutive columns:
+    // one routing weight per row tile and 8-byte LDS writes.
     uint8_t* ps = lds;                                   // [256 rows][kPStride]
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+        const int row = wave_m * 64 + mt * 32 + (lane & 31);
+        const float w = s_w[row];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = wave_m * 64 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            const float w = s_w[row];
+        for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int col = wave_n * 128 + nt * 32 + (lane & 31);
-                *reinterpret_cast<uint16_t*>(ps + row * kPStride + col * 2) =
-                    uint16_t(f32_to_bf16_rne(w * acc[mt][nt][i]));
+            for (int q = 0; q < 4; ++q) {
+                const int col = wave_n * 128 + nt * 32 + q * 8 + (lane >> 5) * 4;
+                uint2 v;
+                v.x = f32x2_to_bf16x2(w * acc[mt][nt][4 * q], w * acc[mt][nt][4 * q + 1]);
+                v.y = f32x2_to_bf16x2(w * acc[mt][nt][4 * q + 2], w * acc[mt][nt][4 * q + 3]);
+                *reinterpret_cast<uint2*>(ps + row * kPStride + col * 2) = v;
             }
         }
     }

@@ -25,6 +25,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+// Two floats -> packed bf16 pair (lo in bits 0-15) in one conversion.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, b16x2_t));
+}
 
 // ------------------------------------------------------ MXFP4 quantizer ---
 //
