@@ -98,9 +98,11 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    acc[rt][q] = mfma_fp4_16x16x128(a[u][rt], b[u][q], acc[rt][q],
-                                                    (sa[u][rt] >> ash) & 0xFFu,
-                                                    (sw[u] >> (8 * q)) & 0xFFu);
+                    // weights as the first operand: acc[rt][q] holds the transposed
+                    // 16x16 tile (lane: row rt*16 + lane%16, columns 4*(lane/16) + i)
+                    acc[rt][q] = mfma_fp4_16x16x128(b[u][q], a[u][rt], acc[rt][q],
+                                                    (sw[u] >> (8 * q)) & 0xFFu,
+                                                    (sa[u][rt] >> ash) & 0xFFu);
     };
     int kt = 0;
     for (; kt + U <= KT; kt += U) steps(std::integral_constant<int, U>{}, kt);
@@ -112,16 +114,15 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
     if (threadIdx.x < BM) s_route[threadIdx.x] = sorted_route[int64_t(blk) * BM + threadIdx.x];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+        const int row = rt * 16 + lane % 16;
+        const float w = sorted_w[int64_t(blk) * BM + row];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = rt * 16 + 4 * (lane / 16) + i;
-            const float w = sorted_w[int64_t(blk) * BM + row];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wave * 64 + q * 16 + lane % 16;
-                *reinterpret_cast<uint16_t*>(stage + row * kRow + col * 2) =
-                    uint16_t(f32_to_bf16_rne(w * acc[rt][q][i]));
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int col = wave * 64 + q * 16 + 4 * (lane / 16);
+            uint2 v;
+            v.x = f32x2_to_bf16x2(w * acc[rt][q][0], w * acc[rt][q][1]);
+            v.y = f32x2_to_bf16x2(w * acc[rt][q][2], w * acc[rt][q][3]);
+            *reinterpret_cast<uint2*>(stage + row * kRow + col * 2) = v;
         }
     }
     __syncthreads();
