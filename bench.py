@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused MXFP4 MoE forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--a16w4]
 
 One step = one full forward through the C ABI on a seeded synthetic
 DeepSeek-R1-shaped batch whose inputs are already resident in HBM: on the
@@ -11,6 +11,8 @@ per-token sum); on the sorted paths the prologue (route sort + activation
 quant), stage 1, stage 2 and the per-token slot reduction.  Prepared weights are kept in
 several copies and rotated step by step, so that every forward streams its
 experts' weights from HBM rather than from the 256 MB Infinity Cache.
+--a16w4 runs the same workload through the A16W4 forward (bf16 activations,
+no activation quantization; route-indexed kernels, up to 32 tokens).
 
 Prints ONE JSON line: the metric (algorithmic GB/s for HBM-bound workloads,
 TFLOP/s for MFMA-bound ones), microseconds per forward, the roofline of the
@@ -46,6 +48,7 @@ METRIC = "µs/forward + HBM GB/s (M≤16) / MXFP4 MFMA TFLOPS (M≥1024), D=7168
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA
 MALL_BYTES = 256 << 20
+NS_A16 = 13.0                   # oracle ns per multiply-add with bf16 activations
 # the stage-1 (dominant) kernel and the sources that define it, per path
 _CSRC = "mixture_experts_mxfp4_amd/csrc/"
 STAGE1 = {
@@ -154,7 +157,7 @@ def load_traffic(workload, path_name):
 
 # --------------------------------------------------------------- CPU leg ---
 
-def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0):
+def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0, act_quant=True):
     """The CPU oracle on a bounded sample of the same workload (its first
     tokens), weights quantized by the oracle itself (untimed, like the GPU's
     weight preparation)."""
@@ -164,7 +167,8 @@ def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0):
     from mixture_experts_mxfp4_amd import inputs
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    per_tok_cpu_s = 16e-9 * 3 * w.I * w.D * w.topk         # measured oracle cost ~16 ns/MAC
+    # measured oracle cost per multiply-add: ~16 ns (MXFP4 operands), ~NS_A16 ns (bf16)
+    per_tok_cpu_s = (16e-9 if act_quant else NS_A16 * 1e-9) * 3 * w.I * w.D * w.topk
     n = int(max(1, min(w.M, round(target_cpu_s / per_tok_cpu_s))))
     toks = np.arange(n)
     ids_np = ids.numpy()
@@ -182,7 +186,8 @@ def cpu_baseline(w, hidden, ids, tw, w13f, w2f, target_cpu_s=16.0):
     hb = inputs.bf16_bits(hidden)
     threads = min(threads, n)          # the oracle runs one token per thread
     t0 = time.perf_counter()
-    oracle.forward(hb, *wq, sub_ids, tw.numpy(), tokens=toks, nthreads=threads)
+    oracle.forward(hb, *wq, sub_ids, tw.numpy(), tokens=toks, nthreads=threads,
+                   act_quant=act_quant)
     dt = time.perf_counter() - t0
     alg = algorithmic(w, ids_np, toks)
     return {"seconds": dt, "tokens": n, "threads": threads, "alg": alg}
@@ -224,18 +229,40 @@ def run(args):
 
     h_d, ids_d, tw_d = hidden.to(dev), ids.to(dev), tw.to(dev)
     out = torch.empty_like(h_d)
-    ws = binding.alloc_workspace(w.M, w.D, w.I, w.E, w.topk, dev)
-    torch.cuda.synchronize()
+    a16 = args.a16w4
+    if a16:
+        if binding.moe_mxfp4_a16w4_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
+            raise SystemExit(f"bench.py: the A16W4 forward does not run {w.name} (M={w.M})")
+        ws = binding.alloc_workspace_a16w4(w.M, w.D, w.I, w.E, w.topk, dev)
+        path = binding.PATH_DIRECT
+        n_wg = binding.a16w4_stage1_workgroups(w.M, w.I, w.E, w.topk)
 
-    path = binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)
+        def forward(wset):
+            binding.moe_mxfp4_forward_a16w4(h_d, *wset, ids_d, tw_d, out, ws)
+
+        def forward_timed(wset, ev, clk=None):
+            binding.moe_mxfp4_forward_a16w4_debug(h_d, *wset, ids_d, tw_d, out, ws,
+                                                  kernel_events=ev, stage1_clock=clk)
+    else:
+        ws = binding.alloc_workspace(w.M, w.D, w.I, w.E, w.topk, dev)
+        path = binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)
+        n_wg = binding.moe_mxfp4_stage1_workgroups(w.M, w.D, w.I, w.E, w.topk)
+
+        def forward(wset):
+            binding.moe_mxfp4_forward(h_d, *wset, ids_d, tw_d, out, ws)
+
+        def forward_timed(wset, ev, clk=None):
+            binding.moe_mxfp4_forward_profiled(h_d, *wset, ids_d, tw_d, out, ws, ev, clk)
+    torch.cuda.synchronize()
     path_name = binding.PATH_NAMES[path]
     launches = binding.PATH_LAUNCHES[path]
+    workload_id = w.name + ("_a16w4" if a16 else "")
 
     # untimed warm-up; the last warm-up pass also times every launch
     stage_ev = Events(8)
     for i in range(args.warmup):
         ev = stage_ev.ev if i == args.warmup - 1 else [None] * 8
-        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev)
+        forward_timed(weight_sets[i % copies], ev)
     torch.cuda.synchronize()
     stages_us = None
     if args.warmup > 0:
@@ -246,7 +273,7 @@ def run(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        binding.moe_mxfp4_forward(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws)
+        forward(weight_sets[i % copies])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = 1000.0 * (t1 - t0) / args.steps
@@ -263,7 +290,6 @@ def run(args):
     prev = 0 if 0 in launches else launches[-1]          # launch before stage 1
     same_forward = prev < 1
     khz = binding.moe_mxfp4_wall_clock_khz()
-    n_wg = binding.moe_mxfp4_stage1_workgroups(w.M, w.D, w.I, w.E, w.topk)
     spans = torch.zeros((args.steps + 1, 2 * n_wg), dtype=torch.int64, device=dev)
     step_ev = Events(2 * (args.steps + 1))
     torch.cuda.synchronize()
@@ -271,8 +297,7 @@ def run(args):
         ev = [None] * 8
         ev[2 * prev + 1] = step_ev.ev[2 * i]
         ev[3] = step_ev.ev[2 * i + 1]
-        binding.moe_mxfp4_forward_profiled(h_d, *weight_sets[i % copies], ids_d, tw_d, out, ws, ev,
-                                           spans[i])
+        forward_timed(weight_sets[i % copies], ev, spans[i])
     torch.cuda.synchronize()
     if same_forward:
         ev_times = [step_ev.ms(2 * i, 2 * i + 1) for i in range(1, args.steps + 1)]
@@ -298,7 +323,7 @@ def run(args):
         achieved = alg["stage1_flops"] / (stage1_ms / 1000.0) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(args.workload, path_name)
+    roof["traffic"] = load_traffic(workload_id, path_name)
     roof["kernel"] = STAGE1[path_name][0]
     roof["source_sha256_16"] = source_hash(STAGE1[path_name][1])
     roof["kernel_us"] = round(stage1_ms * 1000.0, 2)
@@ -308,12 +333,13 @@ def run(args):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, hidden, ids, tw, w13f, w2f, args.cpu_sample_s)
+        cb = cpu_baseline(w, hidden, ids, tw, w13f, w2f, args.cpu_sample_s, act_quant=not a16)
         ca = cb["alg"]
         cval = ca["bytes"] / cb["seconds"] / 1e9 if hbm_bound else ca["flops"] / cb["seconds"] / 1e12
         cpu = {"value": round(cval, 4), "unit": unit, "cores": cb["threads"], "kind": "oracle",
                "sample": f"first {cb['tokens']} of {w.M} tokens of the {w.name} workload "
-                         f"({cb['seconds']:.2f} s wall, fp64 C oracle, {cb['threads']} threads)"}
+                         f"({cb['seconds']:.2f} s wall, fp64 C oracle"
+                         f"{', activations unquantized' if a16 else ''}, {cb['threads']} threads)"}
 
     line = {
         "metric": METRIC,
@@ -326,14 +352,16 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "bf16" if a16 else "mxfp4",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: M={w.M} D={w.D} I={w.I} E={w.E} top{w.topk} "
+        "config": {"workload": f"{w.name}{' A16W4 (bf16 activations, MXFP4 weights)' if a16 else ''}"
+                               f": M={w.M} D={w.D} I={w.I} E={w.E} top{w.topk} "
                                f"({w.n_routed} routed {w.routing} + shared expert {w.E - 1})",
+                   "mode": "a16w4" if a16 else "a4w4",
                    "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
                    "routing": w.routing, "seed": w.seed, "global_batch": w.M,
                    "parallelism": "single GPU", "path": path_name,
-                   "block_m": binding.moe_mxfp4_block_m(w.M, w.D, w.I, w.E, w.topk),
+                   "block_m": 16 if a16 else binding.moe_mxfp4_block_m(w.M, w.D, w.I, w.E, w.topk),
                    "weight_copies": copies},
         "us_per_forward": round(ms_per_step * 1000.0, 2),
         "tokens_per_s": round(w.M / sec, 1),
@@ -409,8 +437,10 @@ def _pmc_mean(d, kernel_prefix):
 
 def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     from mixture_experts_mxfp4_amd import binding, inputs
-    w = inputs.WORKLOADS[workload]
-    path_name = binding.PATH_NAMES[binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)]
+    a16 = workload.endswith("_a16w4")          # the A16W4 forward on that workload
+    w = inputs.WORKLOADS[workload[:-len("_a16w4")] if a16 else workload]
+    path = binding.PATH_DIRECT if a16 else binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)
+    path_name = binding.PATH_NAMES[path]
     kernel, sources = STAGE1[path_name]
     copy_kib = float(1 << 30) / 1024.0
     cf, _ = _pmc_mean(copy_fetch_dir, "__amd_rocclr_copyBuffer")
@@ -441,6 +471,8 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
                    choices=["tiny", "decode", "small_batch", "prefill", "large_prefill"])
+    p.add_argument("--a16w4", action="store_true",
+                   help="the A16W4 forward (bf16 activations; up to 32 tokens)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=16.0,

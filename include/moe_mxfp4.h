@@ -235,6 +235,58 @@ int moe_mxfp4_wall_clock_khz(void);
  * invalid shape or M = 0). */
 int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk);
 
+/* ---------------------------------------------------------------------------
+ * A16W4 forward: bf16 activations, MXFP4 weights.
+ *
+ * The variant that kernelindex.com amd-moe-mxfp4 submission 754773 takes for
+ * its 16-token shapes (`custom_kernel`, the branch taken when the shape's
+ * ksplit is above 1): neither the activations nor the SwiGLU output are
+ * quantized, so
+ *
+ * out[t, :] = bf16( sum_{s < topk, 0 <= e < E} topk_w[t, s] *
+ *                   W2[e] . bf16( silu(Wg[e] . hidden[t]) * (Wu[e] . hidden[t]) ) )
+ *
+ * with each weight element widened to bf16 exactly (e2m1 value x 2^(s-127);
+ * a magnitude past the bf16 range, possible only for scale bytes >= 253,
+ * becomes +-inf), bf16 x bf16 products accumulated in fp32, h rounded to
+ * bf16 once, and the per-token sum in fp32 over the experts in descending
+ * id order, rounded to bf16 once.  Arguments, layouts, ownership, id
+ * semantics and error behaviour are those of moe_mxfp4_forward (the same
+ * prepared weights); the workspace size is moe_mxfp4_a16w4_workspace_bytes.
+ *
+ * Few tokens only: M <= 32, topk <= 16, M * topk <= 1024, E <= 1024, else
+ * MOE_MXFP4_ERR_UNSUPPORTED (and moe_mxfp4_a16w4_workspace_bytes returns 0).
+ * Two launches: stage 1 (route scan, gate_up GEMM + SwiGLU, h stored bf16
+ * per route) and stage 2 (down GEMM x routing weight + per-token sum).
+ * ------------------------------------------------------------------------- */
+size_t moe_mxfp4_a16w4_workspace_bytes(int M, int D, int I, int E, int topk);
+
+int moe_mxfp4_forward_a16w4(const uint16_t* hidden,
+                            const uint8_t* w13, const uint8_t* w13_scale,
+                            const uint8_t* w2, const uint8_t* w2_scale,
+                            const int32_t* topk_ids, const float* topk_w,
+                            uint16_t* out,
+                            int M, int D, int I, int E, int topk,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* moe_mxfp4_forward_a16w4 with exports (any of them may be NULL):
+ *   h             bf16 [M*topk, I]: silu(gate)*up of route r = t*topk + s in
+ *                 row r (rows of invalid ids unspecified), 16-byte aligned
+ *   kernel_events as in moe_mxfp4_forward_profiled (launches 1 and 2 only)
+ *   stage1_clock  as in moe_mxfp4_forward_profiled, for the
+ *                 (I/64) * min(E, M*topk) stage-1 workgroups of this path:
+ *                 2 * (I/64) * min(E, M*topk) uint64, 8-byte aligned */
+int moe_mxfp4_forward_a16w4_debug(const uint16_t* hidden,
+                                  const uint8_t* w13, const uint8_t* w13_scale,
+                                  const uint8_t* w2, const uint8_t* w2_scale,
+                                  const int32_t* topk_ids, const float* topk_w,
+                                  uint16_t* out,
+                                  int M, int D, int I, int E, int topk,
+                                  void* workspace, size_t workspace_bytes,
+                                  uint16_t* h, hipEvent_t* kernel_events,
+                                  uint64_t* stage1_clock, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,13 +43,21 @@ _lib.moe_mxfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.moe_mxfp4_quantize.restype = _I
 _lib.moe_mxfp4_route.argtypes = [_P, _P] + [_I] * 4 + [_P] * 4 + [_P]
 _lib.moe_mxfp4_route.restype = _I
+_lib.moe_mxfp4_a16w4_workspace_bytes.argtypes = [_I] * 5
+_lib.moe_mxfp4_a16w4_workspace_bytes.restype = _SZ
+_lib.moe_mxfp4_forward_a16w4.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
+_lib.moe_mxfp4_forward_a16w4.restype = _I
+_lib.moe_mxfp4_forward_a16w4_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P, _P, _P]
+_lib.moe_mxfp4_forward_a16w4_debug.restype = _I
 
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
            "moe_mxfp4_path",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
            "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
            "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled",
-           "moe_mxfp4_wall_clock_khz", "moe_mxfp4_stage1_workgroups")
+           "moe_mxfp4_wall_clock_khz", "moe_mxfp4_stage1_workgroups",
+           "moe_mxfp4_a16w4_workspace_bytes", "moe_mxfp4_forward_a16w4",
+           "moe_mxfp4_forward_a16w4_debug")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -281,6 +289,75 @@ def moe_mxfp4_route(topk_ids, topk_w, E, block_m, stream=None):
                                 _stream(stream)))
     return {"sorted_route": sr[:cap], "sorted_w": sw[:cap], "block_expert": be[:cap // block_m],
             "num_valid": nv, "cap": cap}
+
+
+def moe_mxfp4_a16w4_workspace_bytes(M, D, I, E, topk) -> int:
+    """Workspace of the A16W4 forward (0: shape not supported by it)."""
+    return int(_lib.moe_mxfp4_a16w4_workspace_bytes(M, D, I, E, topk))
+
+
+def a16w4_stage1_workgroups(M, I, E, topk) -> int:
+    return (I // 64) * min(E, M * topk) if M > 0 else 0
+
+
+def alloc_workspace_a16w4(M, D, I, E, topk, device="cuda"):
+    n = moe_mxfp4_a16w4_workspace_bytes(M, D, I, E, topk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_mxfp4_forward_a16w4(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out=None,
+                            workspace=None, stream=None):
+    """A16W4 forward (bf16 activations, no activation quantization) on
+    prepared weights; returns out (bf16 [M, D])."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        E, D, I = _weight_dims(w13, w2)
+        workspace = alloc_workspace_a16w4(hidden.shape[0], D, I, E, topk_ids.shape[1],
+                                          hidden.device)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_a16w4", _lib.moe_mxfp4_forward_a16w4(*args, _stream(stream)))
+    return out
+
+
+def moe_mxfp4_forward_a16w4_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w,
+                                  out=None, workspace=None, h=None, kernel_events=None,
+                                  stage1_clock=None, stream=None):
+    """A16W4 forward with exports: h (bf16 [M*topk, I], by route; a tensor to
+    fill, True to allocate one, or None), kernel_events (8 raw hipEvent_t
+    handles or None, as in moe_mxfp4_forward_profiled) and stage1_clock
+    (device int64 of 2 * a16w4_stage1_workgroups(...) or None).
+    Returns dict(out, h)."""
+    E, D, I = _weight_dims(w13, w2)
+    M, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        workspace = alloc_workspace_a16w4(M, D, I, E, topk, hidden.device)
+    if h is True:
+        h = torch.empty((max(M * topk, 1), I), dtype=torch.bfloat16, device=hidden.device)
+    hp = None
+    if h is not None:
+        if h.dtype != torch.bfloat16 or h.numel() < M * topk * I or not h.is_contiguous():
+            raise TypeError(f"h: expected a contiguous bf16 tensor of {M * topk * I} elements")
+        hp = ctypes.c_void_p(h.data_ptr())
+    ev = None
+    if kernel_events is not None:
+        if len(kernel_events) != 2 * len(LAUNCHES):
+            raise ValueError(f"kernel_events: expected {2 * len(LAUNCHES)} entries")
+        ev = (ctypes.c_void_p * len(kernel_events))(
+            *[ctypes.c_void_p(e) if e else None for e in kernel_events])
+    clk = None
+    if stage1_clock is not None:
+        need = 2 * a16w4_stage1_workgroups(M, I, E, topk)
+        if (stage1_clock.dtype != torch.int64 or stage1_clock.numel() < need
+                or not stage1_clock.is_cuda or not stage1_clock.is_contiguous()):
+            raise TypeError(f"stage1_clock: expected a contiguous device int64 tensor of {need}")
+        clk = ctypes.c_void_p(stage1_clock.data_ptr())
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_a16w4_debug",
+           _lib.moe_mxfp4_forward_a16w4_debug(*args, hp, ev, clk, _stream(stream)))
+    return {"out": out, "h": h[:M * topk] if h is not None else None}
 
 
 class MoeMxfp4:

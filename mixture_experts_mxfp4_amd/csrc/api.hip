@@ -7,7 +7,9 @@
 //     quant) -> stage 2 -> per-token slot reduction;
 //   sorted paths: prologue (route sort + activation quant) [-> sorted copy of
 //     the activations for the tiled kernels] -> stage 1 -> stage 2 -> slot
-//     reduction.
+//     reduction;
+//   A16W4 (bf16 activations, no quantization; few tokens only): the two
+//     route-indexed kernels in their bf16 mode.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -96,28 +98,41 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, expert_block0, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, expert_block0, h16, total;
 };
 
-Layout layout(int M, int D, int I, int E, int topk)
+// The A16W4 forward runs the route-indexed kernels for any routing within
+// their limits.
+bool a16w4_shape_ok(int M, int E, int topk)
+{
+    return M <= moe::kDirectMaxTokens && topk <= moe::kMaxTopkDirect &&
+           int64_t(M) * topk <= moe::kDirectMaxRoutes && E <= moe::kDirectMaxE;
+}
+
+Layout layout(int M, int D, int I, int E, int topk, bool a16 = false)
 {
     Layout L;
-    L.path = choose_path(M, E, topk);
+    L.path = a16 ? MOE_MXFP4_PATH_DIRECT : choose_path(M, E, topk);
     L.bm = choose_block_m(M, E, topk);
     L.cap = route_capacity(M, E, topk, L.bm);
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.expert_block0 = 0;
+    L.h16 = 0;
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
-        // rows indexed by route: a2 codes and scales row-major; the expert
-        // slots with their token -> route tables
+        // rows indexed by route: a2 codes and scales row-major (A16W4: h in
+        // bf16); the expert slots with their token -> route tables
         const size_t R = size_t(M) * topk;
         const size_t slots = size_t(moe::direct_slots(M, E, topk));
         L.sorted_route = L.sorted_w = L.block_expert = L.num_valid = L.a1q = L.a1s = 0;
-        L.a1f = L.a1fs = L.partial = 0;
-        L.a2q = take(R * I / 2);
-        L.a2s = take(R * I / 32);
+        L.a1f = L.a1fs = L.partial = L.a2q = L.a2s = 0;
+        if (a16) {
+            L.h16 = take(R * I * sizeof(uint16_t));
+        } else {
+            L.a2q = take(R * I / 2);
+            L.a2s = take(R * I / 32);
+        }
         L.slot_expert = take(sizeof(int32_t) * slots);
         L.slot_layers = take(sizeof(int32_t) * slots);
         L.route_of = take(sizeof(int32_t) * size_t(topk) * slots * size_t(M));
@@ -180,7 +195,8 @@ moe::KernelEvents kernel_events(const DebugOut* d, int i)
 int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
                    const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                    const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
-                   uint8_t* ws, const Layout& L, int n_cu, const DebugOut* dbg, hipStream_t stream)
+                   uint8_t* ws, const Layout& L, int n_cu, const DebugOut* dbg, bool a16,
+                   hipStream_t stream)
 {
     moe::DirectArgs a{hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ws + L.a2q,
                       ws + L.a2s, reinterpret_cast<int32_t*>(ws + L.slot_expert),
@@ -188,7 +204,8 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
                       reinterpret_cast<int32_t*>(ws + L.route_of),
                       reinterpret_cast<int32_t*>(ws + L.n_active), out,
                       dbg ? dbg->h : nullptr, M, D, I, E, topk,
-                      dbg ? dbg->stage1_clock : nullptr};
+                      dbg ? dbg->stage1_clock : nullptr,
+                      a16 ? reinterpret_cast<uint16_t*>(ws + L.h16) : nullptr};
     (void)n_cu;
     // two launches: no prologue, and the slot sum is part of stage 2
     hipError_t e = moe::launch_gemm1_direct(a, stream, kernel_events(dbg, 1));
@@ -201,11 +218,13 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
             moe::launch_direct_rows(topk_ids, R, E, dbg->sorted_route, dbg->num_valid, stream) !=
                 hipSuccess)
             return MOE_MXFP4_ERR_HIP;
-        if (dbg->a2_codes && hipMemcpyAsync(dbg->a2_codes, a.a2q, size_t(R) * I / 2,
-                                            hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        if (!a16 && dbg->a2_codes &&
+            hipMemcpyAsync(dbg->a2_codes, a.a2q, size_t(R) * I / 2, hipMemcpyDeviceToDevice,
+                           stream) != hipSuccess)
             return MOE_MXFP4_ERR_HIP;
-        if (dbg->a2_scales && hipMemcpyAsync(dbg->a2_scales, a.a2s, size_t(R) * I / 32,
-                                             hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        if (!a16 && dbg->a2_scales &&
+            hipMemcpyAsync(dbg->a2_scales, a.a2s, size_t(R) * I / 32, hipMemcpyDeviceToDevice,
+                           stream) != hipSuccess)
             return MOE_MXFP4_ERR_HIP;
     }
     return MOE_MXFP4_OK;
@@ -215,16 +234,17 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
                  const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                  const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
                  void* workspace, size_t workspace_bytes, const DebugOut* dbg,
-                 hipStream_t stream)
+                 hipStream_t stream, bool a16 = false)
 {
     int st = check_shape(M, D, I, E, topk);
     if (st) return st;
+    if (a16 && !a16w4_shape_ok(M, E, topk)) return MOE_MXFP4_ERR_UNSUPPORTED;
     if (M == 0) return MOE_MXFP4_OK;
     const void* ptrs[] = {hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace};
     for (const void* p : ptrs)
         if (!p || !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
     if (!aligned(workspace, 256)) return MOE_MXFP4_ERR_INVALID_ARG;
-    const Layout L = layout(M, D, I, E, topk);
+    const Layout L = layout(M, D, I, E, topk, a16);
     if (workspace_bytes < L.total) return MOE_MXFP4_ERR_WORKSPACE;
     int n_cu = 0;
     st = device_check(&n_cu);
@@ -233,7 +253,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (L.path == MOE_MXFP4_PATH_DIRECT)
         return forward_direct(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I,
-                              E, topk, ws, L, n_cu, dbg, stream);
+                              E, topk, ws, L, n_cu, dbg, a16, stream);
     int32_t* sorted_route = reinterpret_cast<int32_t*>(ws + L.sorted_route);
     float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
     int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
@@ -462,4 +482,37 @@ MOE_API int moe_mxfp4_forward_profiled(const uint16_t* hidden, const uint8_t* w1
     DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, kernel_events, stage1_clock};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream);
+}
+
+MOE_API size_t moe_mxfp4_a16w4_workspace_bytes(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk) || !a16w4_shape_ok(M, E, topk)) return 0;
+    return layout(M, D, I, E, topk, true).total;
+}
+
+MOE_API int moe_mxfp4_forward_a16w4(const uint16_t* hidden, const uint8_t* w13,
+                                    const uint8_t* w13_scale, const uint8_t* w2,
+                                    const uint8_t* w2_scale, const int32_t* topk_ids,
+                                    const float* topk_w, uint16_t* out, int M, int D, int I, int E,
+                                    int topk, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream)
+{
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, nullptr, stream, true);
+}
+
+MOE_API int moe_mxfp4_forward_a16w4_debug(const uint16_t* hidden, const uint8_t* w13,
+                                          const uint8_t* w13_scale, const uint8_t* w2,
+                                          const uint8_t* w2_scale, const int32_t* topk_ids,
+                                          const float* topk_w, uint16_t* out, int M, int D, int I,
+                                          int E, int topk, void* workspace,
+                                          size_t workspace_bytes, uint16_t* h,
+                                          hipEvent_t* kernel_events, uint64_t* stage1_clock,
+                                          hipStream_t stream)
+{
+    if ((h && !aligned(h, 16)) || (stage1_clock && !aligned(stage1_clock, 8)))
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    DebugOut d{nullptr, nullptr, h, nullptr, nullptr, kernel_events, stage1_clock};
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, &d, stream, true);
 }

@@ -207,7 +207,11 @@ __device__ __forceinline__ void publish_slot(const DirectArgs& a, int y, const i
 // matching up columns), all K = D, four waves splitting K as in the sorted
 // streaming kernel.  The NG groups share the route scan and each K tile's
 // activation fragment (loaded as bf16 and quantized once).
-template <int U, int NG>
+//
+// A16W4 (a.h16 set): the bf16 activations go to the bf16 matrix cores as
+// they are and each weight fragment is widened to bf16 in registers
+// (mfma_a16w4_block); h stays bf16, stored at its route in a.h16.
+template <int U, int NG, bool A16>
 __global__ void __launch_bounds__(kDirThreads)
 gemm1_direct_kernel(DirectArgs a)
 {
@@ -291,14 +295,25 @@ gemm1_direct_kernel(DirectArgs a)
                            const uint32_t (&sw)[U][NG]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                uint32_t sa;
-                const uint4 av = mx_quant_lane_block(xa[u], sa);
+                if constexpr (A16) {
 #pragma unroll
-                for (int g = 0; g < NG; ++g)
+                    for (int g = 0; g < NG; ++g)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[g][q] = mfma_fp4_16x16x128(av, b[u][g][q], acc[g][q], sa,
-                                                       (sw[u][g] >> (8 * q)) & 0xFFu);
+                        for (int q = 0; q < 4; ++q) {
+                            uint4 w[4];
+                            fp4_block_to_bf16(b[u][g][q], (sw[u][g] >> (8 * q)) & 0xFFu, w);
+                            acc[g][q] = mfma_a16w4_block(xa[u], w, acc[g][q]);
+                        }
+                } else {
+                    uint32_t sa;
+                    const uint4 av = mx_quant_lane_block(xa[u], sa);
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[g][q] = mfma_fp4_16x16x128(av, b[u][g][q], acc[g][q], sa,
+                                                           (sw[u][g] >> (8 * q)) & 0xFFu);
+                }
             }
         };
         const int nchunks = (kt_end - kt_begin + U - 1) / U;
@@ -339,6 +354,13 @@ gemm1_direct_kernel(DirectArgs a)
                 a.h_dbg[r * I + c * 32 + lane % 16] = uint16_t(h0);
                 a.h_dbg[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
             }
+            if constexpr (A16) {
+                if (row_ok) {
+                    a.h16[r * I + c * 32 + lane % 16] = uint16_t(h0);
+                    a.h16[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
+                }
+                continue;
+            }
             // the row's MXFP4 group = columns c*32..+31, held by the 16 lanes of a DPP row
             const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
             const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
@@ -366,15 +388,65 @@ gemm1_direct_kernel(DirectArgs a)
 // slot's expert (zero when there is none), shared by the NS slices.  G slots
 // x 2 K tiles are loaded before their MFMAs: G x 2 x NS KiB of weights in
 // flight per wave, 16 waves per CU (one workgroup per CU, 128 VGPRs each).
+//
+// A16W4 (a.h16 set): the h fragment of a row is 32 bf16 (64 bytes) of its
+// route's bf16 h row, and each weight fragment is widened to bf16 once per
+// slot and K tile and shared by the row tiles (mfma_a16w4_block).
 #ifndef MOE_OS_SLOTS_IN_FLIGHT
 #define MOE_OS_SLOTS_IN_FLIGHT 2
 #endif
-constexpr int kOsThreads = 1024;
+#ifndef MOE_OS_A16_SLOTS_IN_FLIGHT
+#define MOE_OS_A16_SLOTS_IN_FLIGHT 1
+#endif
+#ifndef MOE_OS_THREADS
+#define MOE_OS_THREADS 1024
+#endif
+constexpr int kOsThreads = MOE_OS_THREADS;
 constexpr int kOsWaves = kOsThreads / kWave;
 constexpr int kOsSlices = 2;
 constexpr int kOsMaxSlots = kDirectMaxTokens * kMaxTopkDirect;
 
-template <int RT, int G, int NS>
+// One row's stage-2 operand at K tile kt for route r (r < 0: none, zeros):
+// MXFP4 (16 code bytes + scale byte of 32-block kq) or, A16W4, 32 bf16.
+template <bool A16>
+struct HFrag {
+    uint4 v[A16 ? 4 : 1];
+    uint32_t s;
+};
+template <bool A16>
+__device__ __forceinline__ HFrag<A16> load_hfrag(const DirectArgs& a, int r, int kt, int kq)
+{
+    HFrag<A16> f;
+    const int I = a.I;
+    if constexpr (A16) {
+        f.s = 0u;
+        const uint8_t* p = reinterpret_cast<const uint8_t*>(a.h16 + int64_t(r) * I + kt * 128 + kq * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.v[j] = r >= 0 ? ld16(p + 16 * j) : make_uint4(0, 0, 0, 0);
+    } else {
+        f.v[0] = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + kt * 64 + kq * 16) : make_uint4(0, 0, 0, 0);
+        f.s = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + kt * 4 + kq] : 0u;
+    }
+    return f;
+}
+// acc[rt] += product of the rows' fragments f[rt] with one weight fragment
+// (16 code bytes, scale byte sb) over K tile kt
+template <bool A16, int RT>
+__device__ __forceinline__ void mfma_hfrag(const HFrag<A16> (&f)[RT], uint4 b, uint32_t sb,
+                                           v4f (&acc)[RT])
+{
+    if constexpr (A16) {
+        uint4 w[4];
+        fp4_block_to_bf16(b, sb, w);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma_a16w4_block(f[rt].v, w, acc[rt]);
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma_fp4_16x16x128(f[rt].v[0], b, acc[rt], f[rt].s, sb);
+    }
+}
+
+template <int RT, int G, int NS, bool A16, int KH = 2>
 __global__ void __launch_bounds__(kOsThreads)
 gemm2_direct_kernel(DirectArgs a)
 {
@@ -390,7 +462,7 @@ gemm2_direct_kernel(DirectArgs a)
     const int M = a.M, D = a.D, I = a.I, topk = a.topk;
     const int R = M * topk;
     const int slots = direct_slots(M, a.E, topk);
-    const int KT = I / 128;                   // even
+    const int KT = I / 128;                   // even: KH (1 or 2) K tiles per step
 
     if (threadIdx.x == 0) s_active = *a.n_active;
     for (int y = threadIdx.x; y < slots; y += kOsThreads) {
@@ -427,16 +499,17 @@ gemm2_direct_kernel(DirectArgs a)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) tmp[g][sl][rt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-        for (int kt = 0; kt < KT; kt += 2) {
-            uint4 b[G][2][NS], av[G][2][RT];
-            uint32_t sw[G][2], sa[G][2][RT];
+        for (int kt = 0; kt < KT; kt += KH) {
+            uint4 b[G][KH][NS];
+            HFrag<A16> av[G][KH][RT];
+            uint32_t sw[G][KH];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int y = y0 + g * kOsWaves;
                 const bool on = y < active;
                 const int64_t e = on ? s_e[y] : 0;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < KH; ++h) {
 #pragma unroll
                     for (int sl = 0; sl < NS; ++sl)
                         b[g][h][sl] = on ? ld16_nt(wcol + e * w_stride + int64_t(kt + h) * 4096 + sl * 1024)
@@ -450,24 +523,17 @@ gemm2_direct_kernel(DirectArgs a)
                     const int t = rt * 16 + row;
                     const int r = (on && t < M) ? s_route[y * 16 * RT + t] : -1;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        av[g][h][rt] = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + (kt + h) * 64 + kq * 16)
-                                              : make_uint4(0, 0, 0, 0);
-                        sa[g][h][rt] = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + (kt + h) * 4 + kq] : 0u;
-                    }
+                    for (int h = 0; h < KH; ++h) av[g][h][rt] = load_hfrag<A16>(a, r, kt + h, kq);
                 }
             }
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < KH; ++h)
 #pragma unroll
                     for (int sl = 0; sl < NS; ++sl)
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            tmp[g][sl][rt] = mfma_fp4_16x16x128(av[g][h][rt], b[g][h][sl], tmp[g][sl][rt],
-                                                                sa[g][h][rt],
-                                                                (sw[g][h] >> (8 * (q0 + sl))) & 0xFFu);
+                        mfma_hfrag<A16, RT>(av[g][h], b[g][h][sl], (sw[g][h] >> (8 * (q0 + sl))) & 0xFFu,
+                                            tmp[g][sl]);
         }
         // weight each token's row by its routing weight and accumulate
 #pragma unroll
@@ -504,19 +570,16 @@ gemm2_direct_kernel(DirectArgs a)
 #pragma unroll 1
             for (int kt = 0; kt < KT; ++kt) {
                 const uint32_t sw = *reinterpret_cast<const uint32_t*>(scol + e * s_stride + kt * 256);
+                HFrag<A16> av[RT];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const int t = rt * 16 + row;
-                    const int r = t < M ? tab[t] : -1;
-                    const uint4 av = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + kt * 64 + kq * 16)
-                                            : make_uint4(0, 0, 0, 0);
-                    const uint32_t sa = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + kt * 4 + kq] : 0u;
+                    av[rt] = load_hfrag<A16>(a, t < M ? tab[t] : -1, kt, kq);
+                }
 #pragma unroll
-                    for (int sl = 0; sl < NS; ++sl) {
-                        const uint4 b = ld16(wcol + e * w_stride + int64_t(kt) * 4096 + sl * 1024);
-                        tmp[sl][rt] = mfma_fp4_16x16x128(av, b, tmp[sl][rt], sa,
-                                                         (sw >> (8 * (q0 + sl))) & 0xFFu);
-                    }
+                for (int sl = 0; sl < NS; ++sl) {
+                    const uint4 b = ld16(wcol + e * w_stride + int64_t(kt) * 4096 + sl * 1024);
+                    mfma_hfrag<A16, RT>(av, b, (sw >> (8 * (q0 + sl))) & 0xFFu, tmp[sl]);
                 }
             }
 #pragma unroll
@@ -563,8 +626,13 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
     // two 64-row groups per workgroup (I is a multiple of 256: I/32 is even)
-    MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2>),
-               dim3(a.I / 64, direct_slots(a.M, a.E, a.topk)), dim3(kDirThreads), 0, stream, ev, a);
+    const dim3 grid(a.I / 64, direct_slots(a.M, a.E, a.topk));
+    if (a.h16)
+        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2, true>), grid, dim3(kDirThreads), 0,
+                   stream, ev, a);
+    else
+        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2, false>), grid, dim3(kDirThreads), 0,
+                   stream, ev, a);
     return hipGetLastError();
 }
 
@@ -573,12 +641,20 @@ hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const Ke
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
     const dim3 grid(a.D / (16 * kOsSlices));
-    if (a.M <= 16)
-        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices>), grid,
+    if (a.h16) {
+        if (a.M <= 16)
+            MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>), grid,
+                       dim3(kOsThreads), 0, stream, ev, a);
+        else
+            MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, true, 1>), grid, dim3(kOsThreads), 0,
+                       stream, ev, a);
+    } else if (a.M <= 16) {
+        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>), grid,
                    dim3(kOsThreads), 0, stream, ev, a);
-    else
-        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices>), grid, dim3(kOsThreads), 0, stream, ev,
-                   a);
+    } else {
+        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, false>), grid, dim3(kOsThreads), 0,
+                   stream, ev, a);
+    }
     return hipGetLastError();
 }
 

@@ -193,6 +193,69 @@ __device__ __forceinline__ v4f mfma_fp4_16x16x128(uint4 a, uint4 b, v4f c, uint3
                                                             int(sb));
 }
 
+// ------------------------------------------------ bf16 MFMA (A16W4) ----
+//
+// Weights stay MXFP4 in memory; with bf16 activations they are widened to
+// bf16 in registers and multiplied on the bf16 matrix cores.
+//
+// gfx950's v_cvt_scalef32_pk_bf16_fp4 turns byte SEL of `codes` (two E2M1
+// elements, the low nibble first) into a packed bf16 pair, each element's
+// value times 2^(s-127) read from the exponent field of the scale operand
+// (mx_scale_operand(s)).  The result is exact for every code and every scale
+// byte up to 252, subnormal results included; magnitudes past the bf16 range
+// (scale bytes 253..255 with large codes) become +-inf (checked on the device
+// against the definition for all 256 code bytes at scale bytes 0..255).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair_to_bf16(uint32_t codes, float scale_op)
+{
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale_op, SEL));
+}
+// 8 consecutive elements (one dword of codes) -> 8 bf16, element 0 in the low
+// half of .x
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t codes, float scale_op)
+{
+    return make_uint4(fp4_pair_to_bf16<0>(codes, scale_op), fp4_pair_to_bf16<1>(codes, scale_op),
+                      fp4_pair_to_bf16<2>(codes, scale_op), fp4_pair_to_bf16<3>(codes, scale_op));
+}
+
+// v_mfma_f32_16x16x32_bf16: lane L supplies A row L%16 / B column L%16 at K
+// elements 8*(L/16) .. +8 (8 bf16, element 0 in the low half of .x); lane L
+// receives D[4*(L/16) + i][L%16] in element i (the layout of the FP4 MFMA
+// above).
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(uint4 a, uint4 b, v4f c)
+{
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t av = {a.x, a.y, a.z, a.w}, bv = {b.x, b.y, b.z, b.w};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+}
+
+// A lane's 32-element MX block of weights (16 code bytes, scale byte
+// `scale`) -> 32 bf16 in w[0..3], 8 consecutive elements each.
+__device__ __forceinline__ void fp4_block_to_bf16(uint4 codes, uint32_t scale, uint4 (&w)[4])
+{
+    const float so = mx_scale_operand(scale);
+    w[0] = fp4x8_to_bf16x8(codes.x, so);
+    w[1] = fp4x8_to_bf16x8(codes.y, so);
+    w[2] = fp4x8_to_bf16x8(codes.z, so);
+    w[3] = fp4x8_to_bf16x8(codes.w, so);
+}
+// The A16W4 counterpart of one 16x16x128 FP4 MFMA: lane L holds its row's
+// 32 bf16 activations x[0..3] of 32-block L/16 of the K tile and the same
+// block of its weight column widened by fp4_block_to_bf16.  Four bf16
+// products cover the 128 K values: product j takes elements 8j..+8 of every
+// lane's block from both operands (the same K values on both sides; the
+// order of a sum over K is free).
+__device__ __forceinline__ v4f mfma_a16w4_block(const uint4 (&x)[4], const uint4 (&w)[4], v4f c)
+{
+    c = mfma_bf16_16x16x32(x[0], w[0], c);
+    c = mfma_bf16_16x16x32(x[1], w[1], c);
+    c = mfma_bf16_16x16x32(x[2], w[2], c);
+    return mfma_bf16_16x16x32(x[3], w[3], c);
+}
+
 // ------------------------------------------------------------- loads ----
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p)

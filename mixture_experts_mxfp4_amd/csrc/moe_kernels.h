@@ -133,6 +133,9 @@ struct DirectArgs {
     uint16_t* h_dbg;
     int M, D, I, E, topk;
     uint64_t* clk = nullptr;       // optional stage-1 span (span_begin / span_end)
+    // A16W4 mode when set: bf16 activations, no quantization; h is kept bf16
+    // here, [M*topk][I] (a2q / a2s unused)
+    uint16_t* h16 = nullptr;
 };
 hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});

@@ -73,6 +73,19 @@ class Case:
         torch.cuda.synchronize()
         return out
 
+    def run_gpu_a16w4(self, debug=False):
+        """The A16W4 forward (bf16 activations); with debug, dict(out, h)."""
+        from mixture_experts_mxfp4_amd import binding
+        d = self.device_inputs()
+        if debug:
+            r = binding.moe_mxfp4_forward_a16w4_debug(d["hidden"], *d["prepared"], d["ids"],
+                                                      d["tw"], h=True)
+            torch.cuda.synchronize()
+            return r
+        out = binding.moe_mxfp4_forward_a16w4(d["hidden"], *d["prepared"], d["ids"], d["tw"])
+        torch.cuda.synchronize()
+        return out
+
     def run_oracle(self, tokens=None, **kw):
         return oracle.forward(self.hb, *self.wq, self.ids, self.tw, tokens=tokens, **kw)
 

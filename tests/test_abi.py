@@ -117,6 +117,31 @@ def test_host_validation_without_device(binding):
     assert lib.moe_mxfp4_prepare_weights(*([ok] * 4), 2, 512, 256, *([ok] * 4), null) == 1
 
 
+def test_a16w4_sizing_and_validation(binding):
+    # bf16 h for every route plus the expert slot tables; 0 where the A16W4
+    # forward does not run (M > 32, M*topk > 1024, topk > 16) or a bad shape
+    assert binding.moe_mxfp4_a16w4_workspace_bytes(16, 7168, 256, 257, 9) >= 16 * 9 * 256 * 2
+    assert binding.moe_mxfp4_a16w4_workspace_bytes(32, 7168, 2048, 33, 9) >= 32 * 9 * 2048 * 2
+    assert binding.moe_mxfp4_a16w4_workspace_bytes(33, 7168, 256, 257, 9) == 0
+    assert binding.moe_mxfp4_a16w4_workspace_bytes(8, 512, 256, 9, 17) == 0
+    assert binding.moe_mxfp4_a16w4_workspace_bytes(16, 7000, 256, 257, 9) == 0
+    assert binding.a16w4_stage1_workgroups(16, 256, 257, 9) == 4 * 144
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    f = lib.moe_mxfp4_forward_a16w4
+    f.argtypes = binding._lib.moe_mxfp4_forward_a16w4.argtypes
+    f.restype = ctypes.c_int
+    null, ok = ctypes.c_void_p(0), ctypes.c_void_p(0x1000)
+    assert f(*([null] * 8), 4, 512, 256, 9, 3, null, 1 << 30, null) == 1      # null pointers
+    assert f(*([null] * 8), 33, 512, 256, 9, 3, null, 1 << 30, null) == 2     # M > 32
+    assert f(*([null] * 8), 0, 512, 256, 9, 3, null, 0, null) == 0            # M = 0
+    assert f(*([ok] * 8), 4, 512, 256, 9, 3, ok, 16, null) == 3               # short workspace
+    g = lib.moe_mxfp4_forward_a16w4_debug
+    g.argtypes = binding._lib.moe_mxfp4_forward_a16w4_debug.argtypes
+    g.restype = ctypes.c_int
+    odd = ctypes.c_void_p(0x1000 + 8)
+    assert g(*([ok] * 8), 4, 512, 256, 9, 3, ok, 1 << 30, odd, null, null, null) == 1
+
+
 def test_binding_refuses_wrong_dtypes(binding):
     import torch
     h = torch.zeros(2, 512, dtype=torch.float32)
