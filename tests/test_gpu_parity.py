@@ -277,6 +277,33 @@ def test_forward_route_list_long(binding, name):
     np.testing.assert_array_equal(dbg["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
 
 
+@pytest.mark.parametrize("M,k,E", [(3000, 9, 40), (5000, 9, 257), (4100, 9, 5)])
+def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
+    """Long lists sorted in chunks over several workgroups, with invalid ids,
+    repeated ids within a token and one hot expert: the forward's route list
+    is the oracle's, bit for bit."""
+    D, I = 256, 256
+    rng = np.random.default_rng(M + E)
+    ids = rng.integers(-2, E + 2, (M, k)).astype(np.int32)
+    ids[:, 0] = 0
+    ids[::3, 1] = ids[::3, 0]
+    ids[::7, -1] = 1 << 20
+    tw = rng.random((M, k)).astype(np.float32)
+    prep = binding.moe_mxfp4_prepare_weights(
+        *[torch.zeros(s, dtype=torch.uint8, device="cuda")
+          for s in ((E, 2 * I, D // 2), (E, 2 * I, D // 32), (E, D, I // 2), (E, D, I // 32))])
+    hidden = torch.zeros((M, D), dtype=torch.bfloat16, device="cuda")
+    dbg = binding.moe_mxfp4_forward_debug(hidden, *prep, torch.from_numpy(ids).cuda(),
+                                          torch.from_numpy(tw).cuda())
+    torch.cuda.synchronize()
+    want = oracle.route(ids, tw, E, dbg["block_m"])
+    n = int(want["num_valid"][0])
+    log(f"chunked route list M={M} k={k} E={E}: block_m {dbg['block_m']}, {n} sorted rows")
+    np.testing.assert_array_equal(dbg["num_valid"].cpu().numpy(), want["num_valid"])
+    np.testing.assert_array_equal(dbg["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+    assert torch.all(dbg["out"].float() == 0)
+
+
 @pytest.mark.parametrize("M,D,I,E,n_routed,seed", [
     (1, 512, 256, 9, 2, 21),          # single token (route-indexed path)
     (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
