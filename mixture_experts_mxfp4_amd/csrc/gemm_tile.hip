@@ -36,6 +36,11 @@ constexpr int kOffAS = kOffB + kTN * 64; // A scales: [row][4 B]
 constexpr int kOffBS = kOffAS + kTM * 4; // B scales: [n64 group][lane][4 slices]
 constexpr int kStageBytes = kOffBS + kTN * 4;
 constexpr int kLoadsPerStage = 5;        // global_load_lds per wave per stage
+// MFMAs of a step's second half issued before its barrier: they use only
+// fragments read in the first half (the compiler waits for just the ones each
+// needs), and keep the matrix cores busy while the waves meet; the reads of
+// the next stage come after the barrier.  Two measured best (0-4 tried).
+constexpr int kPreMfma = 2;
 // Stage-2 epilogue staging in the (then idle) ring: rows padded by 16 B so
 // that consecutive rows start 4 banks apart.
 constexpr int kPStride = kTN * 2 + 16;   // 256 bf16 output columns per row
@@ -174,12 +179,13 @@ __device__ __forceinline__ uint32_t read_sb(const uint8_t* buf, int wave_n, int 
 // One K tile (stage) per step, in two halves of eight MFMAs.  The instruction
 // stream of a step is fixed (sched_barrier fences): between the MFMAs of half 0
 // the wave issues its five loads of stage kt+3 (whose ring slot was last read
-// before the previous step's barrier) and reads half 1's fragments; then it
-// waits for its loads of stage kt+1 and joins the barrier; between the MFMAs of
-// half 1 it reads half 0 of stage kt+1.  So the matrix cores always have the
-// next MFMA queued while loads, LDS reads and the barrier are in flight.  The
-// scale words are shifted once per stage to this lane's byte pair and the MFMA
-// byte selects pick chunk and slice.
+// before the previous step's barrier) and reads half 1's fragments; it issues
+// the first kPreMfma MFMAs of half 1, waits for its LDS reads and for its loads
+// of stage kt+1, and joins the barrier; between the remaining MFMAs of half 1
+// it reads half 0 of stage kt+1.  So the matrix cores always have the next
+// MFMA queued while loads, LDS reads and the barrier are in flight.  The scale
+// words are shifted once per stage to this lane's byte pair and the MFMA byte
+// selects pick chunk and slice.
 template <bool kLoad, bool kSwap>
 __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, uint8_t* lds,
                                           uint32_t lds0, int wave, int lane, v16f acc[2][4],
@@ -213,7 +219,25 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
         if (i >= 1 && i < 7) read_frag(cur, 1, wave_m, wave_n, lane, f1, i - 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // this wave's LDS reads are done, and its loads of stage kt+1 have landed
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sb1[g] >>= 8 * ((lane >> 4) & 1);
+    auto mfma1 = [&](int i) {
+        const int mt = i >> 2, nt = i & 3;
+        if constexpr (kSwap)
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt])
+                                   : mfma_fp4_sel<0, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt]);
+        else
+            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
+                                   : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kPreMfma; ++i) {
+        mfma1(i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // this wave's LDS reads of stage kt are done, and its loads of stage kt+1
+    // have landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (kLoad) {
         wait_barrier<2 * kLoadsPerStage>();          // stages kt+2, kt+3 may be in flight
@@ -222,29 +246,27 @@ __device__ __forceinline__ void tile_step(const StageSrc& src, int KT, int kt, u
     } else {
         wait_barrier<0>();
     }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) sb1[g] >>= 8 * ((lane >> 4) & 1);
     __builtin_amdgcn_sched_barrier(0);
+    // the remaining MFMAs carry the reads of stage kt+1 (scale words first,
+    // so they have landed when the next step shifts them); after the last
+    // stage these read a ring slot whose contents go unused
+    constexpr int kSlots = 8 - kPreMfma;
+    static_assert(kSlots >= 3, "two scale-word slots and at least one fragment slot");
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int mt = i >> 2, nt = i & 3;
-        if constexpr (kSwap)
-            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt])
-                                   : mfma_fp4_sel<0, 2>(f1.b[nt], f1.a[mt], acc[mt][nt], sb1[nt >> 1], sa[mt]);
-        else
-            acc[mt][nt] = (nt & 1) ? mfma_fp4_sel<2, 2>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1])
-                                   : mfma_fp4_sel<2, 0>(f1.a[mt], f1.b[nt], acc[mt][nt], sa[mt], sb1[nt >> 1]);
-        // (after the last stage these read a ring slot whose contents go unused;
-        // the scale words first, so they have landed when the next step shifts them)
-        if (i == 0) {
+    for (int i = kPreMfma; i < 8; ++i) {
+        mfma1(i);
+        const int slot = i - kPreMfma;          // A scale words, B scale words, then fragments
+        if (slot == 0) {
             sa_next[0] = read_sa(nxt, wave_m, lane, 0);
             sa_next[1] = read_sa(nxt, wave_m, lane, 1);
         }
-        if (i == 1) {
+        if (slot == 1) {
             sb0[0] = read_sb(nxt, wave_n, lane, 0, 0);
             sb0[1] = read_sb(nxt, wave_n, lane, 0, 1);
         }
-        if (i >= 2) read_frag(nxt, 0, wave_m, wave_n, lane, f0, i - 2);
+#pragma unroll
+        for (int j = 0; j < 6; ++j)
+            if (slot >= 2 && 2 + j * (kSlots - 2) / 6 == slot) read_frag(nxt, 0, wave_m, wave_n, lane, f0, j);
         __builtin_amdgcn_sched_barrier(0);
     }
     sa[0] = sa_next[0];
