@@ -200,13 +200,24 @@ def torch_index(np_idx):
 
 # ------------------------------------------------------------- GPU leg ----
 
+def workload_of(args):
+    """The named workload, or with --shape M,E,I a DeepSeek-R1-shaped one
+    (D=7168, 8 routed ids uniform without replacement + the shared expert E-1,
+    as in the self-test generator of kernelindex submission 723815)."""
+    from mixture_experts_mxfp4_amd import inputs
+    if not args.shape:
+        return inputs.WORKLOADS[args.workload]
+    M, E, I = (int(v) for v in args.shape.split(","))
+    return inputs.Workload(f"shape_M{M}_E{E}_I{I}", M, 7168, I, E, 8, "uniform", 7)
+
+
 def run(args):
     import numpy as np
     import torch
 
     from mixture_experts_mxfp4_amd import binding, inputs
 
-    w = inputs.WORKLOADS[args.workload]
+    w = workload_of(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hidden, ids, tw = inputs.make_activations(w.M, w.D, w.E, w.n_routed, w.routing, w.seed)
@@ -479,6 +490,8 @@ def main():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
                    choices=["tiny", "decode", "small_batch", "prefill", "large_prefill"])
+    p.add_argument("--shape", metavar="M,E,I", default=None,
+                   help="a D=7168 top-9 workload of this shape instead of --workload")
     p.add_argument("--a16w4", action="store_true",
                    help="the A16W4 forward (bf16 activations; up to 32 tokens)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")

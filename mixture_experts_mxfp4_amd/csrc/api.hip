@@ -72,12 +72,17 @@ int64_t route_capacity(int M, int E, int topk, int bm)
 // Rows per expert block.  Few routes per expert (decode, E=257): 16-row
 // blocks waste the least MFMA work on padding; with tens to thousands of
 // routes per expert, larger blocks read each expert's weights fewer times.
+// From 64 routes per expert on average the LDS-tiled kernels win although
+// their 256-row blocks are then partly padding (measured at D=7168: M=512,
+// E=33, I=2048 506 -> 280 us; I=512 172 -> 131 us; M=256, E=33, I=2048
+// 326 -> 260 us); at 32-64 they lose (M=128, E=33: 91 -> 107 us; M=1024,
+// E=257 Zipf: 255 -> 431 us).
 int choose_block_m(int M, int E, int topk)
 {
     const double avg = double(M) * topk / double(E);
     if (avg < 8.0) return 16;
     if (avg < 32.0) return 32;
-    if (avg < 256.0) return 64;
+    if (avg < 64.0) return 64;
     return 256;       // LDS-tiled kernels (gemm_tile.hip)
 }
 

@@ -313,6 +313,7 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     (3, 256, 256, 2, 1, 24),          # smallest dims
     (1400, 512, 256, 5, 2, 25),       # LDS-tiled path (block_m 256), ragged blocks
     (1000, 768, 512, 3, 1, 26),       # LDS-tiled path, D not a multiple of 512
+    (200, 512, 256, 17, 8, 29),       # LDS-tiled path at ~106 routes per expert: blocks half padding
 ])
 def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
