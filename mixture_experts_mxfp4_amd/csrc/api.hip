@@ -343,7 +343,8 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
 {
     if (check_shape(M, D, I, E, topk) || M == 0) return 0;
     const Layout L = layout(M, D, I, E, topk);
-    if (L.path == MOE_MXFP4_PATH_DIRECT) return int64_t(I / 64) * moe::direct_slots(M, E, topk);
+    if (L.path == MOE_MXFP4_PATH_DIRECT)
+        return int64_t(moe::direct_stage1_x(I)) * moe::direct_slots(M, E, topk);
     if (L.path == MOE_MXFP4_PATH_TILED) return moe::tile_grid(2 * I / 256, int(L.nb));
     return int64_t(I / 32) * L.nb;
 }

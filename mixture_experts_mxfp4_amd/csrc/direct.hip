@@ -625,14 +625,13 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
 {
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
-    // two 64-row groups per workgroup (I is a multiple of 256: I/32 is even)
-    const dim3 grid(a.I / 64, direct_slots(a.M, a.E, a.topk));
+    const dim3 grid(direct_stage1_x(a.I), direct_slots(a.M, a.E, a.topk));
     if (a.h16)
-        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2, true>), grid, dim3(kDirThreads), 0,
-                   stream, ev, a);
+        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, kDirectGroups, true>), grid,
+                   dim3(kDirThreads), 0, stream, ev, a);
     else
-        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, 2, false>), grid, dim3(kDirThreads), 0,
-                   stream, ev, a);
+        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, kDirectGroups, false>), grid,
+                   dim3(kDirThreads), 0, stream, ev, a);
     return hipGetLastError();
 }
 

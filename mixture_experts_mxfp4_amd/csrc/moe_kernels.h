@@ -114,6 +114,13 @@ constexpr int kDirectMaxTokens = 32;
 constexpr int kMaxTopkDirect = 16;
 constexpr int kDirectMaxRoutes = 1024;
 constexpr int kDirectMaxE = 1024;
+#ifndef MOE_G1_GROUPS
+#define MOE_G1_GROUPS 2
+#endif
+// 64-row gate_up groups per stage-1 workgroup of the route-indexed path, and
+// the stage-1 grid's x extent (2I/64 groups; I is a multiple of 256)
+constexpr int kDirectGroups = MOE_G1_GROUPS;
+__host__ __device__ inline int direct_stage1_x(int I) { return I / (32 * kDirectGroups); }
 // expert slots: min(E, M*topk), an upper bound of the active experts
 __host__ __device__ inline int direct_slots(int M, int E, int topk)
 {
