@@ -29,6 +29,11 @@ Helper modes (used to make the committed rocprofv3 summaries):
                                profiles/<kernel>_<workload>_hbm_traffic.txt
                                format) from FETCH_SIZE / WRITE_SIZE passes of
                                the workload and of --copy-calibration
+    --mfma-summary WORKLOAD PMC_DIR
+                               print the MFMA counter summary of both GEMM
+                               stages (profiles/<kernel>_<workload>_mfma.txt)
+                               from a `--pmc SQ_INSTS_VALU_MFMA_MOPS_F6F4
+                               MfmaUtil` pass of the workload
 """
 import argparse
 import csv
@@ -483,6 +488,53 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
     print(f"traffic_bytes_per_launch: {traffic:.0f}")
 
 
+def _pmc_rows(d, kernel_prefix):
+    """Per-dispatch counter rows of the kernels whose name starts with the prefix."""
+    out = {}
+    for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+        name = r.get("Kernel_Name", "").replace("void ", "")
+        if name.startswith(kernel_prefix):
+            key = (r["Dispatch_Id"], int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+            out.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def mfma_summary(workload, pmc_dir):
+    """FP4 MFMA work the hardware counted (SQ_INSTS_VALU_MFMA_MOPS_F6F4 x 512
+    FLOP) and the MFMA busy share (MfmaUtil) per dispatch of both GEMM
+    stages, against the algorithmic FLOPs of the valid routes."""
+    import numpy as np
+
+    from mixture_experts_mxfp4_amd import binding, inputs
+    w = inputs.WORKLOADS[workload]
+    path_name = binding.PATH_NAMES[binding.moe_mxfp4_path(w.M, w.D, w.I, w.E, w.topk)]
+    _, ids, _ = inputs.make_activations(w.M, w.D, w.E, w.n_routed, w.routing, w.seed)
+    alg = algorithmic(w, ids.numpy())
+    kernel1, _ = STAGE1[path_name]
+    kernel2 = kernel1.replace("gemm1", "gemm2").replace("_swiglu_quant", "_simple")
+    print(f"# FP4 MFMA counters of the {workload} workload (path {path_name}), per dispatch")
+    print(f"# issued = SQ_INSTS_VALU_MFMA_MOPS_F6F4 x 512 FLOP; busy = MfmaUtil (MFMA busy cycles")
+    print(f"# over active cycles x SIMDs); durations from the same counter run (kernels serialized)")
+    print(f"workload: {workload}")
+    print(f"stage1_source_sha256_16: {source_hash(STAGE1[path_name][1])}")
+    for stage, kernel, fl in (("stage1", kernel1, alg["stage1_flops"]),
+                              ("stage2", kernel2, alg["flops"] - alg["stage1_flops"])):
+        rows = _pmc_rows(pmc_dir, "moe::" + kernel)
+        if not rows:
+            continue
+        mops = np.mean([v.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0) for v in rows.values()])
+        util = np.mean([v.get("MfmaUtil", 0.0) for v in rows.values()])
+        dur = np.mean([(k[2] - k[1]) * 1e-9 for k in rows])
+        issued = mops * 512.0
+        print(f"{stage}_kernel: {kernel}  ({len(rows)} dispatches)")
+        print(f"{stage}_issued_flop_per_dispatch: {issued:.4e}")
+        print(f"{stage}_algorithmic_flop: {fl:.4e}")
+        print(f"{stage}_issued_over_algorithmic: {issued / fl:.3f}")
+        print(f"{stage}_mfma_busy_pct: {util:.1f}")
+        print(f"{stage}_duration_us_counter_run: {dur * 1e6:.1f}")
+        print(f"{stage}_issued_tflops_counter_run: {issued / dur / 1e12:.1f}")
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -499,6 +551,7 @@ def main():
     p.add_argument("--cpu-sample-s", type=float, default=16.0,
                    help="CPU-seconds of oracle work in the baseline sample")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--mfma-summary", nargs=2, metavar=("WORKLOAD", "PMC_DIR"))
     p.add_argument("--summarize-stats", metavar="DIR")
     p.add_argument("--summarize-pmc", metavar="DIR")
     p.add_argument("--traffic-summary", nargs=5,
@@ -506,6 +559,8 @@ def main():
     args = p.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.mfma_summary:
+        return mfma_summary(*args.mfma_summary)
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats)
     if args.summarize_pmc:
