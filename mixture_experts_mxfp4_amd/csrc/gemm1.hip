@@ -10,9 +10,9 @@
 // exactly as the inter-stage quant of 754773 does, so stage 2 reads FP4.
 //
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows (one
-// expert) and one 64-row group of the prepared gate_up weight = 32 gate + 32
-// up columns = one MXFP4 group of h.  The four waves split the K dimension;
-// each wave runs RT x 4 MFMA tiles of 16x16x128, streaming its weight
+// expert) and NG 64-row groups of the prepared gate_up weight; a group is 32
+// gate + 32 up columns = one MXFP4 group of h.  The four waves split the K
+// dimension; each wave runs NG x RT x 4 MFMA tiles of 16x16x128, streaming its weight
 // fragments (1 KiB each, contiguous) with non-temporal loads and gathering the
 // block's activation rows by token id.  Partial sums meet in LDS; the epilogue
 // quantizes h with cross-lane reductions and writes it in sorted-row order in
@@ -27,12 +27,13 @@ namespace moe {
 constexpr int kGemmThreads = 256;
 
 // Loads of U consecutive K tiles are issued before their MFMAs so that every
-// wave keeps U x 4 KiB of weight fragments in flight.
-template <int RT>
-constexpr int g1_unroll() { return RT <= 2 ? 4 : 2; }
+// wave keeps U x NG x 4 KiB of weight fragments in flight (U = 2 at 64-row
+// blocks with two groups would spill).
+template <int RT, int NG>
+constexpr int g1_unroll() { return NG == 1 ? (RT <= 2 ? 4 : 2) : (RT <= 2 ? 2 : 1); }
 
-template <int RT>
-__global__ void __launch_bounds__(kGemmThreads)
+template <int RT, int NG>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
                           const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
                           const int32_t* __restrict__ sorted_route,
@@ -42,10 +43,10 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                           int I, int topk, int64_t cap, uint64_t* clk)
 {
     constexpr int BM = 16 * RT;
-    constexpr int U = g1_unroll<RT>();
+    constexpr int U = g1_unroll<RT, NG>();
     __shared__ float red[4][RT][4][4][kWave];   // [wave][row tile][slice][i][lane]
 
-    const int c = blockIdx.x;          // MXFP4 group of h = 64-row group of w13p
+    const int c0 = blockIdx.x * NG;    // first MXFP4 group of h = 64-row group of w13p
     const int blk = blockIdx.y;
     span_begin(clk);
     const int e = block_expert[blk];       // -1 past the used blocks
@@ -69,25 +70,32 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
         a_ptr[rt] = a1q + tok * a_row + (lane / 16) * 16;
         as_ptr[rt] = a1s + tok * as_row;
     }
-    const uint8_t* wb = w13p + int64_t(e) * I * D + int64_t(c) * KT * 4096 + lane * 16;
-    const uint8_t* sb = w13sp + int64_t(e) * I * D / 16 + int64_t(c) * KT * 256 + lane * 4;
+    // the NG consecutive groups' weight fragments and scale words
+    const uint8_t* wb = w13p + int64_t(e) * I * D + int64_t(c0) * KT * 4096 + lane * 16;
+    const uint8_t* sb = w13sp + int64_t(e) * I * D / 16 + int64_t(c0) * KT * 256 + lane * 4;
     const int ash = 8 * (lane / 16);     // this lane's 32-block inside an A scale word
 
-    v4f acc[RT][4];
+    v4f acc[NG][RT][4];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[g][rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto steps = [&](auto u_const, int kt) {
         constexpr int UU = decltype(u_const)::value;
-        uint32_t sw[UU], sa[UU][RT];
-        uint4 b[UU][4], a[UU][RT];
+        uint32_t sw[UU][NG], sa[UU][RT];
+        uint4 b[UU][NG][4], a[UU][RT];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
-            sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) b[u][q] = ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024);
+            for (int g = 0; g < NG; ++g) {
+                sw[u][g] = *reinterpret_cast<const uint32_t*>(sb + int64_t(g) * KT * 256 + (kt + u) * 256);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    b[u][g][q] = ld16_nt(wb + (int64_t(g) * KT + kt + u) * 4096 + q * 1024);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 sa[u][rt] = ok[rt] ? *reinterpret_cast<const uint32_t*>(as_ptr[rt] + (kt + u) * 4) : 0u;
@@ -97,12 +105,14 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 #pragma unroll
         for (int u = 0; u < UU; ++u)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[rt][q] = mfma_fp4_16x16x128(a[u][rt], b[u][q], acc[rt][q],
-                                                    (sa[u][rt] >> ash) & 0xFFu,
-                                                    (sw[u] >> (8 * q)) & 0xFFu);
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[g][rt][q] = mfma_fp4_16x16x128(a[u][rt], b[u][g][q], acc[g][rt][q],
+                                                           (sa[u][rt] >> ash) & 0xFFu,
+                                                           (sw[u][g] >> (8 * q)) & 0xFFu);
     };
     const int kt1 = (wave + 1) * KT / 4;
     int kt = wave * KT / 4;
@@ -110,41 +120,46 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     for (; kt < kt1; ++kt) steps(std::integral_constant<int, 1>{}, kt);
 
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int g = 0; g < NG; ++g) {
+        const int c = c0 + g;
+        if (g > 0) __syncthreads();        // red is reused group by group
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][rt][q][i][lane] = acc[rt][q][i];
-    __syncthreads();
-
-    for (int rt = wave; rt < RT; rt += 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float s4[4];
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                s4[q] = red[0][rt][q][i][lane] + red[1][rt][q][i][lane] +
-                        red[2][rt][q][i][lane] + red[3][rt][q][i][lane];
-            // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
-            const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
-            const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
-            const int row = 4 * (lane / 16) + i;                     // row within the tile
-            const int64_t srow = int64_t(blk) * BM + rt * 16 + row;  // sorted row
-            if (h_dbg) {
-                h_dbg[srow * I + c * 32 + lane % 16] = uint16_t(h0);
-                h_dbg[srow * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
-            }
-            // MXFP4 group = the 32 columns held by the 16 lanes of this row
-            // (one DPP row): columns lane%16 (h0) and 16 + lane%16 (h1)
-            const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
-            const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
-            const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
-            const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
-            const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
-            if (lane % 16 == 0) {
-                *reinterpret_cast<uint4*>(a2q + frag_code_off(srow, c / 4, c % 4, I / 128)) =
-                    make_uint4(qlo, d1, qhi, d3);
-                a2s[frag_scale_off(srow, c / 4, cap) + c % 4] = uint8_t(s);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[wave][rt][q][i][lane] = acc[g][rt][q][i];
+        __syncthreads();
+
+        for (int rt = wave; rt < RT; rt += 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    s4[q] = red[0][rt][q][i][lane] + red[1][rt][q][i][lane] +
+                            red[2][rt][q][i][lane] + red[3][rt][q][i][lane];
+                // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
+                const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
+                const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
+                const int row = 4 * (lane / 16) + i;                     // row within the tile
+                const int64_t srow = int64_t(blk) * BM + rt * 16 + row;  // sorted row
+                if (h_dbg) {
+                    h_dbg[srow * I + c * 32 + lane % 16] = uint16_t(h0);
+                    h_dbg[srow * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
+                }
+                // MXFP4 group = the 32 columns held by the 16 lanes of this row
+                // (one DPP row): columns lane%16 (h0) and 16 + lane%16 (h1)
+                const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
+                const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
+                const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
+                const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
+                const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
+                if (lane % 16 == 0) {
+                    *reinterpret_cast<uint4*>(a2q + frag_code_off(srow, c / 4, c % 4, I / 128)) =
+                        make_uint4(qlo, d1, qhi, d3);
+                    a2s[frag_scale_off(srow, c / 4, cap) + c % 4] = uint8_t(s);
+                }
             }
         }
     }
@@ -154,7 +169,8 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 template <int RT>
 static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT>), dim3(a.I / 32, a.nb_cap), dim3(kGemmThreads), 0,
+    constexpr int NG = stream_stage1_groups(16 * RT);
+    MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT, NG>), dim3(a.I / (32 * NG), a.nb_cap), dim3(kGemmThreads), 0,
                stream, ev, a.a1q, a.a1s, a.w13p, a.w13sp, a.sorted_route, a.block_expert,
                a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M, a.D, a.I, a.topk, a.cap, a.clk);
     return hipGetLastError();

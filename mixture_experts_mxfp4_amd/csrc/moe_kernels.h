@@ -82,6 +82,20 @@ struct Gemm1Args {
     const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
+#ifndef MOE_G1S_GROUPS
+#define MOE_G1S_GROUPS 2
+#endif
+#ifndef MOE_G1S_GROUPS32
+#define MOE_G1S_GROUPS32 2
+#endif
+// 64-row gate_up groups per workgroup of the streaming stage 1 (grid: I/32 /
+// groups x blocks).  Two groups halve the activation rows each weight byte
+// pays for; at 16-row blocks the gather is small and the wider grid wins.
+// I is a multiple of 256, so I/32 divides by 2.
+constexpr int stream_stage1_groups(int block_m)
+{
+    return block_m == 64 ? MOE_G1S_GROUPS : block_m == 32 ? MOE_G1S_GROUPS32 : 1;
+}
 
 
 struct Gemm2Args {
