@@ -109,20 +109,63 @@ def bf16_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
-def check_close(gpu_bits, oracle_bits, what=""):
+def requant_slack(case, dbg):
+    """Output slack explained by requant codes that differ from the oracle's.
+
+    Stage 1 accumulates in fp32 and the oracle in fp64, so a bf16 h may differ
+    by an ulp; where that ulp straddles a rounding midpoint of the E2M1 grid
+    (or a power of two of the block maximum) the requantized code moves by a
+    whole grid step, up to a third of the block maximum.  Both codes are the
+    correct quantization of their own h (the GPU's is checked bit for bit
+    against the oracle quantizer applied to the GPU h, and the GPU h against
+    the oracle's h, in _check_intermediates), so the output may differ from the
+    oracle's by what the step carries through stage 2:
+    slack[t, d] = sum over the token's routes of |w| * sum_i |dv_i| * |W2[e][d, i]|,
+    dv the difference of the dequantized codes.  Returns (slack [M, D] or None,
+    number of differing h elements, number of h elements)."""
+    sr = dbg["sorted_route"].cpu().numpy()
+    n = int(dbg["num_valid"].cpu().numpy()[0])
+    R = case.M * case.topk
+    rows = np.nonzero(sr[:n] < R)[0]
+    r = sr[rows]
+    if rows.size == 0:
+        return None, 0, 0
+    t, s = r // case.topk, r % case.topk
+    _, h_or = case.run_oracle(want_h=True)
+    oc, os_ = oracle.quantize_rows(h_or[t, s])
+    gc = dbg["a2_codes"].cpu().numpy()[rows]
+    gs = dbg["a2_scales"].cpu().numpy()[rows]
+    dv = np.abs(oracle.dequantize_rows(gc, gs) - oracle.dequantize_rows(oc, os_))
+    moved = np.nonzero(dv.max(axis=1) > 0)[0]
+    if moved.size == 0:
+        return None, 0, dv.size
+    slack = np.zeros((case.M, case.D))
+    experts = case.ids[t[moved], s[moved]]
+    for e in np.unique(experts):
+        w2 = np.abs(oracle.dequantize_rows(case.wq[2][e], case.wq[3][e]))    # [D, I]
+        for j in moved[experts == e]:
+            slack[t[j]] += abs(float(case.tw[t[j], s[j]])) * (w2 @ dv[j])
+    return slack, int(np.count_nonzero(dv)), dv.size
+
+
+def check_close(gpu_bits, oracle_bits, what="", slack=None):
     """The end-to-end tolerance: |gpu - oracle| <= 2e-2 * rms(oracle) + 2^-7 * |oracle|
-    on >= 99.9% of the elements, and no element beyond 0.1 * rms(oracle)."""
+    on >= 99.9% of the elements, and no element beyond 0.1 * rms(oracle); with
+    `slack` (requant_slack), each element's bound grows by its slack."""
     g = bf16_to_f64(gpu_bits)
     o = bf16_to_f64(oracle_bits)
     assert g.shape == o.shape
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     rms = float(np.sqrt(np.mean(o * o)))
     err = np.abs(g - o)
-    bound = 2e-2 * rms + 2.0 ** -7 * np.abs(o)
+    extra = 0.0 if slack is None else slack
+    bound = 2e-2 * rms + 2.0 ** -7 * np.abs(o) + extra
     frac = float(np.mean(err <= bound))
-    worst = float(err.max()) if err.size else 0.0
+    over = err - extra
+    worst = float(over.max()) if err.size else 0.0
     log(f"{what}: rms={rms:.4g} within-bound={frac * 100:.4f}% worst={worst / max(rms, 1e-30):.4g}*rms "
-        f"exact-bf16={float(np.mean(g == o)) * 100:.2f}%")
+        f"exact-bf16={float(np.mean(g == o)) * 100:.2f}%"
+        + ("" if slack is None else f" slack on {int(np.count_nonzero(slack.max(axis=1)))} tokens"))
     assert frac >= 0.999, f"{what}: only {frac:.5f} of elements within tolerance"
     assert worst <= 0.1 * rms, f"{what}: worst error {worst} > 0.1*rms ({rms})"
     return frac, worst / max(rms, 1e-30)

@@ -3,7 +3,9 @@
 Bit-exact: MXFP4 codes/scales (activation quantizer, fused stage-1 requant),
 route lists, weight preparation.  Floating point: the end-to-end tolerance
 |gpu - oracle| <= 2e-2 rms + 2^-7 |oracle| on >= 99.9 % of elements, none
-beyond 0.1 rms.
+beyond 0.1 rms.  Where the debug outputs are at hand, the bound of a token also
+allows for stage-1 requant codes that sit one E2M1 grid step from the oracle's
+because the two h differ by an ulp at a rounding midpoint (requant_slack).
 """
 import numpy as np
 import pytest
@@ -11,7 +13,8 @@ import torch
 
 import oracle
 from mixture_experts_mxfp4_amd import inputs
-from tests.moe_cases import Case, bf16_to_f64, check_close, custom_case, log, workload_case
+from tests.moe_cases import (Case, bf16_to_f64, check_close, custom_case, log, requant_slack,
+                             workload_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -233,12 +236,21 @@ def _check_intermediates(case, dbg):
     np.testing.assert_array_equal(dbg["a2_codes"].cpu().numpy()[valid], codes)
 
 
+def _check_forward(case, dbg, what):
+    """Intermediates first (h, bit-exact requant of the GPU h), then the output
+    with the slack of requant codes one grid step from the oracle's (rare: at
+    most one h element in a thousand)."""
+    _check_intermediates(case, dbg)
+    slack, moved, total = requant_slack(case, dbg)
+    log(f"{what}: requant codes one grid step from the oracle's: {moved} of {total}")
+    assert moved <= 1e-3 * total
+    out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(out, case.run_oracle(), what, slack=slack)
+
+
 def test_forward_tiny_full_and_intermediates(binding):
     case = workload_case("tiny")
-    dbg = case.run_gpu(debug=True)
-    out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
-    check_close(out, case.run_oracle(), "tiny")
-    _check_intermediates(case, dbg)
+    _check_forward(case, case.run_gpu(debug=True), "tiny")
 
 
 @pytest.mark.parametrize("name,n_sample", [("decode", 16), ("small_batch", 24),
@@ -318,10 +330,7 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
 def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
     case = custom_case(M, D, I, E, n_routed, seed)
-    dbg = case.run_gpu(debug=True)
-    out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
-    check_close(out, case.run_oracle(), f"shape M={M} D={D} I={I} E={E}")
-    _check_intermediates(case, dbg)
+    _check_forward(case, case.run_gpu(debug=True), f"shape M={M} D={D} I={I} E={E}")
 
 
 @pytest.mark.parametrize("M,E", [(20, 6), (8, 40)])      # sorted and route-indexed paths
@@ -336,6 +345,23 @@ def test_forward_invalid_and_duplicate_ids(binding, M, E):
     case = custom_case(M, D, I, E, 2, 31, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
     out = case.run_gpu().cpu().view(torch.int16).numpy().view(np.uint16)
     check_close(out, case.run_oracle(), "invalid/duplicate ids")
+
+
+def test_forward_tiled_invalid_and_duplicate_ids(binding):
+    """The LDS-tiled path (block_m 256, chunked sort) with invalid and repeated
+    ids: an expert's valid routes decide which of its rows are computed."""
+    M, D, I, E = 1100, 512, 256, 5
+    rng = np.random.default_rng(41)
+    ids = rng.integers(0, E, (M, 4)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]            # duplicate slot
+    ids[::2, 2] = -1                 # invalid
+    ids[1::4, 3] = E + 3             # invalid
+    ids[::5, 3] = E - 1              # one expert with more routes
+    tw = rng.random((M, 4)).astype(np.float32)
+    case = custom_case(M, D, I, E, 2, 43, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
+    dbg = case.run_gpu(debug=True)
+    assert dbg["block_m"] == 256
+    _check_forward(case, dbg, "tiled invalid/duplicate ids")
 
 
 def test_forward_all_tokens_one_expert(binding):
