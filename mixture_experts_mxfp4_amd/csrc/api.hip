@@ -103,7 +103,7 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, expert_block0, h16, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, total;
 };
 
 // The A16W4 forward runs the route-indexed kernels for any routing within
@@ -123,7 +123,7 @@ Layout layout(int M, int D, int I, int E, int topk, bool a16 = false)
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.expert_block0 = 0;
+    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.block_info = 0;
     L.h16 = 0;
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
         // rows indexed by route: a2 codes and scales row-major (A16W4: h in
@@ -150,7 +150,7 @@ Layout layout(int M, int D, int I, int E, int topk, bool a16 = false)
     L.sorted_w = take(sizeof(float) * size_t(L.cap));
     L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
     L.num_valid = take(sizeof(int32_t) * 4);
-    L.expert_block0 = take(sizeof(int32_t) * (size_t(E) + 1));
+    L.block_info = take(sizeof(int32_t) * 4 * size_t(L.nb));
     L.a1q = take(size_t(M) * D / 2);
     L.a1s = take(size_t(M) * D / 32);
     // sorted fragment-layout copy of a1, only for the tiled kernels
@@ -263,7 +263,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
     int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
     int32_t* num_valid = reinterpret_cast<int32_t*>(ws + L.num_valid);
-    int32_t* expert_block0 = reinterpret_cast<int32_t*>(ws + L.expert_block0);
+    int32_t* block_info = reinterpret_cast<int32_t*>(ws + L.block_info);
     uint8_t* a1q = ws + L.a1q;
     uint8_t* a1s = ws + L.a1s;
     uint8_t* a1f = ws + L.a1f;
@@ -278,7 +278,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
                          block_expert, num_valid, hidden, D, a1q, a1s,
-                         reinterpret_cast<int32_t*>(ws + L.chunk_counts), expert_block0};
+                         reinterpret_cast<int32_t*>(ws + L.chunk_counts), block_info};
     const moe::KernelEvents ev0 = kernel_events(dbg, 0);
     hipError_t e = moe::launch_prologue(pa, n_cu, stream,
                                         tile ? moe::KernelEvents{ev0.start, nullptr} : ev0);
@@ -289,13 +289,13 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
                       a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap,
-                      dbg ? dbg->stage1_clock : nullptr, expert_block0};
+                      dbg ? dbg->stage1_clock : nullptr, block_info};
     const moe::KernelEvents ev1 = kernel_events(dbg, 1);
     e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      partial, M, D, I, topk, L.bm, nb, L.cap, expert_block0};
+                      partial, M, D, I, topk, L.bm, nb, L.cap, block_info};
     const moe::KernelEvents ev2 = kernel_events(dbg, 2);
     e = tile ? moe::launch_gemm2_tile(g2, stream, ev2) : moe::launch_gemm2(g2, stream, ev2);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;

@@ -110,9 +110,8 @@ struct TileArgs {
     const uint8_t* wsp;        // prepared weight scales
     const int32_t* sorted_route;
     const float* sorted_w;
-    const int32_t* block_expert;
     const int32_t* num_valid;
-    const int32_t* expert_block0;   // [E+1] first block of each expert, then the used blocks
+    const int4* block_info;    // per used block: expert, its first block, block count, routes
     int M, topk, N, K;         // N, K of one expert's weight matrix
     int64_t cap;               // rows of the sorted fragment-layout operands
     uint8_t* a2q;              // stage 1 outputs
@@ -342,12 +341,9 @@ __device__ __forceinline__ void tile_mainloop_idle(const StageSrc& src, int KT, 
     }
 }
 
-// Whether this wave's 64 rows of block blk hold any route (wave-uniform).
-__device__ __forceinline__ bool rows_in_use(const TileArgs& p, int blk, int wave_m)
-{
-    const int sr = __builtin_amdgcn_readfirstlane(p.sorted_route[int64_t(blk) * kTM + wave_m * 64]);
-    return sr < p.M * p.topk;
-}
+// Whether this wave's 64 rows of a block with `valid` routes hold any route
+// (an expert's routes fill its segment first, padding comes last).
+__device__ __forceinline__ bool rows_in_use(int valid, int wave_m) { return valid > wave_m * 64; }
 
 __device__ __forceinline__ void zero_acc(v16f acc[2][4])
 {
@@ -422,28 +418,31 @@ __device__ __forceinline__ void xcd_share(const TileArgs& p, int n_tiles, int64_
     hi = used * (xcd + 1) / kXcds;
 }
 
-// Column tile, block and expert of tile t of the order above.
+// Column tile, block, expert and the block's number of routes for tile t of
+// the order above: one 16-byte record of the sort (tiles t of an expert's
+// n_tiles * nb run lie within its blocks' records).
 __device__ __forceinline__ void tile_at(const TileArgs& p, int n_tiles, int64_t t, int& ntile,
-                                        int& blk, int& e)
+                                        int& blk, int& e, int& valid)
 {
-    e = p.block_expert[t / n_tiles];
-    const int first = p.expert_block0[e];
-    const int nb = p.expert_block0[e + 1] - first;
+    const int4 bi = p.block_info[t / n_tiles];
+    e = bi.x;
+    const int first = bi.y, nb = bi.z;
     const int local = int(t - int64_t(n_tiles) * first);
     ntile = local / nb;
     blk = first + local % nb;
+    valid = min(kTM, bi.w - (blk - first) * kTM);
 }
 
-// Column tile, block and expert of this workgroup (one tile per workgroup);
-// false past the used tiles.
+// Column tile, block, expert and valid rows of this workgroup (one tile per
+// workgroup); false past the used tiles.
 __device__ __forceinline__ bool tile_of(const TileArgs& p, int n_tiles, int& ntile, int& blk,
-                                        int& e)
+                                        int& e, int& valid)
 {
     int64_t lo, hi;
     int j;
     xcd_share(p, n_tiles, lo, hi, j);
     if (lo + j >= hi) return false;
-    tile_at(p, n_tiles, lo + j, ntile, blk, e);
+    tile_at(p, n_tiles, lo + j, ntile, blk, e, valid);
     return true;
 }
 
@@ -454,8 +453,8 @@ gemm1_tile_kernel(TileArgs p, int I)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     span_begin(p.clk);
-    int ntile, blk, e;
-    if (!tile_of(p, p.N / kTN, ntile, blk, e)) {
+    int ntile, blk, e, valid;
+    if (!tile_of(p, p.N / kTN, ntile, blk, e, valid)) {
         span_end(p.clk);
         return;
     }
@@ -469,7 +468,7 @@ gemm1_tile_kernel(TileArgs p, int I)
 
     v16f acc[2][4];
     zero_acc(acc);
-    if (rows_in_use(p, blk, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
+    if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
     else tile_mainloop_idle(src, p.K / 128, lds);
 
     // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
@@ -547,8 +546,8 @@ gemm2_tile_kernel(TileArgs p)
     __shared__ int32_t s_route[kTM];
     __shared__ float s_w[kTM];
     span_begin(p.clk);
-    int ntile, blk, e;
-    if (!tile_of(p, p.N / kTN, ntile, blk, e)) {
+    int ntile, blk, e, valid;
+    if (!tile_of(p, p.N / kTN, ntile, blk, e, valid)) {
         span_end(p.clk);
         return;
     }
@@ -556,19 +555,22 @@ gemm2_tile_kernel(TileArgs p)
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const int R = p.M * p.topk;
     const int D = p.N;
-    if (tid < kTM) {
-        s_route[tid] = p.sorted_route[blk * kTM + tid];
-        s_w[tid] = p.sorted_w[blk * kTM + tid];
-    }
-    __syncthreads();
+    // the rows' routes and weights travel in registers through the main loop
+    // (nothing waits for them before the first K stages are requested)
+    const int my_route = tid < kTM ? p.sorted_route[blk * kTM + tid] : R;
+    const float my_w = tid < kTM ? p.sorted_w[blk * kTM + tid] : 0.f;
     StageSrc src;
     a_sources(p, blk, src);
     b_sources(p, e, ntile, src);
 
     v16f acc[2][4];
     zero_acc(acc);
-    if (rows_in_use(p, blk, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
+    if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
     else tile_mainloop_idle(src, p.K / 128, lds);
+    if (tid < kTM) {
+        s_route[tid] = my_route;
+        s_w[tid] = my_w;
+    }
 
     // Epilogue: the routing weight times the sum, rounded to bf16, goes through
     // LDS as the 256 x 256 tile; then each half-wave stores one row's 512
@@ -620,9 +622,9 @@ hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const Kerne
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || (2 * a.I) % kTN != 0) return hipErrorInvalidValue;
-    if (!a.expert_block0) return hipErrorInvalidValue;
-    TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.block_expert,
-               a.num_valid, a.expert_block0, a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s,
+    if (!a.block_info) return hipErrorInvalidValue;
+    TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.num_valid,
+               reinterpret_cast<const int4*>(a.block_info), a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s,
                a.h_dbg, nullptr, a.clk};
     MOE_LAUNCH(gemm1_tile_kernel, dim3(tile_grid(2 * a.I / kTN, a.nb_cap)), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
@@ -633,9 +635,9 @@ hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const Kerne
 {
     if (a.nb_cap == 0) return hipSuccess;
     if (a.block_m != kTM || a.D % kTN != 0) return hipErrorInvalidValue;
-    if (!a.expert_block0) return hipErrorInvalidValue;
-    TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.block_expert,
-               a.num_valid, a.expert_block0, a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr,
+    if (!a.block_info) return hipErrorInvalidValue;
+    TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.num_valid,
+               reinterpret_cast<const int4*>(a.block_info), a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr,
                nullptr, a.partial, a.clk};
     MOE_LAUNCH(gemm2_tile_kernel, dim3(tile_grid(a.D / kTN, a.nb_cap)), dim3(kTThreads),
                uint32_t(tile_lds_bytes()), stream, ev, p);

@@ -47,7 +47,9 @@ struct PrologueArgs {
     int D;
     uint8_t *a1q, *a1s;
     int32_t* chunk_counts;         // [route_chunks][E] for long lists (else unused)
-    int32_t* expert_block0;        // [E+1]: first block of each expert, then the used blocks
+    // [nb_cap][4], per used block: its expert, the expert's first block, its
+    // number of blocks and its number of routes (tiled kernels; may be null)
+    int32_t* block_info;
 };
 // Chunks of the two-launch route sort for this many routes (0: one workgroup).
 int route_chunks(int M, int topk);
@@ -79,7 +81,7 @@ struct Gemm1Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
     uint64_t* clk = nullptr;       // optional kernel span (span_begin / span_end)
-    const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
+    const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 #ifndef MOE_G1S_GROUPS
@@ -106,7 +108,7 @@ struct Gemm2Args {
     uint16_t* partial;          // bf16 [M*topk][D], weighted contribution per route
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
-    const int32_t* expert_block0 = nullptr;   // [E+1] (tiled kernels)
+    const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
     uint64_t* clk = nullptr;       // optional workgroup spans (tiled kernel)
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});

@@ -72,30 +72,51 @@ __device__ __forceinline__ void fill_padding(int R, int bm, int nb_cap,
     for (int b = b0 + threadIdx.x; b < b1; b += kPrologueThreads) block_expert[b] = -1;
 }
 
-// Per-wave histograms of the routes [c0, c1): each wave takes a contiguous
-// sub-range, 64 routes at a time; lanes holding the same expert are found
-// with ballots over the bits of the id, and the lowest such lane adds their
-// number to the wave's row cnt[wave * E + id] (no atomics).
+// Each wave of a workgroup takes a contiguous sub-range [w_begin, w_end) of
+// the routes [c0, c1), kWave * U routes per batch; the first batch is loaded
+// by the caller ahead of the work that can overlap its latency.
+__device__ __forceinline__ void wave_range(int c0, int c1, int& w_begin, int& w_end)
+{
+    const int per_wave = (c1 - c0 + kRouteWaves - 1) / kRouteWaves;
+    w_begin = min(c1, c0 + int(threadIdx.x / kWave) * per_wave);
+    w_end = min(c1, w_begin + per_wave);
+}
+
 template <int U>
-__device__ __forceinline__ void wave_histograms(const int32_t* __restrict__ ids, int c0, int c1,
-                                                int E, int nbits, int32_t* cnt)
+__device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int base, int w_end,
+                                           int (&id)[U])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = base + u * kWave + int(threadIdx.x % kWave);
+        id[u] = r < w_end ? ids[r] : -1;
+    }
+}
+
+// Per-wave histograms of the wave's routes: lanes holding the same expert are
+// found with ballots over the bits of the id, and the lowest such lane adds
+// their number to the wave's row cnt[wave * E + id] (no atomics).  id0 holds
+// the first batch.
+template <int U>
+__device__ __forceinline__ void wave_histograms(const int32_t* __restrict__ ids, int w_begin,
+                                                int w_end, const int (&id0)[U], int E, int nbits,
+                                                int32_t* cnt)
 {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int per_wave = (c1 - c0 + kRouteWaves - 1) / kRouteWaves;
-    const int w_begin = min(c1, c0 + wave * per_wave), w_end = min(c1, w_begin + per_wave);
 #pragma unroll 1
     for (int base = w_begin; base < w_end; base += kWave * U) {
         int id[U];
+        if (base == w_begin) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int r = base + u * kWave + lane;
-            id[u] = r < w_end ? ids[r] : -1;
+            for (int u = 0; u < U; ++u) id[u] = id0[u];
+        } else {
+            load_batch<U>(ids, base, w_end, id);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            bool valid = id[u] >= 0 && id[u] < E;
-            uint64_t peers = same_expert_lanes(id[u], valid, nbits);
+            const bool valid = id[u] >= 0 && id[u] < E;
+            const uint64_t peers = same_expert_lanes(id[u], valid, nbits);
             if (valid && (peers & lanes_below) == 0) cnt[wave * E + id[u]] += __popcll(peers);
         }
     }
@@ -106,8 +127,8 @@ __device__ __forceinline__ void wave_histograms(const int32_t* __restrict__ ids,
 // [G][E], from the counting launch) the expert segments' bases come from the
 // totals of every chunk and this chunk's routes go after those of chunks
 // 0..g-1; without, the chunk is the whole list.  Chunk 0 (or the only one)
-// writes block_expert, num_valid and, when given, expert_block0 (each
-// expert's first block, then the number of used blocks).  The order inside an expert's segment
+// writes block_expert, num_valid and, when given, block_info (per used block:
+// expert, the expert's first block, its block count, its route count).  The order inside an expert's segment
 // is ascending route: chunk, then wave, then lane order.
 template <int U>
 __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __restrict__ tw,
@@ -115,7 +136,7 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
                                 int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
                                 int32_t* __restrict__ block_expert,
                                 int32_t* __restrict__ num_valid,
-                                int32_t* __restrict__ expert_block0, int32_t* lds,
+                                int32_t* __restrict__ block_info, int32_t* lds,
                                 int c0 = 0, int c1 = -1,
                                 const int32_t* __restrict__ chunk_counts = nullptr, int G = 1,
                                 int g = 0)
@@ -128,12 +149,40 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+    // The wave's first batch of routes (the whole range of a chunk) and this
+    // thread's per-chunk counts are loaded up front, so that both passes and
+    // the scan wait on one round of memory latency.
+    int w_begin, w_end;
+    wave_range(c0, c1, w_begin, w_end);
+    int id0[U];
+    float wt0[U];
+    load_batch<U>(ids, w_begin, w_end, id0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = w_begin + u * kWave + lane;
+        wt0[u] = r < w_end ? tw[r] : 0.0f;
+    }
+    int pre_total = 0, pre_earlier = 0;     // expert tid, when E fits one scan round
+    if (chunk_counts && tid < E) {
+#pragma unroll 1
+        for (int c0g = 0; c0g < G; c0g += 8) {     // 8 loads in flight at a time
+            int n[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) n[j] = c0g + j < G ? chunk_counts[int64_t(c0g + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pre_total += n[j];
+                pre_earlier += c0g + j < g ? n[j] : 0;
+            }
+        }
+    }
+
     for (int i = tid; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
     if (!chunk_counts) fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert);
     __syncthreads();
 
     // pass 1: per-wave histogram of this chunk
-    wave_histograms<U>(ids, c0, c1, E, nbits, cnt);
+    wave_histograms<U>(ids, w_begin, w_end, id0, E, nbits, cnt);
     __syncthreads();
 
     // scan over experts of the padded totals (one expert per thread per round)
@@ -143,7 +192,10 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
         const int e = e0 + tid;
         int total = 0, earlier = 0;       // all routes of e; those of chunks before this one
         if (e < E) {
-            if (chunk_counts) {
+            if (chunk_counts && e0 == 0) {
+                total = pre_total;
+                earlier = pre_earlier;
+            } else if (chunk_counts) {
 #pragma unroll 1
                 for (int c = 0; c < G; ++c) {
                     const int n = chunk_counts[int64_t(c) * E + e];
@@ -183,8 +235,12 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
             }
             if (g == 0) {
 #pragma unroll 1
-                for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
-                if (expert_block0) expert_block0[e] = base_e / bm;
+                for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) {
+                    block_expert[b] = e;
+                    if (block_info)
+                        *reinterpret_cast<int4*>(block_info + 4 * b) =
+                            make_int4(e, base_e / bm, padded / bm, total);
+                }
             }
         }
         carry += all;
@@ -194,21 +250,23 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     if (tid == 0 && g == 0) {
         num_valid[0] = carry;
         num_valid[1] = valid_total;
-        if (expert_block0) expert_block0[E] = carry / bm;
     }
 
     // pass 2: stable scatter (each wave only touches its own histogram row)
-    const int per_wave = (c1 - c0 + kRouteWaves - 1) / kRouteWaves;
-    const int w_begin = min(c1, c0 + wave * per_wave), w_end = min(c1, w_begin + per_wave);
 #pragma unroll 1
     for (int base = w_begin; base < w_end; base += kWave * U) {
         int id[U];
         float wt[U];
+        if (base == w_begin) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int r = base + u * kWave + lane;
-            id[u] = r < w_end ? ids[r] : -1;
-            wt[u] = r < w_end ? tw[r] : 0.0f;
+            for (int u = 0; u < U; ++u) { id[u] = id0[u]; wt[u] = wt0[u]; }
+        } else {
+            load_batch<U>(ids, base, w_end, id);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = base + u * kWave + lane;
+                wt[u] = r < w_end ? tw[r] : 0.0f;
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -237,11 +295,14 @@ __device__ void route_count_body(const int32_t* __restrict__ ids, int R, int E, 
 {
     int32_t* cnt = lds;                                   // [waves][E]
     const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
+    int w_begin, w_end;
+    wave_range(g * kRouteChunk, min(R, (g + 1) * kRouteChunk), w_begin, w_end);
+    int id0[4];
+    load_batch<4>(ids, w_begin, w_end, id0);       // in flight during the fill
     for (int i = threadIdx.x; i < kRouteWaves * E; i += kPrologueThreads) cnt[i] = 0;
     fill_padding(R, bm, nb_cap, sorted_route, sorted_w, block_expert, g, G);
     __syncthreads();
-    const int c0 = g * kRouteChunk, c1 = min(R, c0 + kRouteChunk);
-    wave_histograms<4>(ids, c0, c1, E, nbits, cnt);
+    wave_histograms<4>(ids, w_begin, w_end, id0, E, nbits, cnt);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kPrologueThreads) {
         int total = 0;
@@ -261,7 +322,7 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
                                 int32_t* __restrict__ sorted_route, float* __restrict__ sorted_w,
                                 int32_t* __restrict__ block_expert,
                                 int32_t* __restrict__ num_valid,
-                                int32_t* __restrict__ expert_block0, int32_t* lds)
+                                int32_t* __restrict__ block_info, int32_t* lds)
 {
     int32_t* ids = lds;                                          // [R]
     float* tw = reinterpret_cast<float*>(lds + kShortList);      // [R]
@@ -304,8 +365,12 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
         if (e < E) {
             cnt[e] = base_e;
 #pragma unroll 1
-            for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) block_expert[b] = e;
-            if (expert_block0) expert_block0[e] = base_e / bm;
+            for (int b = base_e / bm; b < (base_e + padded) / bm; ++b) {
+                block_expert[b] = e;
+                if (block_info)
+                    *reinterpret_cast<int4*>(block_info + 4 * b) =
+                        make_int4(e, base_e / bm, padded / bm, total);
+            }
         }
         carry += __builtin_amdgcn_readlane(inc, kWave - 1);
         vcarry += __builtin_amdgcn_readlane(vinc, kWave - 1);
@@ -314,7 +379,6 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
     if (lane == 0) {
         num_valid[0] = carry;
         num_valid[1] = vcarry;
-        if (expert_block0) expert_block0[E] = carry / bm;
     }
     // pass 2: stable scatter
 #pragma unroll 1
@@ -402,7 +466,7 @@ prologue_kernel(PrologueArgs a)
     extern __shared__ int32_t lds[];
     if (blockIdx.x == 0) {
         route_sort_wave(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route, a.sorted_w,
-                        a.block_expert, a.num_valid, a.expert_block0, lds);
+                        a.block_expert, a.num_valid, a.block_info, lds);
     } else {
         quant_rows_body(a.hidden, a.M, a.D, a.a1q, a.a1s, blockIdx.x - 1, gridDim.x - 1,
                         kPrologueThreads);
@@ -434,7 +498,7 @@ route_scatter_kernel(PrologueArgs a, int G)
     const int g = blockIdx.x;
     const int R = a.M * a.topk;
     route_sort_body<4>(a.ids, a.tw, a.M, a.topk, a.E, a.bm, a.nb_cap, a.sorted_route, a.sorted_w,
-                       a.block_expert, a.num_valid, a.expert_block0, lds, g * kRouteChunk,
+                       a.block_expert, a.num_valid, a.block_info, lds, g * kRouteChunk,
                        min(R, (g + 1) * kRouteChunk), a.chunk_counts, G, g);
 }
 
