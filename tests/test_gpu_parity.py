@@ -333,6 +333,22 @@ def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     _check_forward(case, case.run_gpu(debug=True), f"shape M={M} D={D} I={I} E={E}")
 
 
+@pytest.mark.parametrize("M,D,I,E,n_routed,seed,path", [
+    (20, 512, 256, 130, 15, 51, "direct"),     # 16 slots: the route-indexed path's limit
+    (100, 512, 256, 64, 19, 52, "stream"),     # 20 slots: the 32-slot reduction
+    (300, 512, 256, 20, 16, 53, "tiled"),      # 17 slots on the LDS-tiled path
+])
+def test_forward_large_topk(binding, M, D, I, E, n_routed, seed, path):
+    """Many slots per token: per-token route tables on the route-indexed path,
+    the reduction instances for more than 8 and more than 16 slots."""
+    case = custom_case(M, D, I, E, n_routed, seed)
+    dbg = case.run_gpu(debug=True)
+    want = {"direct": binding.PATH_DIRECT, "stream": binding.PATH_STREAM,
+            "tiled": binding.PATH_TILED}[path]
+    assert dbg["path"] == want
+    _check_forward(case, dbg, f"top-{case.topk} {path} M={M} E={E}")
+
+
 @pytest.mark.parametrize("M,E", [(20, 6), (8, 40)])      # sorted and route-indexed paths
 def test_forward_invalid_and_duplicate_ids(binding, M, E):
     D, I = 512, 256
