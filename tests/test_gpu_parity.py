@@ -326,6 +326,8 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     (1400, 512, 256, 5, 2, 25),       # LDS-tiled path (block_m 256), ragged blocks
     (1000, 768, 512, 3, 1, 26),       # LDS-tiled path, D not a multiple of 512
     (200, 512, 256, 17, 8, 29),       # LDS-tiled path at ~106 routes per expert: blocks half padding
+    (1100, 512, 256, 9, 2, 30),       # LDS-tiled, 7 of 9 experts end in a block of <= 64 routes
+    (560, 256, 256, 3, 1, 31),        # the same with two K tiles per stage loop
 ])
 def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
