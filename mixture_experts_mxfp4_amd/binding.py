@@ -79,7 +79,10 @@ def _stream(stream=None):
     return ctypes.c_void_p(0)
 
 
-def _ptr(t, dtype=None, shape=None, name="tensor"):
+def _ptr(t, dtype=None, shape=None, name="tensor", device=None):
+    """Device pointer of t after checking what the kernels assume: a GPU tensor
+    (on `device` when given), dtype, shape, contiguity.  A host tensor would
+    hand a host address to a GPU kernel, so it is refused here."""
     if t is None:
         return None
     if dtype is not None and t.dtype != dtype:
@@ -88,6 +91,10 @@ def _ptr(t, dtype=None, shape=None, name="tensor"):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor, got device {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device} like the other operands")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -121,12 +128,12 @@ def _weight_dims(w13, w2):
     return E, Dh * 2, twoI // 2
 
 
-def _weight_ptrs(w13, w13s, w2, w2s, E, D, I, tag):
+def _weight_ptrs(w13, w13s, w2, w2s, E, D, I, tag, device=None):
     u8 = torch.uint8
-    return (_ptr(w13, u8, (E, 2 * I, D // 2), tag + "w13"),
-            _ptr(w13s, u8, (E, 2 * I, D // 32), tag + "w13_scale"),
-            _ptr(w2, u8, (E, D, I // 2), tag + "w2"),
-            _ptr(w2s, u8, (E, D, I // 32), tag + "w2_scale"))
+    return (_ptr(w13, u8, (E, 2 * I, D // 2), tag + "w13", device),
+            _ptr(w13s, u8, (E, 2 * I, D // 32), tag + "w13_scale", device),
+            _ptr(w2, u8, (E, D, I // 2), tag + "w2", device),
+            _ptr(w2s, u8, (E, D, I // 32), tag + "w2_scale", device))
 
 
 def moe_mxfp4_prepare_weights(w13, w13_scale, w2, w2_scale, w13_out=None, w13_scale_out=None,
@@ -136,8 +143,8 @@ def moe_mxfp4_prepare_weights(w13, w13_scale, w2, w2_scale, w13_out=None, w13_sc
     outs = [o if o is not None else torch.empty_like(i)
             for o, i in zip((w13_out, w13_scale_out, w2_out, w2_scale_out),
                             (w13, w13_scale, w2, w2_scale))]
-    src = _weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, "")
-    dst = _weight_ptrs(*outs, E, D, I, "out ")
+    src = _weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, "", w13.device)
+    dst = _weight_ptrs(*outs, E, D, I, "out ", w13.device)
     _check("moe_mxfp4_prepare_weights",
            _lib.moe_mxfp4_prepare_weights(*src, E, D, I, *dst, _stream(stream)))
     return tuple(outs)
@@ -146,8 +153,8 @@ def moe_mxfp4_prepare_weights(w13, w13_scale, w2, w2_scale, w13_out=None, w13_sc
 def moe_mxfp4_unprepare_weights(w13p, w13p_scale, w2p, w2p_scale, stream=None):
     E, D, I = _weight_dims(w13p, w2p)
     outs = [torch.empty_like(t) for t in (w13p, w13p_scale, w2p, w2p_scale)]
-    src = _weight_ptrs(w13p, w13p_scale, w2p, w2p_scale, E, D, I, "")
-    dst = _weight_ptrs(*outs, E, D, I, "out ")
+    src = _weight_ptrs(w13p, w13p_scale, w2p, w2p_scale, E, D, I, "", w13p.device)
+    dst = _weight_ptrs(*outs, E, D, I, "out ", w13p.device)
     _check("moe_mxfp4_unprepare_weights",
            _lib.moe_mxfp4_unprepare_weights(*src, E, D, I, *dst, _stream(stream)))
     return tuple(outs)
@@ -162,12 +169,13 @@ def _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, w
     E, D, I = _weight_dims(w13, w2)
     M = hidden.shape[0]
     topk = topk_ids.shape[1]
+    dev = hidden.device
     args = (_ptr(hidden, torch.bfloat16, (M, D), "hidden"),
-            *_weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, ""),
-            _ptr(topk_ids, torch.int32, (M, topk), "topk_ids"),
-            _ptr(topk_w, torch.float32, (M, topk), "topk_w"),
-            _ptr(out, torch.bfloat16, (M, D), "out"),
-            M, D, I, E, topk, _ptr(workspace, torch.uint8, None, "workspace"),
+            *_weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, "", dev),
+            _ptr(topk_ids, torch.int32, (M, topk), "topk_ids", dev),
+            _ptr(topk_w, torch.float32, (M, topk), "topk_w", dev),
+            _ptr(out, torch.bfloat16, (M, D), "out", dev),
+            M, D, I, E, topk, _ptr(workspace, torch.uint8, None, "workspace", dev),
             workspace.numel())
     return args, (M, D, I, E, topk)
 
@@ -225,7 +233,7 @@ def moe_mxfp4_forward_profiled(hidden, w13, w13_scale, w2, w2_scale, topk_ids, t
         if (stage1_clock.dtype != torch.int64 or stage1_clock.numel() < need
                 or not stage1_clock.is_cuda or not stage1_clock.is_contiguous()):
             raise TypeError(f"stage1_clock: expected a contiguous device int64 tensor of {need}")
-        clk = ctypes.c_void_p(stage1_clock.data_ptr())
+        clk = _ptr(stage1_clock, name="stage1_clock", device=hidden.device)
     _check("moe_mxfp4_forward_profiled",
            _lib.moe_mxfp4_forward_profiled(*args, ev, clk, _stream(stream)))
     return out
@@ -340,7 +348,7 @@ def moe_mxfp4_forward_a16w4_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids
     if h is not None:
         if h.dtype != torch.bfloat16 or h.numel() < M * topk * I or not h.is_contiguous():
             raise TypeError(f"h: expected a contiguous bf16 tensor of {M * topk * I} elements")
-        hp = ctypes.c_void_p(h.data_ptr())
+        hp = _ptr(h, name="h", device=hidden.device)
     ev = None
     if kernel_events is not None:
         if len(kernel_events) != 2 * len(LAUNCHES):
@@ -353,7 +361,7 @@ def moe_mxfp4_forward_a16w4_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids
         if (stage1_clock.dtype != torch.int64 or stage1_clock.numel() < need
                 or not stage1_clock.is_cuda or not stage1_clock.is_contiguous()):
             raise TypeError(f"stage1_clock: expected a contiguous device int64 tensor of {need}")
-        clk = ctypes.c_void_p(stage1_clock.data_ptr())
+        clk = _ptr(stage1_clock, name="stage1_clock", device=hidden.device)
     args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
     _check("moe_mxfp4_forward_a16w4_debug",
            _lib.moe_mxfp4_forward_a16w4_debug(*args, hp, ev, clk, _stream(stream)))

@@ -154,3 +154,25 @@ def test_binding_refuses_wrong_dtypes(binding):
     h = torch.zeros(2, 512, dtype=torch.float32)
     with pytest.raises(TypeError):
         binding._ptr(h, torch.bfloat16, (2, 512), "hidden")
+
+
+def test_binding_refuses_host_tensors():
+    """Tensors on the host would give the kernels host addresses: the binding
+    raises before any call into the library."""
+    import pytest
+    import torch
+    from mixture_experts_mxfp4_amd import binding
+    M, D, I, E, k = 4, 512, 256, 9, 3
+    u8 = torch.uint8
+    w = [torch.zeros(s, dtype=u8) for s in ((E, 2 * I, D // 2), (E, 2 * I, D // 32),
+                                            (E, D, I // 2), (E, D, I // 32))]
+    hidden = torch.zeros((M, D), dtype=torch.bfloat16)
+    ids = torch.zeros((M, k), dtype=torch.int32)
+    tw = torch.ones((M, k), dtype=torch.float32)
+    ws = torch.empty(binding.moe_mxfp4_workspace_bytes(M, D, I, E, k), dtype=u8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.moe_mxfp4_forward(hidden, *w, ids, tw, workspace=ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.moe_mxfp4_prepare_weights(*w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.moe_mxfp4_quantize(hidden)
