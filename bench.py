@@ -394,6 +394,8 @@ def run(args):
         "roofline_frac_forward": round(max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
                                            alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)) / sec, 4),
         "active_experts": alg["n_active"],
+        "launches_per_forward": 2 if a16 else binding.moe_mxfp4_launch_count(w.M, w.D, w.I, w.E,
+                                                                               w.topk),
         "kernel_us_warmup": stages_us,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -25,6 +25,7 @@ _lib.moe_mxfp4_workspace_bytes.argtypes = [_I] * 5
 _lib.moe_mxfp4_workspace_bytes.restype = _SZ
 _lib.moe_mxfp4_block_m.argtypes, _lib.moe_mxfp4_block_m.restype = [_I] * 5, _I
 _lib.moe_mxfp4_path.argtypes, _lib.moe_mxfp4_path.restype = [_I] * 5, _I
+_lib.moe_mxfp4_launch_count.argtypes, _lib.moe_mxfp4_launch_count.restype = [_I] * 5, _I
 _lib.moe_mxfp4_route_capacity.argtypes = [_I] * 4
 _lib.moe_mxfp4_route_capacity.restype = _I64
 for _name in ("moe_mxfp4_prepare_weights", "moe_mxfp4_unprepare_weights"):
@@ -51,7 +52,7 @@ _lib.moe_mxfp4_forward_a16w4_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P
 _lib.moe_mxfp4_forward_a16w4_debug.restype = _I
 
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
-           "moe_mxfp4_path",
+           "moe_mxfp4_path", "moe_mxfp4_launch_count",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
            "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
            "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled",
@@ -117,6 +118,11 @@ PATH_NAMES = {PATH_DIRECT: "direct", PATH_STREAM: "stream", PATH_TILED: "tiled"}
 def moe_mxfp4_path(M, D, I, E, topk) -> int:
     """Kernel path of the forward for this shape (PATH_DIRECT / _STREAM / _TILED; 0 if invalid)."""
     return int(_lib.moe_mxfp4_path(M, D, I, E, topk))
+
+
+def moe_mxfp4_launch_count(M, D, I, E, topk) -> int:
+    """Kernel launches of one forward for this shape (0 if invalid or M = 0)."""
+    return int(_lib.moe_mxfp4_launch_count(M, D, I, E, topk))
 
 
 def moe_mxfp4_route_capacity(M, E, topk, block_m) -> int:

@@ -339,6 +339,15 @@ MOE_API int moe_mxfp4_block_m(int M, int D, int I, int E, int topk)
     return choose_block_m(M, E, topk);
 }
 
+MOE_API int moe_mxfp4_launch_count(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk) || M == 0) return 0;
+    const int path = choose_path(M, E, topk);
+    if (path == MOE_MXFP4_PATH_DIRECT) return 2;
+    const int prologue = moe::route_chunks(M, topk) > 0 ? 2 : 1;
+    return prologue + (path == MOE_MXFP4_PATH_TILED ? 1 : 0) + 3;   // + stage 1, stage 2, sum
+}
+
 MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk) || M == 0) return 0;
