@@ -43,7 +43,7 @@ int device_check(int* n_cu)
         st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         if (st == 1 && (moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess ||
-                        moe::tile_allow_lds() != hipSuccess))
+                        moe::tile_allow_lds() != hipSuccess || moe::direct_allow_lds() != hipSuccess))
             return MOE_MXFP4_ERR_HIP;
         g_arch_state[dev].store(st, std::memory_order_relaxed);
     }

@@ -413,19 +413,37 @@ struct HFrag {
     uint4 v[A16 ? 4 : 1];
     uint32_t s;
 };
+// hl: h staged in LDS (A16W4: [M*topk][I] bf16; else the codes [M*topk][I/2]
+// followed by the scales [M*topk][I/32]), or null to read the global copy.
 template <bool A16>
-__device__ __forceinline__ HFrag<A16> load_hfrag(const DirectArgs& a, int r, int kt, int kq)
+__device__ __forceinline__ HFrag<A16> load_hfrag(const DirectArgs& a, int r, int kt, int kq,
+                                                 const uint8_t* hl)
 {
     HFrag<A16> f;
     const int I = a.I;
     if constexpr (A16) {
         f.s = 0u;
-        const uint8_t* p = reinterpret_cast<const uint8_t*>(a.h16 + int64_t(r) * I + kt * 128 + kq * 32);
+        const int64_t off = (int64_t(r) * I + kt * 128 + kq * 32) * 2;
+        if (hl) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.v[j] = r >= 0 ? ld16(p + 16 * j) : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                f.v[j] = r >= 0 ? *reinterpret_cast<const uint4*>(hl + off + 16 * j) : make_uint4(0, 0, 0, 0);
+        } else {
+            const uint8_t* p = reinterpret_cast<const uint8_t*>(a.h16) + off;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.v[j] = r >= 0 ? ld16(p + 16 * j) : make_uint4(0, 0, 0, 0);
+        }
     } else {
-        f.v[0] = r >= 0 ? ld16(a.a2q + int64_t(r) * (I / 2) + kt * 64 + kq * 16) : make_uint4(0, 0, 0, 0);
-        f.s = r >= 0 ? a.a2s[int64_t(r) * (I / 32) + kt * 4 + kq] : 0u;
+        const int64_t off = int64_t(r) * (I / 2) + kt * 64 + kq * 16;
+        const int64_t soff = int64_t(r) * (I / 32) + kt * 4 + kq;
+        if (hl) {
+            const int64_t codes = int64_t(a.M) * a.topk * (I / 2);
+            f.v[0] = r >= 0 ? *reinterpret_cast<const uint4*>(hl + off) : make_uint4(0, 0, 0, 0);
+            f.s = r >= 0 ? hl[codes + soff] : 0u;
+        } else {
+            f.v[0] = r >= 0 ? ld16(a.a2q + off) : make_uint4(0, 0, 0, 0);
+            f.s = r >= 0 ? a.a2s[soff] : 0u;
+        }
     }
     return f;
 }
@@ -456,6 +474,7 @@ gemm2_direct_kernel(DirectArgs a)
     __shared__ float s_tw[kOsMaxSlots];                    // topk_w by route
     __shared__ float red[kOsWaves][NS][RT][4][kWave];
     __shared__ int32_t s_active;
+    extern __shared__ __attribute__((aligned(16))) uint8_t hbuf[];   // a.h_lds bytes
     const int n16_0 = blockIdx.x * NS;          // first slice; NS | 4, so one 64-row group
     const int n64 = n16_0 / 4, q0 = n16_0 % 4;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -474,6 +493,22 @@ gemm2_direct_kernel(DirectArgs a)
         s_route[y * 16 * RT + t] = int16_t(a.route_of[i]);
     }
     for (int r = threadIdx.x; r < R; r += kOsThreads) s_tw[r] = a.tw[r];
+    // bf16 h of every route (A16W4, when it fits): staged once, the slots
+    // below gather their rows from LDS instead of the L2
+    const uint8_t* hl = nullptr;
+    if (a.h_lds > 0) {
+        const int64_t code_bytes = A16 ? int64_t(R) * I * 2 : int64_t(R) * (I / 2);
+        const uint8_t* src = A16 ? reinterpret_cast<const uint8_t*>(a.h16) : a.a2q;
+        for (int64_t i = int64_t(threadIdx.x) * 16; i < code_bytes; i += int64_t(kOsThreads) * 16)
+            *reinterpret_cast<uint4*>(hbuf + i) = ld16(src + i);
+        if constexpr (!A16) {
+            const int64_t scale_bytes = int64_t(R) * (I / 32);          // a multiple of 8
+            for (int64_t i = int64_t(threadIdx.x) * 8; i < scale_bytes; i += int64_t(kOsThreads) * 8)
+                *reinterpret_cast<uint2*>(hbuf + code_bytes + i) =
+                    *reinterpret_cast<const uint2*>(a.a2s + i);
+        }
+        hl = hbuf;
+    }
     __syncthreads();
     const int active = s_active;
 
@@ -523,7 +558,7 @@ gemm2_direct_kernel(DirectArgs a)
                     const int t = rt * 16 + row;
                     const int r = (on && t < M) ? s_route[y * 16 * RT + t] : -1;
 #pragma unroll
-                    for (int h = 0; h < KH; ++h) av[g][h][rt] = load_hfrag<A16>(a, r, kt + h, kq);
+                    for (int h = 0; h < KH; ++h) av[g][h][rt] = load_hfrag<A16>(a, r, kt + h, kq, hl);
                 }
             }
 #pragma unroll
@@ -574,7 +609,7 @@ gemm2_direct_kernel(DirectArgs a)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const int t = rt * 16 + row;
-                    av[rt] = load_hfrag<A16>(a, t < M ? tab[t] : -1, kt, kq);
+                    av[rt] = load_hfrag<A16>(a, t < M ? tab[t] : -1, kt, kq, hl);
                 }
 #pragma unroll
                 for (int sl = 0; sl < NS; ++sl) {
@@ -635,24 +670,62 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
     return hipGetLastError();
 }
 
-hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev)
+// The four stage-2 instances, and the LDS each can take for h beyond its
+// static arrays (the CU's 160 KiB less those), found once per process.
+static const void* const kG2Direct[4] = {
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>),
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, true, 1>),
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>),
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, false>)};
+static int g_h_lds_max[4] = {0, 0, 0, 0};
+constexpr int kCuLds = 160 * 1024;
+
+hipError_t direct_allow_lds()
 {
-    if (!direct_shape_ok(a)) return hipErrorInvalidValue;
-    if (a.M == 0) return hipSuccess;
-    const dim3 grid(a.D / (16 * kOsSlices));
-    if (a.h16) {
-        if (a.M <= 16)
-            MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>), grid,
-                       dim3(kOsThreads), 0, stream, ev, a);
-        else
-            MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, true, 1>), grid, dim3(kOsThreads), 0,
-                       stream, ev, a);
-    } else if (a.M <= 16) {
-        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>), grid,
-                   dim3(kOsThreads), 0, stream, ev, a);
-    } else {
-        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, false>), grid, dim3(kOsThreads), 0,
+    for (int i = 0; i < 4; ++i) {
+        hipFuncAttributes attr;
+        hipError_t e = hipFuncGetAttributes(&attr, kG2Direct[i]);
+        if (e != hipSuccess) return e;
+        const int avail = kCuLds - int(attr.sharedSizeBytes);
+        if (avail <= 0) continue;
+        e = hipFuncSetAttribute(kG2Direct[i], hipFuncAttributeMaxDynamicSharedMemorySize, avail);
+        if (e != hipSuccess) return e;
+        g_h_lds_max[i] = avail;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemm2_direct(const DirectArgs& a0, hipStream_t stream, const KernelEvents& ev)
+{
+    if (!direct_shape_ok(a0)) return hipErrorInvalidValue;
+    if (a0.M == 0) return hipSuccess;
+    const dim3 grid(a0.D / (16 * kOsSlices));
+    const int inst = (a0.h16 ? 0 : 2) + (a0.M <= 16 ? 0 : 1);
+    const int64_t R = int64_t(a0.M) * a0.topk;
+    const int64_t hbytes = a0.h16 ? R * a0.I * 2 : R * (a0.I / 2 + a0.I / 32);
+    DirectArgs a = a0;
+    // bf16 h (A16W4) is four times the MXFP4 codes: staging it pays for its copy
+    // (decode stage 2 24.5 -> 23.4 us); the MXFP4 h gathers from the L2 cost less
+    // than copying it (21.5 -> 22.3 us when staged), so those stay global
+    a.h_lds = a0.h16 && hbytes <= g_h_lds_max[inst] ? int(hbytes) : 0;
+    const uint32_t dyn = uint32_t(a.h_lds);
+    switch (inst) {
+    case 0:
+        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>), grid,
+                   dim3(kOsThreads), dyn, stream, ev, a);
+        break;
+    case 1:
+        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, true, 1>), grid, dim3(kOsThreads), dyn,
                    stream, ev, a);
+        break;
+    case 2:
+        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>), grid,
+                   dim3(kOsThreads), dyn, stream, ev, a);
+        break;
+    default:
+        MOE_LAUNCH((gemm2_direct_kernel<2, 1, kOsSlices, false>), grid, dim3(kOsThreads), dyn,
+                   stream, ev, a);
+        break;
     }
     return hipGetLastError();
 }

@@ -159,7 +159,9 @@ struct DirectArgs {
     // A16W4 mode when set: bf16 activations, no quantization; h is kept bf16
     // here, [M*topk][I] (a2q / a2s unused)
     uint16_t* h16 = nullptr;
+    int h_lds = 0;                 // stage 2: bytes of h it stages in LDS (set by its launcher)
 };
+hipError_t direct_allow_lds();     // lift the dynamic-LDS limit of the stage-2 kernels
 hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_direct_rows(const int32_t* ids, int R, int E, int32_t* row_route,
