@@ -66,6 +66,7 @@ def test_a16w4_e33_sixteen_tokens_sampled(binding):
     (13, 768, 768, 5, 3, 63),         # ragged M, D and I not multiples of 512
     (3, 256, 256, 2, 1, 64),          # smallest dims
     (24, 256, 256, 1024, 8, 65),      # largest E
+    (20, 512, 256, 9, 1, 69),         # two row tiles with h staged in LDS (40 routes, 20 KB)
 ])
 def test_a16w4_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"a16w4 shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
