@@ -35,6 +35,7 @@
 // Descending id order: a shared expert is conventionally the last id and has
 // a route from every token, the heaviest stage-1 work; its workgroups then
 // run first instead of forming the tail.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -677,7 +678,7 @@ static const void* const kG2Direct[4] = {
     reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, true, 1>),
     reinterpret_cast<const void*>(&gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>),
     reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, false>)};
-static int g_h_lds_max[4] = {0, 0, 0, 0};
+static std::atomic<int> g_h_lds_max[4];   // written once per device set-up (same values)
 constexpr int kCuLds = 160 * 1024;
 
 hipError_t direct_allow_lds()
@@ -690,7 +691,7 @@ hipError_t direct_allow_lds()
         if (avail <= 0) continue;
         e = hipFuncSetAttribute(kG2Direct[i], hipFuncAttributeMaxDynamicSharedMemorySize, avail);
         if (e != hipSuccess) return e;
-        g_h_lds_max[i] = avail;
+        g_h_lds_max[i].store(avail, std::memory_order_relaxed);
     }
     return hipSuccess;
 }
@@ -707,7 +708,7 @@ hipError_t launch_gemm2_direct(const DirectArgs& a0, hipStream_t stream, const K
     // bf16 h (A16W4) is four times the MXFP4 codes: staging it pays for its copy
     // (decode stage 2 24.5 -> 23.4 us); the MXFP4 h gathers from the L2 cost less
     // than copying it (21.5 -> 22.3 us when staged), so those stay global
-    a.h_lds = a0.h16 && hbytes <= g_h_lds_max[inst] ? int(hbytes) : 0;
+    a.h_lds = a0.h16 && hbytes <= g_h_lds_max[inst].load(std::memory_order_relaxed) ? int(hbytes) : 0;
     const uint32_t dyn = uint32_t(a.h_lds);
     switch (inst) {
     case 0:
