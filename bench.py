@@ -569,7 +569,7 @@ def main():
         return summarize_pmc(args.summarize_pmc)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
+        print(f"bench.py: the forward is measured on exactly one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported.", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.copy_calibration:
