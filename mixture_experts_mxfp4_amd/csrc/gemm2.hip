@@ -36,8 +36,12 @@ constexpr int kGemmThreads = 256;
 template <int RT>
 constexpr int g2_unroll() { return RT <= 2 ? 4 : 1; }
 
+// Four waves per SIMD: the register allocation then fits 128 registers (116
+// VGPRs at 64-row blocks, no accumulation registers) instead of taking 150 and
+// three waves; one wave more per SIMD keeps more weight loads in flight
+// (prefill stage 2 90 -> 88.5 us, 128 tokens on E=33 19 -> 17 us).
 template <int RT>
-__global__ void __launch_bounds__(kGemmThreads)
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)))
 gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
                       const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
                       const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
