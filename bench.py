@@ -16,9 +16,12 @@ no activation quantization; route-indexed kernels, up to 32 tokens).
 
 Prints ONE JSON line: the metric (algorithmic GB/s for HBM-bound workloads,
 TFLOP/s for MFMA-bound ones), microseconds per forward, the roofline of the
-dominant kernel (stage 1) timed with HIP events on its launch stream over the
-same K steps (in a second pass: the event records would perturb the timed
-one), and the CPU oracle timed on a bounded sample of the same workload.
+dominant kernel (stage 1) timed on the device over the same K steps (in a
+second pass: its timing records would perturb the timed one), and the CPU
+oracle timed on a bounded sample of the same workload.  With the default
+decode workload the line also carries a `workloads` map: the other D = 7168
+workloads (small_batch, prefill, large_prefill), each timed the same way with
+the same K and W (--headline-only leaves them out).
 
 Helper modes (used to make the committed rocprofv3 summaries):
     --copy-calibration         run a plain 1 GiB device copy (counter scale)
@@ -216,13 +219,15 @@ def workload_of(args):
     return inputs.Workload(f"shape_M{M}_E{E}_I{I}", M, 7168, I, E, 8, "uniform", 7)
 
 
-def run(args):
+def measure(w, args, a16=False):
+    """One workload on the GPU: K timed forwards after W untimed ones, then the
+    kernel-timing pass.  Returns the timing and roofline figures (and the
+    float inputs, for the CPU leg)."""
     import numpy as np
     import torch
 
     from mixture_experts_mxfp4_amd import binding, inputs
 
-    w = workload_of(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hidden, ids, tw = inputs.make_activations(w.M, w.D, w.E, w.n_routed, w.routing, w.seed)
@@ -245,7 +250,6 @@ def run(args):
 
     h_d, ids_d, tw_d = hidden.to(dev), ids.to(dev), tw.to(dev)
     out = torch.empty_like(h_d)
-    a16 = args.a16w4
     if a16:
         if binding.moe_mxfp4_a16w4_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
             raise SystemExit(f"bench.py: the A16W4 forward does not run {w.name} (M={w.M})")
@@ -283,7 +287,7 @@ def run(args):
     # untimed warm-up; the last warm-up pass also times every launch.  Under
     # sustained matrix-core load the chip's power controller overshoots after
     # any pause: the first ~20 forwards of large_prefill run up to 40% slower
-    # than the steady state (per-dispatch kernel traces), hence W = 20.
+    # than the steady state (per-dispatch kernel traces).
     stage_ev = Events(8)
     for i in range(args.warmup):
         ev = stage_ev.ev if i == args.warmup - 1 else [None] * 8
@@ -354,25 +358,110 @@ def run(args):
     roof["kernel_us_events"] = round(stage1_event_ms * 1000.0, 2)
     roof["kernel_timing"] = ("kernel span on the device clock; events: stop-to-stop "
                              "with the runtime's launch marker")
+    res = {
+        "w": w, "alg": alg, "hbm_bound": hbm_bound, "value": value, "unit": unit,
+        "ms_per_step": ms_per_step, "sec": sec, "path_name": path_name, "copies": copies,
+        "stages_us": stages_us, "roof": roof,
+        "inputs": (hidden, ids, tw, w13f, w2f),
+    }
+    del weight_sets, prepared, ws, out, h_d, spans
+    return res
+
+
+def forward_fraction(r):
+    """The whole forward's roofline fraction: the larger of its HBM and MFMA
+    floors over its measured time."""
+    alg = r["alg"]
+    return max(alg["bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)) / r["sec"]
+
+
+def workload_summary(r):
+    """The figures of one further workload for the `workloads` map."""
+    alg, sec = r["alg"], r["sec"]
+    return {
+        "us_per_forward": round(r["ms_per_step"] * 1000.0, 2),
+        "value": round(r["value"], 3 if r["unit"] == "TFLOP/s" else 1),
+        "unit": r["unit"],
+        "tokens_per_s": round(r["w"].M / sec, 1),
+        "hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
+        "mfma_tflops": round(alg["flops"] / sec / 1e12, 3),
+        "roofline_frac_forward": round(forward_fraction(r), 4),
+        "stage1": {k: r["roof"][k] for k in ("bound", "kernel", "achieved", "unit", "frac",
+                                             "kernel_us")},
+        "path": r["path_name"],
+        "launches_per_forward": _launches(r["w"]),
+        "kernel_us_warmup": r["stages_us"],
+    }
+
+
+def _launches(w):
+    from mixture_experts_mxfp4_amd import binding
+    return binding.moe_mxfp4_launch_count(w.M, w.D, w.I, w.E, w.topk)
+
+
+def host_cpu():
+    """The host's logical CPU count and CPU model (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def run(args):
+    import torch
+
+    from mixture_experts_mxfp4_amd import binding
+
+    w = workload_of(args)
+    a16 = args.a16w4
+    r = measure(w, args, a16)
+    hidden, ids, tw, w13f, w2f = r.pop("inputs")
+    alg, sec, unit = r["alg"], r["sec"], r["unit"]
 
     cpu = None
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, hidden, ids, tw, w13f, w2f, args.cpu_sample_s, act_quant=not a16)
         ca = cb["alg"]
-        cval = ca["bytes"] / cb["seconds"] / 1e9 if hbm_bound else ca["flops"] / cb["seconds"] / 1e12
+        cval = ca["bytes"] / cb["seconds"] / 1e9 if r["hbm_bound"] else ca["flops"] / cb["seconds"] / 1e12
+        n_cpu, model = host_cpu()
         cpu = {"value": round(cval, 4), "unit": unit, "cores": cb["threads"], "kind": "oracle",
+               "host_logical_cpus": n_cpu, "host_cpu_model": model,
                "sample": f"first {cb['tokens']} of {w.M} tokens of the {w.name} workload "
                          f"({cb['seconds']:.2f} s wall, fp64 C oracle"
-                         f"{', activations unquantized' if a16 else ''}, {cb['threads']} threads)"}
+                         f"{', activations unquantized' if a16 else ''}, {cb['threads']} threads "
+                         f"on a host with {n_cpu} logical CPUs)"}
+    del hidden, ids, tw, w13f, w2f
+
+    # the other D = 7168 workloads of the metric, timed with the same K and W
+    extra = {}
+    if not args.headline_only and not args.shape and not a16:
+        from mixture_experts_mxfp4_amd import inputs
+        for name in ("small_batch", "prefill", "large_prefill"):
+            if name == w.name:
+                continue
+            torch.cuda.empty_cache()
+            ro = measure(inputs.WORKLOADS[name], args)
+            ro.pop("inputs")
+            extra[name] = workload_summary(ro)
+            extra[name]["config"] = (f"M={ro['w'].M} D={ro['w'].D} I={ro['w'].I} E={ro['w'].E} "
+                                     f"top{ro['w'].topk} ({ro['w'].n_routed} routed "
+                                     f"{ro['w'].routing} + shared expert {ro['w'].E - 1})")
+            del ro
 
     line = {
         "metric": METRIC,
-        "value": round(value, 3 if unit == "TFLOP/s" else 1),
+        "value": round(r["value"], 3 if unit == "TFLOP/s" else 1),
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -384,22 +473,22 @@ def run(args):
                    "mode": "a16w4" if a16 else "a4w4",
                    "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
                    "routing": w.routing, "seed": w.seed, "global_batch": w.M,
-                   "parallelism": "single GPU", "path": path_name,
+                   "parallelism": "single GPU", "path": r["path_name"],
                    "block_m": 16 if a16 else binding.moe_mxfp4_block_m(w.M, w.D, w.I, w.E, w.topk),
-                   "weight_copies": copies},
-        "us_per_forward": round(ms_per_step * 1000.0, 2),
+                   "weight_copies": r["copies"]},
+        "us_per_forward": round(r["ms_per_step"] * 1000.0, 2),
         "tokens_per_s": round(w.M / sec, 1),
         "hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
         "mfma_tflops": round(alg["flops"] / sec / 1e12, 3),
-        "roofline_frac_forward": round(max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
-                                           alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)) / sec, 4),
+        "roofline_frac_forward": round(forward_fraction(r), 4),
         "active_experts": alg["n_active"],
-        "launches_per_forward": 2 if a16 else binding.moe_mxfp4_launch_count(w.M, w.D, w.I, w.E,
-                                                                               w.topk),
-        "kernel_us_warmup": stages_us,
-        "roofline": roof,
+        "launches_per_forward": 2 if a16 else _launches(w),
+        "kernel_us_warmup": r["stages_us"],
+        "roofline": r["roof"],
         "cpu_baseline": cpu,
     }
+    if extra:
+        line["workloads"] = extra
     print(json.dumps(line, ensure_ascii=False), flush=True)
 
 
@@ -550,6 +639,8 @@ def main():
                    help="the A16W4 forward (bf16 activations; up to 32 tokens)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only the named workload (no `workloads` map of the others)")
     p.add_argument("--cpu-sample-s", type=float, default=16.0,
                    help="CPU-seconds of oracle work in the baseline sample")
     p.add_argument("--copy-calibration", action="store_true")

@@ -22,7 +22,12 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device and must
  *    be 16-byte aligned (the forward's workspace 256-byte aligned).  bf16
- *    tensors are passed as uint16_t bit patterns.
+ *    tensors are passed as uint16_t bit patterns.  16 bytes is the widest
+ *    access any kernel makes to a caller's tensor (one 16-byte vector load or
+ *    store per lane), so it is all they need; submission 723815 asserts
+ *    128-byte alignment of its shuffled scale tensors for its own kernels,
+ *    which these do not share.  The workspace is carved into sub-buffers at
+ *    256-byte boundaries, hence its stricter rule.
  *  - The caller owns every buffer, including the workspace.  The library keeps
  *    no pointer after a call returns and allocates no device memory.
  *  - Work is enqueued asynchronously on `stream`; nothing synchronizes with the
@@ -65,10 +70,24 @@ const char* moe_mxfp4_status_string(int status);
 
 /* Limits of this implementation (host-validated):
  *   D, I: multiples of 256, 256 <= D, I <= 65536
- *   1 <= E <= 1024, 1 <= topk <= 32, 0 <= M, M * topk <= 2^24. */
+ *   1 <= E <= 1024, 1 <= topk <= 32, 0 <= M, M * topk <= 2^24;
+ *   on the TILED path (moe_mxfp4_path) also I * D < 2^31 and
+ *   max(D, I) / 128 * moe_mxfp4_route_capacity(M, E, topk, 256) * 4 < 2^32
+ *   (its kernels address one expert's weights and the sorted operands' scale
+ *   words with 32-bit offsets); a shape beyond them is
+ *   MOE_MXFP4_ERR_UNSUPPORTED, and the shape queries below return 0 for it. */
 
 /* ---------------------------------------------------------------------------
  * Weight preparation (offline, once per weight set).
+ *
+ * Passage: both kernelindex.com amd-moe-mxfp4 submissions receive each weight
+ * set twice in their input tuple, raw and pre-shuffled for their kernels
+ * (the `*_shuffled` gate_up / down weights and scales that `custom_kernel`
+ * passes to its fused MoE call, next to the raw ones that the reference
+ * `_dequant` / `_reference_forward` of submission 723815 reads).  The
+ * shuffle is kernel-specific and the pages do not define it; this call is the
+ * equivalent step for this library's kernels: a pure permutation of bytes
+ * that leaves every code and scale value unchanged.
  *
  * Permutes raw MXFP4 weights into the kernel layout.  Raw layouts:
  *   w13       u8 [E, 2I, D/2]   gate_up codes (rows 0..I-1 gate, I..2I-1 up)
@@ -138,7 +157,8 @@ int moe_mxfp4_forward(const uint16_t* hidden,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* The kernel path the forward takes for this shape (0 for an invalid shape):
+/* The kernel path the forward takes for this shape (0 for an invalid or
+ * unsupported shape):
  * DIRECT when M <= 32, topk <= 16, E <= 1024 and block_m is 16; else TILED when
  * block_m is 256; else STREAM.  The choice depends on the shape only. */
 int moe_mxfp4_path(int M, int D, int I, int E, int topk);
@@ -160,17 +180,49 @@ int moe_mxfp4_launch_count(int M, int D, int I, int E, int topk);
  * ------------------------------------------------------------------------- */
 
 /* MXFP4-quantize a bf16 matrix [rows, cols] (cols % 32 == 0) per 32 along a
- * row: codes u8 [rows, cols/2], scales u8 [rows, cols/32] (row-major). */
+ * row: codes u8 [rows, cols/2], scales u8 [rows, cols/32] (row-major).
+ *
+ * Passage: the dynamic activation quantization of kernelindex.com
+ * amd-moe-mxfp4 submission 754773 (`custom_kernel`, FP4 branch: the hidden
+ * states are quantized per 32 elements to E2M1 codes with one e8m0 scale
+ * before the gate_up GEMM, "per_1x32"), in the format its weights use (two
+ * codes per byte, low nibble first, as submission 723815's `_dequant` reads
+ * them).  The page imports that quantizer without showing its rounding; the
+ * rule here is the OCP MX v1.0 one stated at the top of this header.  The
+ * forward runs this same quantizer inside its prologue; this entry point
+ * exposes it alone (tests; quantizing float weights).
+ * Arguments: x bf16 device [rows, cols], 16-byte aligned; codes and scales
+ * device, caller-owned, codes 4-byte aligned.  rows = 0 is a no-op.
+ * Errors: INVALID_ARG for rows < 0, cols <= 0 or not a multiple of 32, a null
+ * or misaligned pointer; UNSUPPORTED off gfx950; ERR_HIP if the launch fails. */
 int moe_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                        uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
-/* Route sort alone: expert-sorted, block_m-padded route lists.  A route is
- * r = t*topk + s.  Experts appear in ascending order, each expert's routes in
+/* Route sort alone: expert-sorted, block_m-padded route lists.
+ *
+ * Passage: the sorting workspace of kernelindex.com amd-moe-mxfp4 submission
+ * 754773 (sorted token ids, sorted routing weights, one expert id per block
+ * of block_m rows and a num_valid pair, sized for M*topk + E*block_m - topk
+ * rows, each expert's segment padded to a multiple of block_m, filled by
+ * aiter's `moe_sorting_fwd` before stage 1), and the routing kernels of
+ * submission 723815 (`kernel_count_tokens`: a histogram of the expert ids,
+ * skipping ids outside [0, E); `kernel_prefix_sum`: an exclusive scan;
+ * `kernel_scatter_tokens`: each route into its expert's segment).  The
+ * forward runs the same sort in its prologue on the sorted paths; this entry
+ * point exposes it alone (tests).  Unlike the atomics of 723815, the order
+ * inside a segment is fixed (ascending route), so the list is deterministic.
+ *
+ * A route is r = t*topk + s.  Experts appear in ascending order, each expert's routes in
  * ascending r, padded with the id M*topk (weight 0) to a multiple of block_m.
  *   sorted_route i32 [cap], sorted_w f32 [cap], block_expert i32 [cap/block_m]
  *   (-1 past the last used block), num_valid i32 [2] = {padded rows, valid
  *   routes}; cap = moe_mxfp4_route_capacity(M, E, topk, block_m).
- * block_m must be 16, 32, 64, 128 or 256. */
+ * block_m must be 16, 32, 64, 128 or 256.
+ * Arguments: topk_ids i32 / topk_w f32 device [M, topk]; outputs device,
+ * caller-owned, 4-byte aligned, sized from moe_mxfp4_route_capacity.
+ * Errors: INVALID_ARG for a bad M / E / topk / block_m or a null or
+ * misaligned pointer; UNSUPPORTED for E > 1024 or M*topk > 2^24 and off
+ * gfx950; ERR_HIP if the launch fails. */
 int moe_mxfp4_route(const int32_t* topk_ids, const float* topk_w,
                     int M, int E, int topk, int block_m,
                     int32_t* sorted_route, float* sorted_w,

@@ -4,7 +4,7 @@
 // host synchronization (grids are sized for the worst-case route list;
 // blocks past the real one exit):
 //   route-indexed path (few tokens): stage 1 (own route scan + activation
-//     quant) -> stage 2 -> per-token slot reduction;
+//     quant) -> stage 2 (with the per-token sum over slots);
 //   sorted paths: prologue (route sort + activation quant) [-> sorted copy of
 //     the activations for the tiled kernels] -> stage 1 -> stage 2 -> slot
 //     reduction;
@@ -164,11 +164,25 @@ Layout layout(int M, int D, int I, int E, int topk, bool a16 = false)
     return L;
 }
 
+// The LDS-tiled kernels address one expert's weights and the sorted
+// operands' K-major scale words with 32-bit per-lane offsets (gemm_tile.hip):
+// an expert's gate_up codes (I*D bytes) must stay below 2^31, and the scale
+// words of all K tiles (K/128 tiles x cap rows x 4 bytes, K = D in stage 1
+// and I in stage 2) below 2^32.
+bool tiled_offsets_ok(int M, int D, int I, int E, int topk)
+{
+    const int64_t cap = route_capacity(M, E, topk, 256);
+    const int64_t kmax = D > I ? D : I;
+    return int64_t(I) * D < (int64_t(1) << 31) && kmax / 128 * cap * 4 < (int64_t(1) << 32);
+}
+
 int check_shape(int M, int D, int I, int E, int topk)
 {
     if (M < 0 || E < 1 || topk < 1 || topk > kMaxTopk || !dims_ok(D, I))
         return MOE_MXFP4_ERR_INVALID_ARG;
     if (E > kMaxE || int64_t(M) * topk > kMaxRoutes) return MOE_MXFP4_ERR_UNSUPPORTED;
+    if (choose_path(M, E, topk) == MOE_MXFP4_PATH_TILED && !tiled_offsets_ok(M, D, I, E, topk))
+        return MOE_MXFP4_ERR_UNSUPPORTED;
     return MOE_MXFP4_OK;
 }
 

@@ -44,9 +44,7 @@
 namespace moe {
 
 constexpr int kDirThreads = 256;
-#ifndef MOE_G1_UNROLL
-#define MOE_G1_UNROLL 1          // K tiles per double-buffered chunk (x NG x 4 KiB of weights)
-#endif
+constexpr int kG1Unroll = 1;     // K tiles per double-buffered chunk (x NG x 4 KiB of weights)
 
 // Picks this workgroup's expert and its routes; run by one whole wave.
 // Pass 1 marks the experts that have a route in an LDS bitmap; the y-th
@@ -393,16 +391,9 @@ gemm1_direct_kernel(DirectArgs a)
 // A16W4 (a.h16 set): the h fragment of a row is 32 bf16 (64 bytes) of its
 // route's bf16 h row, and each weight fragment is widened to bf16 once per
 // slot and K tile and shared by the row tiles (mfma_a16w4_block).
-#ifndef MOE_OS_SLOTS_IN_FLIGHT
-#define MOE_OS_SLOTS_IN_FLIGHT 2
-#endif
-#ifndef MOE_OS_A16_SLOTS_IN_FLIGHT
-#define MOE_OS_A16_SLOTS_IN_FLIGHT 1
-#endif
-#ifndef MOE_OS_THREADS
-#define MOE_OS_THREADS 1024
-#endif
-constexpr int kOsThreads = MOE_OS_THREADS;
+constexpr int kOsSlotsInFlight = 2;       // slots loaded before their MFMAs (MXFP4 h)
+constexpr int kOsA16SlotsInFlight = 1;    // the same with bf16 h (64-byte fragments)
+constexpr int kOsThreads = 1024;
 constexpr int kOsWaves = kOsThreads / kWave;
 constexpr int kOsSlices = 2;
 constexpr int kOsMaxSlots = kDirectMaxTokens * kMaxTopkDirect;
@@ -663,10 +654,10 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
     if (a.M == 0) return hipSuccess;
     const dim3 grid(direct_stage1_x(a.I), direct_slots(a.M, a.E, a.topk));
     if (a.h16)
-        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, kDirectGroups, true>), grid,
+        MOE_LAUNCH((gemm1_direct_kernel<kG1Unroll, kDirectGroups, true>), grid,
                    dim3(kDirThreads), 0, stream, ev, a);
     else
-        MOE_LAUNCH((gemm1_direct_kernel<MOE_G1_UNROLL, kDirectGroups, false>), grid,
+        MOE_LAUNCH((gemm1_direct_kernel<kG1Unroll, kDirectGroups, false>), grid,
                    dim3(kDirThreads), 0, stream, ev, a);
     return hipGetLastError();
 }
@@ -674,9 +665,9 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
 // The four stage-2 instances, and the LDS each can take for h beyond its
 // static arrays (the CU's 160 KiB less those), found once per process.
 static const void* const kG2Direct[4] = {
-    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>),
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, kOsA16SlotsInFlight, kOsSlices, true>),
     reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, true, 1>),
-    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>),
+    reinterpret_cast<const void*>(&gemm2_direct_kernel<1, kOsSlotsInFlight, kOsSlices, false>),
     reinterpret_cast<const void*>(&gemm2_direct_kernel<2, 1, kOsSlices, false>)};
 static std::atomic<int> g_h_lds_max[4];   // written once per device set-up (same values)
 constexpr int kCuLds = 160 * 1024;
@@ -712,7 +703,7 @@ hipError_t launch_gemm2_direct(const DirectArgs& a0, hipStream_t stream, const K
     const uint32_t dyn = uint32_t(a.h_lds);
     switch (inst) {
     case 0:
-        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_A16_SLOTS_IN_FLIGHT, kOsSlices, true>), grid,
+        MOE_LAUNCH((gemm2_direct_kernel<1, kOsA16SlotsInFlight, kOsSlices, true>), grid,
                    dim3(kOsThreads), dyn, stream, ev, a);
         break;
     case 1:
@@ -720,7 +711,7 @@ hipError_t launch_gemm2_direct(const DirectArgs& a0, hipStream_t stream, const K
                    stream, ev, a);
         break;
     case 2:
-        MOE_LAUNCH((gemm2_direct_kernel<1, MOE_OS_SLOTS_IN_FLIGHT, kOsSlices, false>), grid,
+        MOE_LAUNCH((gemm2_direct_kernel<1, kOsSlotsInFlight, kOsSlices, false>), grid,
                    dim3(kOsThreads), dyn, stream, ev, a);
         break;
     default:

@@ -84,19 +84,13 @@ struct Gemm1Args {
     const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
-#ifndef MOE_G1S_GROUPS
-#define MOE_G1S_GROUPS 2
-#endif
-#ifndef MOE_G1S_GROUPS32
-#define MOE_G1S_GROUPS32 2
-#endif
 // 64-row gate_up groups per workgroup of the streaming stage 1 (grid: I/32 /
 // groups x blocks).  Two groups halve the activation rows each weight byte
 // pays for; at 16-row blocks the gather is small and the wider grid wins.
 // I is a multiple of 256, so I/32 divides by 2.
 constexpr int stream_stage1_groups(int block_m)
 {
-    return block_m == 64 ? MOE_G1S_GROUPS : block_m == 32 ? MOE_G1S_GROUPS32 : 1;
+    return block_m == 64 || block_m == 32 ? 2 : 1;
 }
 
 
@@ -130,12 +124,9 @@ constexpr int kDirectMaxTokens = 32;
 constexpr int kMaxTopkDirect = 16;
 constexpr int kDirectMaxRoutes = 1024;
 constexpr int kDirectMaxE = 1024;
-#ifndef MOE_G1_GROUPS
-#define MOE_G1_GROUPS 2
-#endif
 // 64-row gate_up groups per stage-1 workgroup of the route-indexed path, and
 // the stage-1 grid's x extent (2I/64 groups; I is a multiple of 256)
-constexpr int kDirectGroups = MOE_G1_GROUPS;
+constexpr int kDirectGroups = 2;
 __host__ __device__ inline int direct_stage1_x(int I) { return I / (32 * kDirectGroups); }
 // expert slots: min(E, M*topk), an upper bound of the active experts
 __host__ __device__ inline int direct_slots(int M, int E, int topk)

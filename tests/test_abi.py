@@ -93,6 +93,31 @@ def test_workspace_bytes(binding):
     assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 2000, 9) == 0     # E > 1024
 
 
+def test_tiled_path_offset_limits(binding):
+    """The LDS-tiled kernels use 32-bit per-lane offsets: an expert's gate_up
+    codes (I*D bytes) below 2^31 and the sorted operands' scale words below
+    2^32; beyond that every shape query reports the shape unsupported and the
+    forward refuses it before touching the device."""
+    M, E, k = 4096, 33, 9
+    assert binding.moe_mxfp4_path(M, 7168, 2048, E, k) == binding.PATH_TILED
+    assert binding.moe_mxfp4_path(M, 65536, 65536, E, k) == 0              # I*D = 2^32
+    assert binding.moe_mxfp4_workspace_bytes(M, 65536, 65536, E, k) == 0
+    assert binding.moe_mxfp4_path(M, 65536, 32512, E, k) == binding.PATH_TILED   # I*D < 2^31
+    assert binding.moe_mxfp4_path(M, 65536, 32768, E, k) == 0              # I*D = 2^31
+    # the other paths keep 64-bit addressing: a streaming shape of the same dims is fine
+    assert binding.moe_mxfp4_path(64, 65536, 65536, E, k) == binding.PATH_STREAM
+    # scale words: 65536/128 K tiles x cap rows x 4 bytes >= 2^32 for a very long route list
+    big = 1 << 21
+    assert binding.moe_mxfp4_path(big, 65536, 256, E, 8) == 0
+    assert binding.moe_mxfp4_path(big, 7168, 256, E, 8) == binding.PATH_TILED
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    lib.moe_mxfp4_forward.argtypes = binding._lib.moe_mxfp4_forward.argtypes
+    lib.moe_mxfp4_forward.restype = ctypes.c_int
+    ok = ctypes.c_void_p(0x1000)
+    assert lib.moe_mxfp4_forward(*([ok] * 8), M, 65536, 65536, E, k, ok, 1 << 40,
+                                 ctypes.c_void_p(0)) == 2
+
+
 def test_host_validation_without_device(binding):
     lib = ctypes.CDLL(binding.LIB_PATH)
     lib.moe_mxfp4_forward.argtypes = binding._lib.moe_mxfp4_forward.argtypes

@@ -57,3 +57,21 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+def test_host_cpu_and_workload_summary():
+    """The CPU leg states the host's logical CPU count and model; a further
+    workload's entry carries its time, rate and both roofline fractions."""
+    n, model = bench.host_cpu()
+    assert n == os.cpu_count() and (model is None or isinstance(model, str))
+    w = inputs.WORKLOADS["large_prefill"]
+    ids = np.tile(np.arange(9, dtype=np.int32) + 24, (w.M, 1))
+    alg = bench.algorithmic(w, ids)
+    r = {"w": w, "alg": alg, "sec": 1e-3, "ms_per_step": 1.0, "value": alg["flops"] / 1e-3 / 1e12,
+         "unit": "TFLOP/s", "path_name": "tiled", "stages_us": None,
+         "roof": {"bound": "mfma", "kernel": "gemm1_tile_kernel", "achieved": 4000.0,
+                  "unit": "TFLOP/s", "frac": 0.396, "kernel_us": 540.0}}
+    s = bench.workload_summary(r)
+    assert s["us_per_forward"] == 1000.0 and s["unit"] == "TFLOP/s"
+    assert abs(s["roofline_frac_forward"] - alg["flops"] / (bench.FP4_PEAK_TFLOPS * 1e12) / 1e-3) < 1e-4
+    assert s["stage1"]["frac"] == 0.396 and s["path"] == "tiled"

@@ -3,9 +3,12 @@
 Bit-exact: MXFP4 codes/scales (activation quantizer, fused stage-1 requant),
 route lists, weight preparation.  Floating point: the end-to-end tolerance
 |gpu - oracle| <= 2e-2 rms + 2^-7 |oracle| on >= 99.9 % of elements, none
-beyond 0.1 rms.  Where the debug outputs are at hand, the bound of a token also
-allows for stage-1 requant codes that sit one E2M1 grid step from the oracle's
-because the two h differ by an ulp at a rounding midpoint (requant_slack).
+beyond 0.1 rms.  Where the debug outputs are at hand, a requant code may sit
+one E2M1 grid step from the oracle's only where the GPU h and the oracle h lie
+on opposite sides of that rounding midpoint (or the block maxima on opposite
+sides of a scale step); then, and only then, the token's bound grows by what
+the moved code carries (tests/moe_cases.requant_moves / requant_slack).
+Without such a move the strict bound is asserted.
 """
 import numpy as np
 import pytest
@@ -13,8 +16,8 @@ import torch
 
 import oracle
 from mixture_experts_mxfp4_amd import inputs
-from tests.moe_cases import (Case, bf16_to_f64, check_close, custom_case, log, requant_slack,
-                             workload_case)
+from tests.moe_cases import (Case, bf16_to_f64, check_close, covering_tokens, custom_case, log,
+                             requant_slack, workload_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -204,10 +207,12 @@ def test_prepare_layout_and_round_trip(binding, E, D, I):
 
 # --------------------------------------------------------------- forward ---
 
-def _check_intermediates(case, dbg):
+def _check_intermediates(case, dbg, h_or, tokens=None):
+    """The route list the forward used (bit for bit), h per row against the
+    oracle's h, and the fused requant bit for bit against the oracle quantizer
+    applied to the GPU's own h; h_or is the oracle's h [ntok, topk, I] for
+    `tokens` (all tokens when None): only their rows are compared."""
     from mixture_experts_mxfp4_amd import binding
-    """h per sorted row against the oracle's h; the fused requant bit-exact
-    against the oracle quantizer applied to the GPU's own h."""
     sr = dbg["sorted_route"].cpu().numpy()
     n = int(dbg["num_valid"].cpu().numpy()[0])
     bm = dbg["block_m"]
@@ -220,32 +225,41 @@ def _check_intermediates(case, dbg):
     else:
         want_route = oracle.route(case.ids, case.tw, case.E, bm)
         np.testing.assert_array_equal(sr[:n], want_route["sorted_route"])
+    tok_list = np.arange(case.M) if tokens is None else np.asarray(tokens)
+    pos = np.full(case.M, -1, np.int64)
+    pos[tok_list] = np.arange(tok_list.size)
     valid = np.nonzero(sr[:n] < R)[0]
+    valid = valid[pos[sr[valid] // case.topk] >= 0]
     h_gpu = dbg["h"].cpu().view(torch.int16).numpy().view(np.uint16)[valid]
-    _, h_or = case.run_oracle(want_h=True)
     r = sr[valid]
-    h_ref = h_or[r // case.topk, r % case.topk]
+    h_ref = h_or[pos[r // case.topk], r % case.topk]
     g, o = bf16_to_f64(h_gpu), bf16_to_f64(h_ref)
     rms = float(np.sqrt(np.mean(o * o)))
     assert np.all(np.abs(g - o) <= 2.0 ** -6 * np.abs(o) + 1e-3 * rms)
     exact = float(np.mean(h_gpu == h_ref))
-    log(f"h exact-bits fraction {exact:.4f}")
+    log(f"h: {valid.size} rows compared, exact-bits fraction {exact:.4f}")
     assert exact >= 0.95
     codes, scales = oracle.quantize_rows(h_gpu)
     np.testing.assert_array_equal(dbg["a2_scales"].cpu().numpy()[valid], scales)
     np.testing.assert_array_equal(dbg["a2_codes"].cpu().numpy()[valid], codes)
+    return valid.size
 
 
-def _check_forward(case, dbg, what):
-    """Intermediates first (h, bit-exact requant of the GPU h), then the output
-    with the slack of requant codes one grid step from the oracle's (rare: at
-    most one h element in a thousand)."""
-    _check_intermediates(case, dbg)
-    slack, moved, total = requant_slack(case, dbg)
-    log(f"{what}: requant codes one grid step from the oracle's: {moved} of {total}")
-    assert moved <= 1e-3 * total
+def _check_forward(case, dbg, what, tokens=None):
+    """One oracle run (output and h) over `tokens` (all when None): the
+    intermediates, then the output.  Requant codes may differ from the
+    oracle's only as tests/moe_cases.requant_moves explains; without any
+    such difference the strict tolerance is asserted, with one the output's
+    bound grows by what the moved codes carry (requant_slack)."""
+    out_or, h_or = case.run_oracle(tokens=tokens, want_h=True)
+    _check_intermediates(case, dbg, h_or, tokens)
+    slack, moved, total = requant_slack(case, dbg, h_or, tokens)
+    log(f"{what}: requant codes moved across a rounding boundary: {moved} of {total}")
+    assert moved <= 1e-3 * max(total, 1)
     out = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
-    check_close(out, case.run_oracle(), what, slack=slack)
+    if tokens is not None:
+        out = out[tokens]
+    return check_close(out, out_or, what, slack=slack)
 
 
 def test_forward_tiny_full_and_intermediates(binding):
@@ -253,20 +267,35 @@ def test_forward_tiny_full_and_intermediates(binding):
     _check_forward(case, case.run_gpu(debug=True), "tiny")
 
 
-@pytest.mark.parametrize("name,n_sample", [("decode", 16), ("small_batch", 24),
-                                           ("prefill", 48), ("large_prefill", 16)])
-def test_forward_workload_sampled(binding, name, n_sample):
+# (workload, part, parts): large_prefill's covering tokens are checked in two
+# halves so that each test's oracle run stays near a minute
+_COVERING = [("decode", 0, 1), ("small_batch", 0, 1), ("prefill", 0, 1),
+             ("large_prefill", 0, 2), ("large_prefill", 1, 2)]
+
+
+@pytest.mark.parametrize("name,part,parts", _COVERING,
+                         ids=[f"{c[0]}-{c[1]}" for c in _COVERING])
+def test_forward_workload_covering(binding, name, part, parts):
+    """The full-size workloads, in the launch configuration the benchmark
+    times: the plain forward's output equals the debug forward's bit for bit,
+    and on tokens whose routes touch every used block of the sorted list (every
+    64-row group's first 16-row slice and the slice of its last route; all
+    tokens at decode) the route list, h, the requant codes and the output
+    match the oracle.  Every other output element must be finite."""
     case = workload_case(name)
-    out = case.run_gpu()
-    rng = np.random.default_rng(11)
-    toks = np.unique(np.concatenate([[0, case.M - 1],
-                                     rng.choice(case.M, min(n_sample, case.M), replace=False)]))
-    log(f"{name}: oracle on {toks.size} tokens")
-    want = case.run_oracle(tokens=toks)
-    got = out.cpu().view(torch.int16).numpy().view(np.uint16)[toks]
-    check_close(got, want, name)
-    full = out.cpu().float()
-    assert torch.isfinite(full).all()
+    plain = case.run_gpu().cpu().view(torch.int16).numpy().view(np.uint16)
+    dbg = case.run_gpu(debug=True)
+    got = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(plain, got), "debug forward and plain forward differ"
+    assert np.all(np.isfinite(bf16_to_f64(plain)))
+    toks = covering_tokens(case.ids, case.tw, case.E, dbg["block_m"], must=(0, case.M - 1))
+    if name == "small_batch":                       # a few more tokens than the 10 that cover
+        rng = np.random.default_rng(11)
+        toks = np.union1d(toks, rng.choice(case.M, 16, replace=False))
+    toks = np.array_split(toks, parts)[part]
+    log(f"{name} part {part + 1}/{parts}: path {binding.PATH_NAMES[dbg['path']]}, block_m "
+        f"{dbg['block_m']}, oracle on {toks.size} tokens")
+    _check_forward(case, dbg, f"{name} ({toks.size} covering tokens)", tokens=toks)
 
 
 @pytest.mark.parametrize("name", ["prefill", "large_prefill"])

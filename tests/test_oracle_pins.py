@@ -3,6 +3,7 @@
 - hand-written E2M1 / e8m0 tables (tests/golden), from the decoders printed on
   kernelindex submission 723815 and the OCP MX v1.0 definitions;
 - hand-worked MXFP4 quantization cases (tests/golden/mx_quant_cases.txt);
+- the MXFP4 dequantizer element by element against the hand tables;
 - brute force: every quantized element is the nearest grid point (ties to even);
 - invariants: requantizing an MXFP4-representable block is the identity;
 - the textbook float32 -> bf16 round-to-nearest-even bit trick;
@@ -202,6 +203,40 @@ def test_quantize_rows_matches_numpy_quantizer():
     codes_np, scales_np = dense_ref.quantize(dense_ref.bf16_bits_to_f64(bits))
     np.testing.assert_array_equal(scales, scales_np)
     np.testing.assert_array_equal(dense_ref.unpack(packed), codes_np)
+
+
+def test_dequantize_rows_against_hand_tables():
+    """oracle_mx_dequantize_rows on a non-square matrix (3 rows x 3 blocks):
+    every byte holds two different nibbles, every (row, block) its own scale
+    byte from the hand-written e8m0 table, so a swapped nibble order, a wrong
+    row pitch of the scales (cols/32) or a wrong block index (i/32) changes
+    the result.  Expected values: the hand tables, element by element."""
+    e2m1 = {int(c, 16): float(v) for c, v in _read_pairs("e2m1_table.txt")}
+    e8m0 = {int(b): float.fromhex(v) for b, v in _read_pairs("e8m0_table.txt") if v != "nan"}
+    rows, cols = 3, 96
+    rng = np.random.default_rng(17)
+    lo = rng.integers(0, 16, (rows, cols // 2))
+    hi = (lo + rng.integers(1, 16, (rows, cols // 2))) % 16        # differs from lo
+    packed = (lo | (hi << 4)).astype(np.uint8)
+    table_bytes = sorted(e8m0)                                    # 0, 1, 126, 127, 128, 200, 254
+    scales = np.array(table_bytes + table_bytes[:2], np.uint8).reshape(rows, cols // 32)
+    got = oracle.dequantize_rows(packed, scales)
+    for r in range(rows):
+        for i in range(cols):
+            code = int(packed[r, i // 2]) >> (4 * (i % 2)) & 0xF
+            want = e2m1[code] * e8m0[int(scales[r, i // 32])]
+            assert got[r, i] == want and math.copysign(1, got[r, i]) == math.copysign(1, want), \
+                (r, i, got[r, i], want)
+
+
+def test_dequantize_rows_matches_numpy_dequant():
+    """The same function against the independent numpy decoder on random
+    codes and random (finite) scale bytes per block."""
+    rng = np.random.default_rng(23)
+    packed = rng.integers(0, 256, (7, 160)).astype(np.uint8)
+    scales = rng.integers(0, 255, (7, 10)).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.dequantize_rows(packed, scales),
+                                  dense_ref.dequant(packed, scales))
 
 
 def test_mx_dot_matches_dense_dot():
