@@ -273,6 +273,18 @@ _COVERING = [("decode", 0, 1), ("small_batch", 0, 1), ("prefill", 0, 1),
              ("large_prefill", 0, 2), ("large_prefill", 1, 2)]
 
 
+_LAST_CASE = {}
+
+
+def _workload_case_cached(name):
+    """The workload's case, kept for the next test when it asks for the same
+    one (large_prefill's two halves share one oracle weight quantization)."""
+    if name not in _LAST_CASE:
+        _LAST_CASE.clear()
+        _LAST_CASE[name] = workload_case(name)
+    return _LAST_CASE[name]
+
+
 @pytest.mark.parametrize("name,part,parts", _COVERING,
                          ids=[f"{c[0]}-{c[1]}" for c in _COVERING])
 def test_forward_workload_covering(binding, name, part, parts):
@@ -282,7 +294,7 @@ def test_forward_workload_covering(binding, name, part, parts):
     64-row group's first 16-row slice and the slice of its last route; all
     tokens at decode) the route list, h, the requant codes and the output
     match the oracle.  Every other output element must be finite."""
-    case = workload_case(name)
+    case = _workload_case_cached(name)
     plain = case.run_gpu().cpu().view(torch.int16).numpy().view(np.uint16)
     dbg = case.run_gpu(debug=True)
     got = dbg["out"].cpu().view(torch.int16).numpy().view(np.uint16)
