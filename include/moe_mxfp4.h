@@ -157,6 +157,35 @@ int moe_mxfp4_forward(const uint16_t* hidden,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Forward that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments and result as moe_mxfp4_forward without the workspace: the
+ * library uses a static device array of MOE_MXFP4_NOALLOC_SCRATCH_BYTES
+ * instead (each GPU the library runs on holds its own copy, from the first
+ * call on that device until the process ends; nothing is allocated per
+ * call, and no kernel relies on its contents from a previous call).
+ * A shape whose workspace (moe_mxfp4_workspace_bytes) exceeds that size is
+ * refused with MOE_MXFP4_ERR_WORKSPACE before anything is enqueued: the
+ * decode and small-batch shapes fit (for example M <= 16 with E = 257,
+ * I = 256, or M <= 64 with E = 33, I = 2048 at D = 7168), the prefill shapes
+ * do not.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one device (different streams, or different host threads
+ * without ordering) race and give undefined results; calls on one stream are
+ * ordered and safe.
+ * ------------------------------------------------------------------------- */
+#define MOE_MXFP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int moe_mxfp4_forward_noalloc(const uint16_t* hidden,
+                              const uint8_t* w13, const uint8_t* w13_scale,
+                              const uint8_t* w2, const uint8_t* w2_scale,
+                              const int32_t* topk_ids, const float* topk_w,
+                              uint16_t* out,
+                              int M, int D, int I, int E, int topk,
+                              hipStream_t stream);
+
 /* The kernel path the forward takes for this shape (0 for an invalid or
  * unsupported shape):
  * DIRECT when M <= 32, topk <= 16, E <= 1024 and block_m is 16; else TILED when

@@ -33,6 +33,8 @@ for _name in ("moe_mxfp4_prepare_weights", "moe_mxfp4_unprepare_weights"):
     getattr(_lib, _name).restype = _I
 _lib.moe_mxfp4_forward.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
 _lib.moe_mxfp4_forward.restype = _I
+_lib.moe_mxfp4_forward_noalloc.argtypes = [_P] * 8 + [_I] * 5 + [_P]
+_lib.moe_mxfp4_forward_noalloc.restype = _I
 _lib.moe_mxfp4_forward_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
 _lib.moe_mxfp4_forward_debug.restype = _I
 _lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P, _P]
@@ -54,7 +56,8 @@ _lib.moe_mxfp4_forward_a16w4_debug.restype = _I
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
            "moe_mxfp4_path", "moe_mxfp4_launch_count",
            "moe_mxfp4_route_capacity", "moe_mxfp4_prepare_weights",
-           "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_debug",
+           "moe_mxfp4_unprepare_weights", "moe_mxfp4_forward", "moe_mxfp4_forward_noalloc",
+           "moe_mxfp4_forward_debug",
            "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled",
            "moe_mxfp4_wall_clock_khz", "moe_mxfp4_stage1_workgroups",
            "moe_mxfp4_a16w4_workspace_bytes", "moe_mxfp4_forward_a16w4",
@@ -196,6 +199,30 @@ def moe_mxfp4_forward(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ou
         workspace = alloc_workspace(hidden.shape[0], D, I, E, topk_ids.shape[1], hidden.device)
     args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
     _check("moe_mxfp4_forward", _lib.moe_mxfp4_forward(*args, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # MOE_MXFP4_NOALLOC_SCRATCH_BYTES
+
+
+def moe_mxfp4_forward_noalloc(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out=None,
+                              stream=None):
+    """The forward on the library's static scratch array (no workspace, no
+    allocation by the library; `out` is allocated here only when not given).
+    Shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise
+    (MOE_MXFP4_ERR_WORKSPACE)."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    E, D, I = _weight_dims(w13, w2)
+    M = hidden.shape[0]
+    topk = topk_ids.shape[1]
+    dev = hidden.device
+    args = (_ptr(hidden, torch.bfloat16, (M, D), "hidden"),
+            *_weight_ptrs(w13, w13_scale, w2, w2_scale, E, D, I, "", dev),
+            _ptr(topk_ids, torch.int32, (M, topk), "topk_ids", dev),
+            _ptr(topk_w, torch.float32, (M, topk), "topk_w", dev),
+            _ptr(out, torch.bfloat16, (M, D), "out", dev), M, D, I, E, topk)
+    _check("moe_mxfp4_forward_noalloc", _lib.moe_mxfp4_forward_noalloc(*args, _stream(stream)))
     return out
 
 

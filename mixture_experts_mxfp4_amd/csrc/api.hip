@@ -29,26 +29,49 @@ constexpr int64_t kMaxRoutes = int64_t(1) << 24;
 
 std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<uintptr_t> g_scratch[kMaxDevices];  // device address of `scratch` per device
 
-// Checks that the current device is gfx950; returns its CU count in *n_cu.
-int device_check(int* n_cu)
+}  // namespace
+
+// The workspace of moe_mxfp4_forward_noalloc, for callers that cannot
+// allocate.  Every device the library runs on holds its own copy of this
+// array (the module is loaded per device) until the process ends.  In host
+// code the name `scratch` is only a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, taken once per device in device_check
+// (with that device current) and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_MXFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Checks that the current device is gfx950; returns its CU count in *n_cu
+// and, when asked, the device address of its `scratch` array.  The first call
+// on a device also lifts the kernels' LDS limits and takes that address.
+int device_check(int* n_cu, uint8_t** scratch_out = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return MOE_MXFP4_ERR_UNSUPPORTED;
-    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
     if (st == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
         st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-        if (st == 1 && (moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess ||
-                        moe::tile_allow_lds() != hipSuccess || moe::direct_allow_lds() != hipSuccess))
-            return MOE_MXFP4_ERR_HIP;
-        g_arch_state[dev].store(st, std::memory_order_relaxed);
+        if (st == 1) {
+            if (moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess ||
+                moe::tile_allow_lds() != hipSuccess || moe::direct_allow_lds() != hipSuccess)
+                return MOE_MXFP4_ERR_HIP;
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return MOE_MXFP4_ERR_HIP;
+            g_scratch[dev].store(reinterpret_cast<uintptr_t>(p), std::memory_order_relaxed);
+        }
+        g_arch_state[dev].store(st, std::memory_order_release);
     }
     if (st != 1) return MOE_MXFP4_ERR_UNSUPPORTED;
     *n_cu = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (scratch_out)
+        *scratch_out = reinterpret_cast<uint8_t*>(g_scratch[dev].load(std::memory_order_relaxed));
     return MOE_MXFP4_OK;
 }
 
@@ -249,25 +272,30 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
     return MOE_MXFP4_OK;
 }
 
+// noalloc: the workspace is the current device's `scratch` array
+// (`workspace` and `workspace_bytes` are ignored).
 int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
                  const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                  const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
                  void* workspace, size_t workspace_bytes, const DebugOut* dbg,
-                 hipStream_t stream, bool a16 = false)
+                 hipStream_t stream, bool a16 = false, bool noalloc = false)
 {
     int st = check_shape(M, D, I, E, topk);
     if (st) return st;
     if (a16 && !a16w4_shape_ok(M, E, topk)) return MOE_MXFP4_ERR_UNSUPPORTED;
     if (M == 0) return MOE_MXFP4_OK;
-    const void* ptrs[] = {hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace};
+    const void* ptrs[] = {hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out};
     for (const void* p : ptrs)
         if (!p || !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
-    if (!aligned(workspace, 256)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (!noalloc && (!workspace || !aligned(workspace, 256))) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (noalloc) workspace_bytes = MOE_MXFP4_NOALLOC_SCRATCH_BYTES;
     const Layout L = layout(M, D, I, E, topk, a16);
     if (workspace_bytes < L.total) return MOE_MXFP4_ERR_WORKSPACE;
     int n_cu = 0;
-    st = device_check(&n_cu);
+    uint8_t* scratch_ptr = nullptr;
+    st = device_check(&n_cu, noalloc ? &scratch_ptr : nullptr);
     if (st) return st;
+    if (noalloc) workspace = scratch_ptr;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (L.path == MOE_MXFP4_PATH_DIRECT)
@@ -448,6 +476,16 @@ MOE_API int moe_mxfp4_forward(const uint16_t* hidden, const uint8_t* w13, const 
 {
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, nullptr, stream);
+}
+
+MOE_API int moe_mxfp4_forward_noalloc(const uint16_t* hidden, const uint8_t* w13,
+                                      const uint8_t* w13_scale, const uint8_t* w2,
+                                      const uint8_t* w2_scale, const int32_t* topk_ids,
+                                      const float* topk_w, uint16_t* out, int M, int D, int I,
+                                      int E, int topk, hipStream_t stream)
+{
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, nullptr, 0, nullptr, stream, false, true);
 }
 
 MOE_API int moe_mxfp4_forward_debug(const uint16_t* hidden, const uint8_t* w13,

@@ -118,6 +118,25 @@ def test_tiled_path_offset_limits(binding):
                                  ctypes.c_void_p(0)) == 2
 
 
+def test_noalloc_host_validation_without_device(binding):
+    """The forward without a workspace refuses bad arguments, and shapes whose
+    workspace exceeds its static scratch array, before touching a device."""
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    lib.moe_mxfp4_forward_noalloc.argtypes = binding._lib.moe_mxfp4_forward_noalloc.argtypes
+    lib.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
+    null, ok = ctypes.c_void_p(0), ctypes.c_void_p(0x1000)
+    assert lib.moe_mxfp4_forward_noalloc(*([null] * 8), 4, 512, 256, 9, 3, null) == 1
+    assert lib.moe_mxfp4_forward_noalloc(*([ok] * 8), 4, 500, 256, 9, 3, null) == 1
+    assert lib.moe_mxfp4_forward_noalloc(*([ok] * 8), 0, 512, 256, 9, 3, null) == 0
+    limit = binding.NOALLOC_SCRATCH_BYTES
+    assert binding.moe_mxfp4_workspace_bytes(1024, 7168, 256, 257, 9) > limit
+    assert lib.moe_mxfp4_forward_noalloc(*([ok] * 8), 1024, 7168, 256, 257, 9, null) == 3
+    assert binding.moe_mxfp4_workspace_bytes(16, 7168, 256, 257, 9) <= limit
+    assert binding.moe_mxfp4_workspace_bytes(64, 7168, 2048, 33, 9) <= limit
+    text = open(HEADER).read()
+    assert f"MOE_MXFP4_NOALLOC_SCRATCH_BYTES (32u << 20)" in text and limit == 32 << 20
+
+
 def test_host_validation_without_device(binding):
     lib = ctypes.CDLL(binding.LIB_PATH)
     lib.moe_mxfp4_forward.argtypes = binding._lib.moe_mxfp4_forward.argtypes
