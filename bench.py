@@ -60,8 +60,10 @@ NS_A16 = 13.0                   # oracle ns per multiply-add with bf16 activatio
 # the stage-1 (dominant) kernel and the sources that define it, per path
 _CSRC = "mixture_experts_mxfp4_amd/csrc/"
 STAGE1 = {
-    "direct": ("gemm1_direct_kernel", (_CSRC + "direct.hip", _CSRC + "moe_common.h",
-                                       _CSRC + "moe_kernels.h")),
+    "direct": ("gemm1_direct_kernel", (_CSRC + "direct.hip", _CSRC + "direct_common.h",
+                                       _CSRC + "moe_common.h", _CSRC + "moe_kernels.h")),
+    "persistent": ("decode_fused_kernel", (_CSRC + "decode_fused.hip", _CSRC + "direct_common.h",
+                                           _CSRC + "moe_common.h", _CSRC + "moe_kernels.h")),
     "stream": ("gemm1_swiglu_quant_kernel", (_CSRC + "gemm1.hip", _CSRC + "moe_common.h",
                                              _CSRC + "moe_kernels.h")),
     "tiled": ("gemm1_tile_kernel", (_CSRC + "gemm_tile.hip", _CSRC + "moe_common.h",
@@ -219,7 +221,7 @@ def workload_of(args):
     return inputs.Workload(f"shape_M{M}_E{E}_I{I}", M, 7168, I, E, 8, "uniform", 7)
 
 
-def measure(w, args, a16=False):
+def measure(w, args, a16=False, persistent=False):
     """One workload on the GPU: K timed forwards after W untimed ones, then the
     kernel-timing pass.  Returns the timing and roofline figures (and the
     float inputs, for the CPU leg)."""
@@ -250,7 +252,21 @@ def measure(w, args, a16=False):
 
     h_d, ids_d, tw_d = hidden.to(dev), ids.to(dev), tw.to(dev)
     out = torch.empty_like(h_d)
-    if a16:
+    if persistent:
+        if binding.moe_mxfp4_persistent_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
+            raise SystemExit(f"bench.py: the persistent forward does not run {w.name} (M={w.M})")
+        ws = binding.alloc_workspace_persistent(w.M, w.D, w.I, w.E, w.topk, dev)
+        path = binding.PATH_DIRECT
+        n_wg = binding.moe_mxfp4_persistent_workgroups(w.M)
+
+        def forward(wset):
+            binding.moe_mxfp4_forward_persistent(h_d, *wset, ids_d, tw_d, out, ws)
+
+        def forward_timed(wset, ev, clk=None):
+            binding.moe_mxfp4_forward_persistent_debug(h_d, *wset, ids_d, tw_d, out, ws,
+                                                       intermediates=False, kernel_events=ev,
+                                                       clock=clk)
+    elif a16:
         if binding.moe_mxfp4_a16w4_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
             raise SystemExit(f"bench.py: the A16W4 forward does not run {w.name} (M={w.M})")
         ws = binding.alloc_workspace_a16w4(w.M, w.D, w.I, w.E, w.topk, dev)
@@ -274,9 +290,9 @@ def measure(w, args, a16=False):
         def forward_timed(wset, ev, clk=None):
             binding.moe_mxfp4_forward_profiled(h_d, *wset, ids_d, tw_d, out, ws, ev, clk)
     torch.cuda.synchronize()
-    path_name = binding.PATH_NAMES[path]
-    launches = binding.PATH_LAUNCHES[path]
-    workload_id = w.name + ("_a16w4" if a16 else "")
+    path_name = "persistent" if persistent else binding.PATH_NAMES[path]
+    launches = (1,) if persistent else binding.PATH_LAUNCHES[path]
+    workload_id = w.name + ("_a16w4" if a16 else "") + ("_persistent" if persistent else "")
 
     # buffers of the kernel-timing pass, allocated up front so that no host
     # work separates the passes
@@ -323,12 +339,15 @@ def measure(w, args, a16=False):
         forward(weight_sets[i % copies])
     for i in range(args.steps + 1):
         ev = [None] * 8
-        ev[2 * prev + 1] = step_ev.ev[2 * i]
+        if prev != 1:                  # one launch per forward: its own previous stop
+            ev[2 * prev + 1] = step_ev.ev[2 * i]
         ev[3] = step_ev.ev[2 * i + 1]
         forward_timed(weight_sets[i % copies], ev, spans[i])
     torch.cuda.synchronize()
     if same_forward:
         ev_times = [step_ev.ms(2 * i, 2 * i + 1) for i in range(1, args.steps + 1)]
+    elif prev == 1:
+        ev_times = [step_ev.ms(2 * (i - 1) + 1, 2 * i + 1) for i in range(1, args.steps + 1)]
     else:
         ev_times = [step_ev.ms(2 * (i - 1), 2 * i + 1) for i in range(1, args.steps + 1)]
     sp = spans[1:].cpu()
@@ -343,7 +362,9 @@ def measure(w, args, a16=False):
     hbm_bound = alg["bytes"] / (HBM_PEAK_GBS * 1e9) >= alg["flops"] / (FP4_PEAK_TFLOPS * 1e12)
     if hbm_bound:
         value, unit = alg["bytes"] / sec / 1e9, "GB/s"
-        achieved = alg["stage1_bytes"] / (stage1_ms / 1000.0) / 1e9
+        # the persistent kernel is the whole forward: all of its bytes
+        kbytes = alg["bytes"] if persistent else alg["stage1_bytes"]
+        achieved = kbytes / (stage1_ms / 1000.0) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
@@ -354,6 +375,8 @@ def measure(w, args, a16=False):
     roof["traffic"] = load_traffic(workload_id, path_name)
     roof["kernel"] = STAGE1[path_name][0]
     roof["source_sha256_16"] = source_hash(STAGE1[path_name][1])
+    if persistent:
+        roof["algorithmic_bytes"] = "the whole forward (one launch)"
     roof["kernel_us"] = round(stage1_ms * 1000.0, 2)
     roof["kernel_us_events"] = round(stage1_event_ms * 1000.0, 2)
     roof["kernel_timing"] = ("kernel span on the device clock; events: stop-to-stop "
@@ -420,7 +443,7 @@ def run(args):
 
     w = workload_of(args)
     a16 = args.a16w4
-    r = measure(w, args, a16)
+    r = measure(w, args, a16, persistent=args.persistent)
     hidden, ids, tw, w13f, w2f = r.pop("inputs")
     alg, sec, unit = r["alg"], r["sec"], r["unit"]
 
@@ -440,7 +463,7 @@ def run(args):
 
     # the other D = 7168 workloads of the metric, timed with the same K and W
     extra = {}
-    if not args.headline_only and not args.shape and not a16:
+    if not args.headline_only and not args.shape and not a16 and not args.persistent:
         from mixture_experts_mxfp4_amd import inputs
         for name in ("small_batch", "prefill", "large_prefill"):
             if name == w.name:
@@ -471,6 +494,7 @@ def run(args):
                                f": M={w.M} D={w.D} I={w.I} E={w.E} top{w.topk} "
                                f"({w.n_routed} routed {w.routing} + shared expert {w.E - 1})",
                    "mode": "a16w4" if a16 else "a4w4",
+                   "variant": "persistent (one launch)" if args.persistent else "default",
                    "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
                    "routing": w.routing, "seed": w.seed, "global_batch": w.M,
                    "parallelism": "single GPU", "path": r["path_name"],
@@ -482,7 +506,7 @@ def run(args):
         "mfma_tflops": round(alg["flops"] / sec / 1e12, 3),
         "roofline_frac_forward": round(forward_fraction(r), 4),
         "active_experts": alg["n_active"],
-        "launches_per_forward": 2 if a16 else _launches(w),
+        "launches_per_forward": 2 if a16 else 1 if args.persistent else _launches(w),
         "kernel_us_warmup": r["stages_us"],
         "roofline": r["roof"],
         "cpu_baseline": cpu,
@@ -637,6 +661,8 @@ def main():
                    help="a D=7168 top-9 workload of this shape instead of --workload")
     p.add_argument("--a16w4", action="store_true",
                    help="the A16W4 forward (bf16 activations; up to 32 tokens)")
+    p.add_argument("--persistent", action="store_true",
+                   help="the persistent forward (one launch; up to 32 tokens)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--headline-only", action="store_true",

@@ -374,6 +374,84 @@ int moe_mxfp4_forward_a16w4_debug(const uint16_t* hidden,
                                   uint16_t* h, hipEvent_t* kernel_events,
                                   uint64_t* stage1_clock, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Persistent forward: the route-indexed (few-token) forward in ONE launch.
+ *
+ * Passage: the b12x CuTeDSL W4A16 fused MoE kernel (`W4A16FusedMoeKernel.kernel`)
+ * runs FC1 and FC2 in one persistent launch separated by a grid barrier
+ * (`_grid_barrier`: an arrival count and a sense word in a caller buffer),
+ * with the top-k sum folded into the FC2 epilogue for small-M decode
+ * ("TC-decode").  Here: one launch of as many 256-thread workgroups as the
+ * CUs hold at once; each runs stage-1 units (route scan, MXFP4 activation
+ * quant, gate_up GEMM, SwiGLU, requant of h per route), then builds its
+ * stage-2 tables from the routing and issues its first down-projection weight
+ * loads, then waits at a grid barrier, then computes 16-column output slices
+ * for all tokens with the per-token sum in fp32.  Result: the same operation
+ * as moe_mxfp4_forward (same arguments, prepared weights, id semantics and
+ * error behaviour; per-token sum over experts in descending id order, in
+ * fp32, then one bf16 rounding; deterministic).
+ *
+ * Shapes: those of the A16W4 forward (M <= 32, topk <= 16, M*topk <= 1024,
+ * E <= 1024); any other returns MOE_MXFP4_ERR_UNSUPPORTED and
+ * moe_mxfp4_persistent_workspace_bytes returns 0 for it.
+ *
+ * Workspace: moe_mxfp4_persistent_workspace_bytes(...) bytes, 256-byte
+ * aligned.  Its first 2048 bytes hold the barrier's words: they must be zero
+ * before the first call, which moe_mxfp4_workspace_init arranges (enqueued
+ * on `stream`; once per workspace), and every completed call leaves them
+ * as it found them except the generation word (the uint32 at byte offset
+ * 0), which counts the calls.  The barrier needs every workgroup resident at once; each wait
+ * is bounded (50 ms of the device's constant-rate clock).  If a wait times
+ * out (another kernel holding CUs), the waiting workgroups fill the output
+ * slices they own with NaN, the uint32 at byte offset 4 of the workspace
+ * becomes nonzero, the kernel still exits, and the workspace must be
+ * initialized again before its next use.  Concurrent calls need different
+ * workspaces.
+ * ------------------------------------------------------------------------- */
+size_t moe_mxfp4_persistent_workspace_bytes(int M, int D, int I, int E, int topk);
+
+/* Fills a workspace with zeros (one kernel on `stream`, plain stores, no
+ * memset, so it may be captured in a graph): the set-up the persistent
+ * forward needs once per workspace (and again after a timed-out call).
+ * workspace_bytes must be a multiple of 256 (every workspace size the
+ * library reports is).  INVALID_ARG for a null or misaligned pointer or a
+ * bad size. */
+int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workgroups of the persistent launch for M tokens on the current device
+ * (its per-CU occupancy times its CUs; 0 for M outside 1..32 or no usable
+ * device): the size of its clock array below is twice this. */
+int64_t moe_mxfp4_persistent_workgroups(int M);
+
+int moe_mxfp4_forward_persistent(const uint16_t* hidden,
+                                 const uint8_t* w13, const uint8_t* w13_scale,
+                                 const uint8_t* w2, const uint8_t* w2_scale,
+                                 const int32_t* topk_ids, const float* topk_w,
+                                 uint16_t* out,
+                                 int M, int D, int I, int E, int topk,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* moe_mxfp4_forward_persistent with exports (each may be NULL):
+ *   h         bf16 [M*topk, I], a2_codes u8 [M*topk, I/2], a2_scales u8
+ *             [M*topk, I/32]: silu(gate)*up and its MXFP4 form by route
+ *             (rows of invalid ids unspecified), 16-byte aligned;
+ *   kernel_events  as in moe_mxfp4_forward_profiled; the single launch is
+ *             launch 1 (entries 2 and 3);
+ *   clock     device uint64 [2 * moe_mxfp4_persistent_workgroups(M)],
+ *             8-byte aligned: each workgroup's start and end on the
+ *             constant-rate clock (moe_mxfp4_wall_clock_khz). */
+int moe_mxfp4_forward_persistent_debug(const uint16_t* hidden,
+                                       const uint8_t* w13, const uint8_t* w13_scale,
+                                       const uint8_t* w2, const uint8_t* w2_scale,
+                                       const int32_t* topk_ids, const float* topk_w,
+                                       uint16_t* out,
+                                       int M, int D, int I, int E, int topk,
+                                       void* workspace, size_t workspace_bytes,
+                                       uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
+                                       hipEvent_t* kernel_events, uint64_t* clock,
+                                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,15 @@ _lib.moe_mxfp4_forward_a16w4.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
 _lib.moe_mxfp4_forward_a16w4.restype = _I
 _lib.moe_mxfp4_forward_a16w4_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P, _P, _P]
 _lib.moe_mxfp4_forward_a16w4_debug.restype = _I
+_lib.moe_mxfp4_persistent_workspace_bytes.argtypes = [_I] * 5
+_lib.moe_mxfp4_persistent_workspace_bytes.restype = _SZ
+_lib.moe_mxfp4_workspace_init.argtypes, _lib.moe_mxfp4_workspace_init.restype = [_P, _SZ, _P], _I
+_lib.moe_mxfp4_persistent_workgroups.argtypes = [_I]
+_lib.moe_mxfp4_persistent_workgroups.restype = _I64
+_lib.moe_mxfp4_forward_persistent.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
+_lib.moe_mxfp4_forward_persistent.restype = _I
+_lib.moe_mxfp4_forward_persistent_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
+_lib.moe_mxfp4_forward_persistent_debug.restype = _I
 
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
            "moe_mxfp4_path", "moe_mxfp4_launch_count",
@@ -61,7 +70,9 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_bl
            "moe_mxfp4_quantize", "moe_mxfp4_route", "moe_mxfp4_forward_profiled",
            "moe_mxfp4_wall_clock_khz", "moe_mxfp4_stage1_workgroups",
            "moe_mxfp4_a16w4_workspace_bytes", "moe_mxfp4_forward_a16w4",
-           "moe_mxfp4_forward_a16w4_debug")
+           "moe_mxfp4_forward_a16w4_debug", "moe_mxfp4_persistent_workspace_bytes",
+           "moe_mxfp4_workspace_init", "moe_mxfp4_persistent_workgroups",
+           "moe_mxfp4_forward_persistent", "moe_mxfp4_forward_persistent_debug")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -399,6 +410,92 @@ def moe_mxfp4_forward_a16w4_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids
     _check("moe_mxfp4_forward_a16w4_debug",
            _lib.moe_mxfp4_forward_a16w4_debug(*args, hp, ev, clk, _stream(stream)))
     return {"out": out, "h": h[:M * topk] if h is not None else None}
+
+
+def moe_mxfp4_persistent_workspace_bytes(M, D, I, E, topk) -> int:
+    """Workspace of the persistent forward (0: shape not supported by it)."""
+    return int(_lib.moe_mxfp4_persistent_workspace_bytes(M, D, I, E, topk))
+
+
+def moe_mxfp4_workspace_init(workspace, stream=None):
+    """Fill a workspace with zeros (enqueued): the persistent forward's set-up."""
+    _check("moe_mxfp4_workspace_init",
+           _lib.moe_mxfp4_workspace_init(_ptr(workspace, torch.uint8, None, "workspace"),
+                                         workspace.numel(), _stream(stream)))
+
+
+def moe_mxfp4_persistent_workgroups(M) -> int:
+    return int(_lib.moe_mxfp4_persistent_workgroups(M))
+
+
+def alloc_workspace_persistent(M, D, I, E, topk, device="cuda", stream=None):
+    """A persistent-forward workspace, initialized."""
+    n = moe_mxfp4_persistent_workspace_bytes(M, D, I, E, topk)
+    if n == 0:
+        raise MoeMxfp4Error("moe_mxfp4_persistent_workspace_bytes", 2)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_mxfp4_workspace_init(ws, stream)
+    return ws
+
+
+def persistent_error_word(workspace) -> int:
+    """The workspace's barrier error word (nonzero after a timed-out wait)."""
+    return int(workspace[4:8].view(torch.int32).item())
+
+
+def moe_mxfp4_forward_persistent(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w,
+                                 out=None, workspace=None, stream=None):
+    """The forward in one persistent launch (few tokens); returns out."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        E, D, I = _weight_dims(w13, w2)
+        workspace = alloc_workspace_persistent(hidden.shape[0], D, I, E, topk_ids.shape[1],
+                                               hidden.device, stream)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_persistent",
+           _lib.moe_mxfp4_forward_persistent(*args, _stream(stream)))
+    return out
+
+
+def moe_mxfp4_forward_persistent_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w,
+                                       out=None, workspace=None, intermediates=True,
+                                       kernel_events=None, clock=None, stream=None):
+    """The persistent forward with exports: dict(out, h, a2_codes, a2_scales)
+    by route (intermediates=True), kernel_events (8 raw hipEvent_t handles or
+    None; the launch is entry pair 1) and clock (device int64 of
+    2 * moe_mxfp4_persistent_workgroups(M), or None)."""
+    E, D, I = _weight_dims(w13, w2)
+    M, topk = topk_ids.shape
+    dev = hidden.device
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        workspace = alloc_workspace_persistent(M, D, I, E, topk, dev, stream)
+    R = max(M * topk, 1)
+    h = a2c = a2s = None
+    if intermediates:
+        h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        a2c = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+        a2s = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+    ev = None
+    if kernel_events is not None:
+        if len(kernel_events) != 2 * len(LAUNCHES):
+            raise ValueError(f"kernel_events: expected {2 * len(LAUNCHES)} entries")
+        ev = (ctypes.c_void_p * len(kernel_events))(
+            *[ctypes.c_void_p(e) if e else None for e in kernel_events])
+    clk = None
+    if clock is not None:
+        need = 2 * moe_mxfp4_persistent_workgroups(M)
+        if (clock.dtype != torch.int64 or clock.numel() < need or not clock.is_cuda
+                or not clock.is_contiguous()):
+            raise TypeError(f"clock: expected a contiguous device int64 tensor of {need}")
+        clk = _ptr(clock, name="clock", device=dev)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_persistent_debug",
+           _lib.moe_mxfp4_forward_persistent_debug(*args, _ptr(h), _ptr(a2c), _ptr(a2s), ev, clk,
+                                                   _stream(stream)))
+    return {"out": out, "h": h, "a2_codes": a2c, "a2_scales": a2s, "workspace": workspace}
 
 
 class MoeMxfp4:

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "prologue.hip", "prepare.hip", "gemm1.hip", "gemm2.hip", "gemm_tile.hip", "direct.hip"]
+SOURCES = ["api.hip", "prologue.hip", "prepare.hip", "gemm1.hip", "gemm2.hip", "gemm_tile.hip", "direct.hip",
+           "decode_fused.hip"]
 ARCH = "gfx950"
 
 

@@ -30,6 +30,11 @@ constexpr int64_t kMaxRoutes = int64_t(1) << 24;
 std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_cu_count[kMaxDevices];
 std::atomic<uintptr_t> g_scratch[kMaxDevices];  // device address of `scratch` per device
+std::atomic<int> g_clock_khz[kMaxDevices];      // constant-rate clock of each device
+// Longest wait of the persistent forward's grid barrier before it gives up,
+// and the bytes its words take at the start of that forward's workspace.
+constexpr uint64_t kBarrierTimeoutMs = 50;
+constexpr size_t kBarrierBytes = 2048;
 
 }  // namespace
 
@@ -46,7 +51,7 @@ namespace {
 // Checks that the current device is gfx950; returns its CU count in *n_cu
 // and, when asked, the device address of its `scratch` array.  The first call
 // on a device also lifts the kernels' LDS limits and takes that address.
-int device_check(int* n_cu, uint8_t** scratch_out = nullptr)
+int device_check(int* n_cu, uint8_t** scratch_out = nullptr, int* clock_khz = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_MXFP4_ERR_HIP;
@@ -59,8 +64,13 @@ int device_check(int* n_cu, uint8_t** scratch_out = nullptr)
         g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         if (st == 1) {
             if (moe::route_allow_lds(int(moe::route_lds_bytes(kMaxE))) != hipSuccess ||
-                moe::tile_allow_lds() != hipSuccess || moe::direct_allow_lds() != hipSuccess)
+                moe::tile_allow_lds() != hipSuccess || moe::direct_allow_lds() != hipSuccess ||
+                moe::fused_allow_lds() != hipSuccess)
                 return MOE_MXFP4_ERR_HIP;
+            int khz = 0;
+            if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+                return MOE_MXFP4_ERR_HIP;
+            g_clock_khz[dev].store(khz, std::memory_order_relaxed);
             void* p = nullptr;
             if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
                 return MOE_MXFP4_ERR_HIP;
@@ -70,6 +80,7 @@ int device_check(int* n_cu, uint8_t** scratch_out = nullptr)
     }
     if (st != 1) return MOE_MXFP4_ERR_UNSUPPORTED;
     *n_cu = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (clock_khz) *clock_khz = g_clock_khz[dev].load(std::memory_order_relaxed);
     if (scratch_out)
         *scratch_out = reinterpret_cast<uint8_t*>(g_scratch[dev].load(std::memory_order_relaxed));
     return MOE_MXFP4_OK;
@@ -126,8 +137,11 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, barrier, total;
 };
+
+// Forward variants that share the route-indexed kernels' workspace layout.
+enum class Variant { Plain, A16W4, Persistent };
 
 // The A16W4 forward runs the route-indexed kernels for any routing within
 // their limits.
@@ -137,17 +151,21 @@ bool a16w4_shape_ok(int M, int E, int topk)
            int64_t(M) * topk <= moe::kDirectMaxRoutes && E <= moe::kDirectMaxE;
 }
 
-Layout layout(int M, int D, int I, int E, int topk, bool a16 = false)
+Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
 {
+    const bool a16 = v == Variant::A16W4;
     Layout L;
-    L.path = a16 ? MOE_MXFP4_PATH_DIRECT : choose_path(M, E, topk);
+    L.path = v != Variant::Plain ? MOE_MXFP4_PATH_DIRECT : choose_path(M, E, topk);
     L.bm = choose_block_m(M, E, topk);
     L.cap = route_capacity(M, E, topk, L.bm);
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.block_info = 0;
-    L.h16 = 0;
+    L.h16 = L.barrier = 0;
+    // the persistent forward's barrier words come first (offset 0), so that
+    // its init call needs nothing but the workspace pointer
+    if (v == Variant::Persistent) L.barrier = take(kBarrierBytes);
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
         // rows indexed by route: a2 codes and scales row-major (A16W4: h in
         // bf16); the expert slots with their token -> route tables
@@ -237,9 +255,10 @@ moe::KernelEvents kernel_events(const DebugOut* d, int i)
 int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_scale,
                    const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                    const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
-                   uint8_t* ws, const Layout& L, int n_cu, const DebugOut* dbg, bool a16,
-                   hipStream_t stream)
+                   uint8_t* ws, const Layout& L, int n_cu, int clock_khz, const DebugOut* dbg,
+                   Variant v, hipStream_t stream)
 {
+    const bool a16 = v == Variant::A16W4;
     moe::DirectArgs a{hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, ws + L.a2q,
                       ws + L.a2s, reinterpret_cast<int32_t*>(ws + L.slot_expert),
                       reinterpret_cast<int32_t*>(ws + L.slot_layers),
@@ -248,12 +267,20 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
                       dbg ? dbg->h : nullptr, M, D, I, E, topk,
                       dbg ? dbg->stage1_clock : nullptr,
                       a16 ? reinterpret_cast<uint16_t*>(ws + L.h16) : nullptr};
-    (void)n_cu;
-    // two launches: no prologue, and the slot sum is part of stage 2
-    hipError_t e = moe::launch_gemm1_direct(a, stream, kernel_events(dbg, 1));
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
-    e = moe::launch_gemm2_direct(a, stream, kernel_events(dbg, 2));
-    if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    hipError_t e;
+    if (v == Variant::Persistent) {
+        // one launch: stage 1, the grid barrier, stage 2
+        e = moe::launch_decode_fused(a, reinterpret_cast<uint32_t*>(ws + L.barrier), n_cu,
+                                     uint64_t(clock_khz) * kBarrierTimeoutMs, stream,
+                                     kernel_events(dbg, 1));
+        if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    } else {
+        // two launches: no prologue, and the slot sum is part of stage 2
+        e = moe::launch_gemm1_direct(a, stream, kernel_events(dbg, 1));
+        if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+        e = moe::launch_gemm2_direct(a, stream, kernel_events(dbg, 2));
+        if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
+    }
     if (dbg) {
         const int R = M * topk;
         if ((dbg->sorted_route || dbg->num_valid) &&
@@ -278,29 +305,29 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
                  const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
                  const float* topk_w, uint16_t* out, int M, int D, int I, int E, int topk,
                  void* workspace, size_t workspace_bytes, const DebugOut* dbg,
-                 hipStream_t stream, bool a16 = false, bool noalloc = false)
+                 hipStream_t stream, Variant v = Variant::Plain, bool noalloc = false)
 {
     int st = check_shape(M, D, I, E, topk);
     if (st) return st;
-    if (a16 && !a16w4_shape_ok(M, E, topk)) return MOE_MXFP4_ERR_UNSUPPORTED;
+    if (v != Variant::Plain && !a16w4_shape_ok(M, E, topk)) return MOE_MXFP4_ERR_UNSUPPORTED;
     if (M == 0) return MOE_MXFP4_OK;
     const void* ptrs[] = {hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out};
     for (const void* p : ptrs)
         if (!p || !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
     if (!noalloc && (!workspace || !aligned(workspace, 256))) return MOE_MXFP4_ERR_INVALID_ARG;
     if (noalloc) workspace_bytes = MOE_MXFP4_NOALLOC_SCRATCH_BYTES;
-    const Layout L = layout(M, D, I, E, topk, a16);
+    const Layout L = layout(M, D, I, E, topk, v);
     if (workspace_bytes < L.total) return MOE_MXFP4_ERR_WORKSPACE;
-    int n_cu = 0;
+    int n_cu = 0, clock_khz = 0;
     uint8_t* scratch_ptr = nullptr;
-    st = device_check(&n_cu, noalloc ? &scratch_ptr : nullptr);
+    st = device_check(&n_cu, noalloc ? &scratch_ptr : nullptr, &clock_khz);
     if (st) return st;
     if (noalloc) workspace = scratch_ptr;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (L.path == MOE_MXFP4_PATH_DIRECT)
         return forward_direct(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I,
-                              E, topk, ws, L, n_cu, dbg, a16, stream);
+                              E, topk, ws, L, n_cu, clock_khz, dbg, v, stream);
     int32_t* sorted_route = reinterpret_cast<int32_t*>(ws + L.sorted_route);
     float* sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
     int32_t* block_expert = reinterpret_cast<int32_t*>(ws + L.block_expert);
@@ -485,7 +512,7 @@ MOE_API int moe_mxfp4_forward_noalloc(const uint16_t* hidden, const uint8_t* w13
                                       int E, int topk, hipStream_t stream)
 {
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
-                        topk, nullptr, 0, nullptr, stream, false, true);
+                        topk, nullptr, 0, nullptr, stream, Variant::Plain, true);
 }
 
 MOE_API int moe_mxfp4_forward_debug(const uint16_t* hidden, const uint8_t* w13,
@@ -554,7 +581,7 @@ MOE_API int moe_mxfp4_forward_profiled(const uint16_t* hidden, const uint8_t* w1
 MOE_API size_t moe_mxfp4_a16w4_workspace_bytes(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk) || !a16w4_shape_ok(M, E, topk)) return 0;
-    return layout(M, D, I, E, topk, true).total;
+    return layout(M, D, I, E, topk, Variant::A16W4).total;
 }
 
 MOE_API int moe_mxfp4_forward_a16w4(const uint16_t* hidden, const uint8_t* w13,
@@ -565,7 +592,7 @@ MOE_API int moe_mxfp4_forward_a16w4(const uint16_t* hidden, const uint8_t* w13,
                                     hipStream_t stream)
 {
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
-                        topk, workspace, workspace_bytes, nullptr, stream, true);
+                        topk, workspace, workspace_bytes, nullptr, stream, Variant::A16W4);
 }
 
 MOE_API int moe_mxfp4_forward_a16w4_debug(const uint16_t* hidden, const uint8_t* w13,
@@ -581,5 +608,60 @@ MOE_API int moe_mxfp4_forward_a16w4_debug(const uint16_t* hidden, const uint8_t*
         return MOE_MXFP4_ERR_INVALID_ARG;
     DebugOut d{nullptr, nullptr, h, nullptr, nullptr, kernel_events, stage1_clock};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
-                        topk, workspace, workspace_bytes, &d, stream, true);
+                        topk, workspace, workspace_bytes, &d, stream, Variant::A16W4);
+}
+
+MOE_API size_t moe_mxfp4_persistent_workspace_bytes(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk) || !a16w4_shape_ok(M, E, topk)) return 0;
+    return layout(M, D, I, E, topk, Variant::Persistent).total;
+}
+
+MOE_API int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes % 256 != 0)
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    if (workspace_bytes == 0) return MOE_MXFP4_OK;
+    int n_cu = 0;
+    const int st = device_check(&n_cu);
+    if (st) return st;
+    return hip_status(moe::launch_zero_fill(static_cast<uint8_t*>(workspace), workspace_bytes,
+                                            n_cu, stream));
+}
+
+MOE_API int64_t moe_mxfp4_persistent_workgroups(int M)
+{
+    int n_cu = 0;
+    if (M < 1 || M > moe::kDirectMaxTokens || device_check(&n_cu)) return 0;
+    return moe::fused_grid(M, n_cu);
+}
+
+MOE_API int moe_mxfp4_forward_persistent(const uint16_t* hidden, const uint8_t* w13,
+                                         const uint8_t* w13_scale, const uint8_t* w2,
+                                         const uint8_t* w2_scale, const int32_t* topk_ids,
+                                         const float* topk_w, uint16_t* out, int M, int D, int I,
+                                         int E, int topk, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream)
+{
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, nullptr, stream, Variant::Persistent);
+}
+
+MOE_API int moe_mxfp4_forward_persistent_debug(const uint16_t* hidden, const uint8_t* w13,
+                                               const uint8_t* w13_scale, const uint8_t* w2,
+                                               const uint8_t* w2_scale, const int32_t* topk_ids,
+                                               const float* topk_w, uint16_t* out, int M, int D,
+                                               int I, int E, int topk, void* workspace,
+                                               size_t workspace_bytes, uint16_t* h,
+                                               uint8_t* a2_codes, uint8_t* a2_scales,
+                                               hipEvent_t* kernel_events, uint64_t* clock,
+                                               hipStream_t stream)
+{
+    const void* opt[] = {h, a2_codes, a2_scales};
+    for (const void* p : opt)
+        if (p && !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (clock && !aligned(clock, 8)) return MOE_MXFP4_ERR_INVALID_ARG;
+    DebugOut d{nullptr, nullptr, h, a2_codes, a2_scales, kernel_events, clock};
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, &d, stream, Variant::Persistent);
 }

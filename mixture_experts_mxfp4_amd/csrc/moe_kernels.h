@@ -158,6 +158,16 @@ hipError_t launch_gemm2_direct(const DirectArgs& a, hipStream_t stream, const Ke
 hipError_t launch_direct_rows(const int32_t* ids, int R, int E, int32_t* row_route,
                               int32_t* num_valid, hipStream_t stream);
 
+// Single persistent launch of the route-indexed forward (decode_fused.hip):
+// stage 1, a grid barrier on bar[0..1] (zero before the first call, zero
+// again after each completed call; bar[2] becomes nonzero if a wait timed
+// out), stage 2.  MXFP4 activations only (a.h16 must be null).
+hipError_t fused_allow_lds();      // LDS limits and per-CU occupancy, once per device
+int fused_grid(int M, int n_cu);   // workgroups of the launch (0 before fused_allow_lds)
+hipError_t launch_zero_fill(uint8_t* p, size_t bytes, int n_cu, hipStream_t stream);
+hipError_t launch_decode_fused(const DirectArgs& a, uint32_t* bar, int n_cu, uint64_t timeout_ticks,
+                               hipStream_t stream, const KernelEvents& ev = {});
+
 hipError_t launch_reduce_slots(const uint16_t* partial, const int32_t* ids, int M, int D, int E,
                                int topk, uint16_t* out, int n_cu, hipStream_t stream,
                                const KernelEvents& ev = {});
