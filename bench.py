@@ -221,7 +221,7 @@ def workload_of(args):
     return inputs.Workload(f"shape_M{M}_E{E}_I{I}", M, 7168, I, E, 8, "uniform", 7)
 
 
-def measure(w, args, a16=False, persistent=False):
+def measure(w, args, a16=False, persistent=False, splitk=False):
     """One workload on the GPU: K timed forwards after W untimed ones, then the
     kernel-timing pass.  Returns the timing and roofline figures (and the
     float inputs, for the CPU leg)."""
@@ -266,6 +266,20 @@ def measure(w, args, a16=False, persistent=False):
             binding.moe_mxfp4_forward_persistent_debug(h_d, *wset, ids_d, tw_d, out, ws,
                                                        intermediates=False, kernel_events=ev,
                                                        clock=clk)
+    elif splitk:
+        if binding.moe_mxfp4_splitk_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
+            raise SystemExit(f"bench.py: the split-K forward does not run {w.name} (M={w.M})")
+        ws = binding.alloc_workspace_splitk(w.M, w.D, w.I, w.E, w.topk, dev)
+        path = binding.PATH_DIRECT
+        n_wg = binding.splitk_stage1_workgroups(w.M, w.I, w.E, w.topk)
+
+        def forward(wset):
+            binding.moe_mxfp4_forward_splitk(h_d, *wset, ids_d, tw_d, out, ws)
+
+        def forward_timed(wset, ev, clk=None):
+            binding.moe_mxfp4_forward_splitk_debug(h_d, *wset, ids_d, tw_d, out, ws,
+                                                   intermediates=False, kernel_events=ev,
+                                                   stage1_clock=clk)
     elif a16:
         if binding.moe_mxfp4_a16w4_workspace_bytes(w.M, w.D, w.I, w.E, w.topk) == 0:
             raise SystemExit(f"bench.py: the A16W4 forward does not run {w.name} (M={w.M})")
@@ -292,7 +306,8 @@ def measure(w, args, a16=False, persistent=False):
     torch.cuda.synchronize()
     path_name = "persistent" if persistent else binding.PATH_NAMES[path]
     launches = (1,) if persistent else binding.PATH_LAUNCHES[path]
-    workload_id = w.name + ("_a16w4" if a16 else "") + ("_persistent" if persistent else "")
+    workload_id = (w.name + ("_a16w4" if a16 else "") + ("_persistent" if persistent else "")
+                   + ("_splitk" if splitk else ""))
 
     # buffers of the kernel-timing pass, allocated up front so that no host
     # work separates the passes
@@ -443,7 +458,7 @@ def run(args):
 
     w = workload_of(args)
     a16 = args.a16w4
-    r = measure(w, args, a16, persistent=args.persistent)
+    r = measure(w, args, a16, persistent=args.persistent, splitk=args.splitk)
     hidden, ids, tw, w13f, w2f = r.pop("inputs")
     alg, sec, unit = r["alg"], r["sec"], r["unit"]
 
@@ -463,7 +478,7 @@ def run(args):
 
     # the other D = 7168 workloads of the metric, timed with the same K and W
     extra = {}
-    if not args.headline_only and not args.shape and not a16 and not args.persistent:
+    if not args.headline_only and not args.shape and not a16 and not args.persistent and not args.splitk:
         from mixture_experts_mxfp4_amd import inputs
         for name in ("small_batch", "prefill", "large_prefill"):
             if name == w.name:
@@ -494,7 +509,8 @@ def run(args):
                                f": M={w.M} D={w.D} I={w.I} E={w.E} top{w.topk} "
                                f"({w.n_routed} routed {w.routing} + shared expert {w.E - 1})",
                    "mode": "a16w4" if a16 else "a4w4",
-                   "variant": "persistent (one launch)" if args.persistent else "default",
+                   "variant": ("persistent (one launch)" if args.persistent else
+                               "split-K stage 1" if args.splitk else "default"),
                    "M": w.M, "D": w.D, "I": w.I, "E": w.E, "topk": w.topk,
                    "routing": w.routing, "seed": w.seed, "global_batch": w.M,
                    "parallelism": "single GPU", "path": r["path_name"],
@@ -663,6 +679,8 @@ def main():
                    help="the A16W4 forward (bf16 activations; up to 32 tokens)")
     p.add_argument("--persistent", action="store_true",
                    help="the persistent forward (one launch; up to 32 tokens)")
+    p.add_argument("--splitk", action="store_true",
+                   help="the forward with a split-K stage 1 (up to 32 tokens)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--headline-only", action="store_true",

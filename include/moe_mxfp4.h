@@ -412,7 +412,8 @@ size_t moe_mxfp4_persistent_workspace_bytes(int M, int D, int I, int E, int topk
 
 /* Fills a workspace with zeros (one kernel on `stream`, plain stores, no
  * memset, so it may be captured in a graph): the set-up the persistent
- * forward needs once per workspace (and again after a timed-out call).
+ * and split-K forwards need once per workspace (the persistent one again
+ * after a timed-out call).
  * workspace_bytes must be a multiple of 256 (every workspace size the
  * library reports is).  INVALID_ARG for a null or misaligned pointer or a
  * bad size. */
@@ -451,6 +452,54 @@ int moe_mxfp4_forward_persistent_debug(const uint16_t* hidden,
                                        uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
                                        hipEvent_t* kernel_events, uint64_t* clock,
                                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Split-K forward: the route-indexed (few-token) forward with stage 1's
+ * contraction over D split across two workgroups per unit.
+ *
+ * Passage: submission 754773's per-shape override table (`_flower_shape_overrides`)
+ * gives every 16-token shape ksplit = 2, and the b12x CuTeDSL W4A16 kernel
+ * splits its persistent GEMM's K across CTAs (`_run_persistent_gemm`) and
+ * merges the fp32 partial tiles under a per-tile lock (`_finish_tile`).
+ * Here each stage-1 unit (expert, pair of 64-row gate_up groups) runs on two
+ * workgroups, each over half of D; each writes its fp32 sums of gate and up
+ * per route, and the second to finish adds the two halves in part order
+ * (deterministic), applies SiLU(gate) * up and the MXFP4 requant.  Stage 2 is
+ * the default forward's.  Same operation, arguments, limits (those of the
+ * A16W4 forward) and error behaviour as moe_mxfp4_forward_persistent, with
+ * this variant's own workspace size.
+ *
+ * Workspace: moe_mxfp4_splitk_workspace_bytes(...) bytes, 256-byte aligned,
+ * zero before its first use (moe_mxfp4_workspace_init, once): its first
+ * words count the finished parts of each unit and every call leaves them at
+ * zero again.  Concurrent calls need different workspaces.
+ * ------------------------------------------------------------------------- */
+size_t moe_mxfp4_splitk_workspace_bytes(int M, int D, int I, int E, int topk);
+
+int moe_mxfp4_forward_splitk(const uint16_t* hidden,
+                             const uint8_t* w13, const uint8_t* w13_scale,
+                             const uint8_t* w2, const uint8_t* w2_scale,
+                             const int32_t* topk_ids, const float* topk_w,
+                             uint16_t* out,
+                             int M, int D, int I, int E, int topk,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* moe_mxfp4_forward_splitk with exports (each may be NULL): h, a2_codes,
+ * a2_scales by route as in moe_mxfp4_forward_persistent_debug;
+ * kernel_events as in moe_mxfp4_forward_profiled (launches 1 and 2);
+ * stage1_clock: device uint64 [2 * 2 * (I/64) * min(E, M*topk)], 8-byte
+ * aligned, each stage-1 workgroup's start and end. */
+int moe_mxfp4_forward_splitk_debug(const uint16_t* hidden,
+                                   const uint8_t* w13, const uint8_t* w13_scale,
+                                   const uint8_t* w2, const uint8_t* w2_scale,
+                                   const int32_t* topk_ids, const float* topk_w,
+                                   uint16_t* out,
+                                   int M, int D, int I, int E, int topk,
+                                   void* workspace, size_t workspace_bytes,
+                                   uint16_t* h, uint8_t* a2_codes, uint8_t* a2_scales,
+                                   hipEvent_t* kernel_events, uint64_t* stage1_clock,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,12 @@ _lib.moe_mxfp4_forward_persistent.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
 _lib.moe_mxfp4_forward_persistent.restype = _I
 _lib.moe_mxfp4_forward_persistent_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
 _lib.moe_mxfp4_forward_persistent_debug.restype = _I
+_lib.moe_mxfp4_splitk_workspace_bytes.argtypes = [_I] * 5
+_lib.moe_mxfp4_splitk_workspace_bytes.restype = _SZ
+_lib.moe_mxfp4_forward_splitk.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P]
+_lib.moe_mxfp4_forward_splitk.restype = _I
+_lib.moe_mxfp4_forward_splitk_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] * 5 + [_P]
+_lib.moe_mxfp4_forward_splitk_debug.restype = _I
 
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_block_m",
            "moe_mxfp4_path", "moe_mxfp4_launch_count",
@@ -72,7 +78,9 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_bl
            "moe_mxfp4_a16w4_workspace_bytes", "moe_mxfp4_forward_a16w4",
            "moe_mxfp4_forward_a16w4_debug", "moe_mxfp4_persistent_workspace_bytes",
            "moe_mxfp4_workspace_init", "moe_mxfp4_persistent_workgroups",
-           "moe_mxfp4_forward_persistent", "moe_mxfp4_forward_persistent_debug")
+           "moe_mxfp4_forward_persistent", "moe_mxfp4_forward_persistent_debug",
+           "moe_mxfp4_splitk_workspace_bytes", "moe_mxfp4_forward_splitk",
+           "moe_mxfp4_forward_splitk_debug")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -495,6 +503,78 @@ def moe_mxfp4_forward_persistent_debug(hidden, w13, w13_scale, w2, w2_scale, top
     _check("moe_mxfp4_forward_persistent_debug",
            _lib.moe_mxfp4_forward_persistent_debug(*args, _ptr(h), _ptr(a2c), _ptr(a2s), ev, clk,
                                                    _stream(stream)))
+    return {"out": out, "h": h, "a2_codes": a2c, "a2_scales": a2s, "workspace": workspace}
+
+
+def moe_mxfp4_splitk_workspace_bytes(M, D, I, E, topk) -> int:
+    """Workspace of the split-K forward (0: shape not supported by it)."""
+    return int(_lib.moe_mxfp4_splitk_workspace_bytes(M, D, I, E, topk))
+
+
+def splitk_stage1_workgroups(M, I, E, topk) -> int:
+    return 2 * (I // 64) * min(E, M * topk) if M > 0 else 0
+
+
+def alloc_workspace_splitk(M, D, I, E, topk, device="cuda", stream=None):
+    """A split-K forward workspace, zero-filled (its part counters start at zero)."""
+    n = moe_mxfp4_splitk_workspace_bytes(M, D, I, E, topk)
+    if n == 0:
+        raise MoeMxfp4Error("moe_mxfp4_splitk_workspace_bytes", 2)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_mxfp4_workspace_init(ws, stream)
+    return ws
+
+
+def moe_mxfp4_forward_splitk(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out=None,
+                             workspace=None, stream=None):
+    """The forward with a split-K stage 1 (few tokens); returns out."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        E, D, I = _weight_dims(w13, w2)
+        workspace = alloc_workspace_splitk(hidden.shape[0], D, I, E, topk_ids.shape[1],
+                                           hidden.device, stream)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_splitk", _lib.moe_mxfp4_forward_splitk(*args, _stream(stream)))
+    return out
+
+
+def moe_mxfp4_forward_splitk_debug(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w,
+                                   out=None, workspace=None, intermediates=True,
+                                   kernel_events=None, stage1_clock=None, stream=None):
+    """The split-K forward with exports: dict(out, h, a2_codes, a2_scales,
+    workspace); kernel_events / stage1_clock as in moe_mxfp4_forward_profiled
+    (stage1_clock of 2 * splitk_stage1_workgroups(...) int64)."""
+    E, D, I = _weight_dims(w13, w2)
+    M, topk = topk_ids.shape
+    dev = hidden.device
+    if out is None:
+        out = torch.empty_like(hidden)
+    if workspace is None:
+        workspace = alloc_workspace_splitk(M, D, I, E, topk, dev, stream)
+    R = max(M * topk, 1)
+    h = a2c = a2s = None
+    if intermediates:
+        h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        a2c = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+        a2s = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+    ev = None
+    if kernel_events is not None:
+        if len(kernel_events) != 2 * len(LAUNCHES):
+            raise ValueError(f"kernel_events: expected {2 * len(LAUNCHES)} entries")
+        ev = (ctypes.c_void_p * len(kernel_events))(
+            *[ctypes.c_void_p(e) if e else None for e in kernel_events])
+    clk = None
+    if stage1_clock is not None:
+        need = 2 * splitk_stage1_workgroups(M, I, E, topk)
+        if (stage1_clock.dtype != torch.int64 or stage1_clock.numel() < need
+                or not stage1_clock.is_cuda or not stage1_clock.is_contiguous()):
+            raise TypeError(f"stage1_clock: expected a contiguous device int64 tensor of {need}")
+        clk = _ptr(stage1_clock, name="stage1_clock", device=dev)
+    args, _ = _forward_args(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, workspace)
+    _check("moe_mxfp4_forward_splitk_debug",
+           _lib.moe_mxfp4_forward_splitk_debug(*args, _ptr(h), _ptr(a2c), _ptr(a2s), ev, clk,
+                                               _stream(stream)))
     return {"out": out, "h": h, "a2_codes": a2c, "a2_scales": a2s, "workspace": workspace}
 
 

@@ -137,11 +137,13 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, barrier, total;
+        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, barrier,
+        split_ctr, part, total;
 };
 
 // Forward variants that share the route-indexed kernels' workspace layout.
-enum class Variant { Plain, A16W4, Persistent };
+enum class Variant { Plain, A16W4, Persistent, SplitK };
+constexpr int kSplitParts = 2;     // K parts of a split-K stage-1 unit
 
 // The A16W4 forward runs the route-indexed kernels for any routing within
 // their limits.
@@ -162,10 +164,13 @@ Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.block_info = 0;
-    L.h16 = L.barrier = 0;
-    // the persistent forward's barrier words come first (offset 0), so that
-    // its init call needs nothing but the workspace pointer
+    L.h16 = L.barrier = L.split_ctr = L.part = 0;
+    // the persistent forward's barrier words and the split-K counters come
+    // first (offset 0)
     if (v == Variant::Persistent) L.barrier = take(kBarrierBytes);
+    if (v == Variant::SplitK)
+        L.split_ctr = take(sizeof(uint32_t) * size_t(moe::direct_slots(M, E, topk)) *
+                           size_t(moe::direct_stage1_x(I)));
     if (L.path == MOE_MXFP4_PATH_DIRECT) {
         // rows indexed by route: a2 codes and scales row-major (A16W4: h in
         // bf16); the expert slots with their token -> route tables
@@ -183,6 +188,7 @@ Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
         L.slot_layers = take(sizeof(int32_t) * slots);
         L.route_of = take(sizeof(int32_t) * size_t(topk) * slots * size_t(M));
         L.n_active = take(sizeof(int32_t));
+        if (v == Variant::SplitK) L.part = take(sizeof(float) * size_t(kSplitParts) * R * 2 * size_t(I));
         L.total = off;
         return L;
     }
@@ -267,6 +273,11 @@ int forward_direct(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w1
                       dbg ? dbg->h : nullptr, M, D, I, E, topk,
                       dbg ? dbg->stage1_clock : nullptr,
                       a16 ? reinterpret_cast<uint16_t*>(ws + L.h16) : nullptr};
+    if (v == Variant::SplitK) {
+        a.ks_parts = kSplitParts;
+        a.part = reinterpret_cast<float*>(ws + L.part);
+        a.split_ctr = reinterpret_cast<uint32_t*>(ws + L.split_ctr);
+    }
     hipError_t e;
     if (v == Variant::Persistent) {
         // one launch: stage 1, the grid barrier, stage 2
@@ -664,4 +675,39 @@ MOE_API int moe_mxfp4_forward_persistent_debug(const uint16_t* hidden, const uin
     DebugOut d{nullptr, nullptr, h, a2_codes, a2_scales, kernel_events, clock};
     return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
                         topk, workspace, workspace_bytes, &d, stream, Variant::Persistent);
+}
+
+MOE_API size_t moe_mxfp4_splitk_workspace_bytes(int M, int D, int I, int E, int topk)
+{
+    if (check_shape(M, D, I, E, topk) || !a16w4_shape_ok(M, E, topk)) return 0;
+    return layout(M, D, I, E, topk, Variant::SplitK).total;
+}
+
+MOE_API int moe_mxfp4_forward_splitk(const uint16_t* hidden, const uint8_t* w13,
+                                     const uint8_t* w13_scale, const uint8_t* w2,
+                                     const uint8_t* w2_scale, const int32_t* topk_ids,
+                                     const float* topk_w, uint16_t* out, int M, int D, int I, int E,
+                                     int topk, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream)
+{
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, nullptr, stream, Variant::SplitK);
+}
+
+MOE_API int moe_mxfp4_forward_splitk_debug(const uint16_t* hidden, const uint8_t* w13,
+                                           const uint8_t* w13_scale, const uint8_t* w2,
+                                           const uint8_t* w2_scale, const int32_t* topk_ids,
+                                           const float* topk_w, uint16_t* out, int M, int D, int I,
+                                           int E, int topk, void* workspace,
+                                           size_t workspace_bytes, uint16_t* h, uint8_t* a2_codes,
+                                           uint8_t* a2_scales, hipEvent_t* kernel_events,
+                                           uint64_t* stage1_clock, hipStream_t stream)
+{
+    const void* opt[] = {h, a2_codes, a2_scales};
+    for (const void* p : opt)
+        if (p && !aligned(p, 16)) return MOE_MXFP4_ERR_INVALID_ARG;
+    if (stage1_clock && !aligned(stage1_clock, 8)) return MOE_MXFP4_ERR_INVALID_ARG;
+    DebugOut d{nullptr, nullptr, h, a2_codes, a2_scales, kernel_events, stage1_clock};
+    return forward_impl(hidden, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, M, D, I, E,
+                        topk, workspace, workspace_bytes, &d, stream, Variant::SplitK);
 }

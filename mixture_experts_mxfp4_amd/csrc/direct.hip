@@ -46,16 +46,18 @@ constexpr int kDirThreads = 256;
 
 // ---------------------------------------------------------------- stage 1 --
 //
-// Workgroup (x, y) of four waves runs stage-1 unit (x, y) (stage1_unit,
-// direct_common.h).
-template <int U, int NG, bool A16>
+// Workgroup (x, y) of four waves runs stage-1 unit (x % X, y) (stage1_unit,
+// direct_common.h; X = direct_stage1_x(I)), K part x / X of KS.
+template <int U, int NG, bool A16, int KS = 1>
 __global__ void __launch_bounds__(kDirThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gemm1_direct_kernel(DirectArgs a)
 {
     __shared__ Stage1Lds<NG> L;
     span_begin(a.clk);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    stage1_unit<U, NG, A16>(a, blockIdx.x, blockIdx.y, wave, L, [] { __syncthreads(); });
+    const int X = direct_stage1_x(a.I);
+    stage1_unit<U, NG, A16, KS>(a, blockIdx.x % X, blockIdx.y, wave, L, [] { __syncthreads(); },
+                                blockIdx.x / X);
     span_end(a.clk);
 }
 
@@ -276,9 +278,14 @@ hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const Ke
 {
     if (!direct_shape_ok(a)) return hipErrorInvalidValue;
     if (a.M == 0) return hipSuccess;
-    const dim3 grid(direct_stage1_x(a.I), direct_slots(a.M, a.E, a.topk));
+    if (a.ks_parts != 1 && (a.ks_parts != 2 || a.h16 || !a.part || !a.split_ctr))
+        return hipErrorInvalidValue;
+    const dim3 grid(direct_stage1_x(a.I) * a.ks_parts, direct_slots(a.M, a.E, a.topk));
     if (a.h16)
         MOE_LAUNCH((gemm1_direct_kernel<kG1Unroll, kDirectGroups, true>), grid,
+                   dim3(kDirThreads), 0, stream, ev, a);
+    else if (a.ks_parts == 2)
+        MOE_LAUNCH((gemm1_direct_kernel<kG1Unroll, kDirectGroups, false, 2>), grid,
                    dim3(kDirThreads), 0, stream, ev, a);
     else
         MOE_LAUNCH((gemm1_direct_kernel<kG1Unroll, kDirectGroups, false>), grid,

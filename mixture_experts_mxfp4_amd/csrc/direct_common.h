@@ -186,13 +186,62 @@ template <int NG>
 struct Stage1Lds {
     int32_t list[kDirectMaxRoutes];
     uint32_t bitmap[kDirectMaxE / 32];
-    int32_t n_list, e_sel, n_active;
+    int32_t n_list, e_sel, n_active, last;
     float red[4][NG][4][4][kWave];      // [wave][group][slice][i][lane]
 };
 
-template <int U, int NG, bool A16, class Sync>
+// Split-K partial sums of stage 1 (KS > 1), fp32, by route: for K part k,
+// route r, 64-row group c, 16-row slice q and column j of the slice,
+// part[((k * R + r) * (I/32) + c) * 64 + q * 16 + j].  They are written and
+// read with agent-coherent accesses (write-through; reads from the coherence
+// point), which is what lets the merging workgroup on another XCD see them
+// without cache maintenance.
+__device__ __forceinline__ int64_t split_part_off(int k, int64_t r, int R, int I, int c, int q, int j)
+{
+    return ((int64_t(k) * R + r) * (I / 32) + c) * 64 + q * 16 + j;
+}
+
+// The end of stage 1 for one lane's row of one 64-row group c, from the
+// group's four fp32 sums s4 (gate columns c*32 + lane%16 and +16, then the
+// matching up columns): h = bf16(silu(gate) * up), then (MXFP4 mode) the
+// requant of the 32 h of the row held by the 16 lanes of the DPP row, stored
+// by route; A16W4 stores h as bf16.  Every lane of the wave calls it (the
+// block maximum is a cross-lane reduction); lanes without a row store nothing.
+template <bool A16>
+__device__ __forceinline__ void stage1_finish(const DirectArgs& a, int64_t r, bool row_ok, int c,
+                                              const float (&s4)[4])
+{
+    const int lane = threadIdx.x % kWave;
+    const int I = a.I;
+    // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
+    const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
+    const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
+    if (a.h_dbg && row_ok) {
+        a.h_dbg[r * I + c * 32 + lane % 16] = uint16_t(h0);
+        a.h_dbg[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
+    }
+    if constexpr (A16) {
+        if (row_ok) {
+            a.h16[r * I + c * 32 + lane % 16] = uint16_t(h0);
+            a.h16[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
+        }
+        return;
+    }
+    // the row's MXFP4 group = columns c*32..+31, held by the 16 lanes of a DPP row
+    const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
+    const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
+    const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
+    const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
+    const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
+    if (row_ok && lane % 16 == 0) {
+        *reinterpret_cast<uint4*>(a.a2q + r * (I / 2) + c * 16) = make_uint4(qlo, d1, qhi, d3);
+        a.a2s[r * (I / 32) + c] = uint8_t(s);
+    }
+}
+
+template <int U, int NG, bool A16, int KS = 1, class Sync>
 __device__ __forceinline__ int stage1_unit(const DirectArgs& a, int x, int y, int wave,
-                                           Stage1Lds<NG>& L, Sync sync)
+                                           Stage1Lds<NG>& L, Sync sync, int ks = 0)
 {
     int32_t* list = L.list;
     const int lane = threadIdx.x % kWave;
@@ -206,7 +255,7 @@ __device__ __forceinline__ int stage1_unit(const DirectArgs& a, int x, int y, in
             L.e_sel = ew;
             L.n_active = active;
         }
-        if (x == 0) publish_slot(a, y, list, nw, ew, active);
+        if (x == 0 && ks == 0) publish_slot(a, y, list, nw, ew, active);
     }
     sync();
     const int n = L.n_list, e = L.e_sel, active = L.n_active;
@@ -221,7 +270,9 @@ __device__ __forceinline__ int stage1_unit(const DirectArgs& a, int x, int y, in
                                   NG * sgstride);
     const uint32_t hbytes = uint32_t(a.M) * D * 2;
     const auto hres = buffer_rsrc(a.hidden, hbytes);
-    const int kt_begin = wave * KT / 4, kt_end = (wave + 1) * KT / 4;
+    // K part ks of KS, split over the four waves
+    const int kp0 = ks * KT / KS, kp1 = (ks + 1) * KT / KS;
+    const int kt_begin = kp0 + wave * (kp1 - kp0) / 4, kt_end = kp0 + (wave + 1) * (kp1 - kp0) / 4;
 
 #pragma unroll 1
     for (int t0 = 0; t0 < n; t0 += 16) {
@@ -319,32 +370,55 @@ __device__ __forceinline__ int stage1_unit(const DirectArgs& a, int x, int y, in
             for (int q = 0; q < 4; ++q)
                 s4[q] = L.red[0][g][q][i][lane] + L.red[1][g][q][i][lane] + L.red[2][g][q][i][lane] +
                         L.red[3][g][q][i][lane];
-            // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
-            const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
-            const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
-            if (a.h_dbg && row_ok) {
-                a.h_dbg[r * I + c * 32 + lane % 16] = uint16_t(h0);
-                a.h_dbg[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
-            }
-            if constexpr (A16) {
-                if (row_ok) {
-                    a.h16[r * I + c * 32 + lane % 16] = uint16_t(h0);
-                    a.h16[r * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
-                }
-                continue;
-            }
-            // the row's MXFP4 group = columns c*32..+31, held by the 16 lanes of a DPP row
-            const uint32_t s = mx_scale_from_amax(row16_max(max(h0 & 0x7FFFu, h1 & 0x7FFFu)));
-            const uint32_t qlo = pack8_codes(mx_code(h0, s));   // bytes 0-3 on lane%16 == 0
-            const uint32_t qhi = pack8_codes(mx_code(h1, s));   // bytes 8-11
-            const uint32_t d1 = from_lane_plus<8>(qlo);         // bytes 4-7
-            const uint32_t d3 = from_lane_plus<8>(qhi);         // bytes 12-15
-            if (row_ok && lane % 16 == 0) {
-                *reinterpret_cast<uint4*>(a.a2q + r * (I / 2) + c * 16) = make_uint4(qlo, d1, qhi, d3);
-                a.a2s[r * (I / 32) + c] = uint8_t(s);
+            if constexpr (KS > 1) {
+                // this part's sums, written through for the merging workgroup
+                if (row_ok)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        __hip_atomic_store(a.part + split_part_off(ks, r, R, I, c, q, lane % 16), s4[q],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                stage1_finish<A16>(a, r, row_ok, c, s4);
             }
         }
         sync();                   // red is rewritten by the next row tile
+    }
+    if constexpr (KS > 1) {
+        // The last of the unit's KS workgroups to get here merges: every
+        // wave waits until its partial stores have completed (written
+        // through), then one thread counts this part in; the count returns
+        // to zero after the last part, ready for the next call.  The merge
+        // adds the parts in part order, so the result does not depend on
+        // which workgroup merges.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        sync();
+        if (wave == 0 && lane == 0) {
+            uint32_t* ctr = a.split_ctr + y * (I / (32 * NG)) + x;
+            const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            L.last = old == KS - 1;
+            if (old == KS - 1) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        sync();
+        if (!L.last) return active;
+#pragma unroll 1
+        for (int t0 = 0; t0 < n; t0 += 16) {
+            const int jr = t0 + 4 * (lane / 16) + wave;
+            if (jr >= n) continue;
+            const int64_t r = list[jr];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int c = x * NG + g;
+                float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KS; ++k)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        s4[q] += __hip_atomic_load(a.part + split_part_off(k, r, R, I, c, q, lane % 16),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                stage1_finish<A16>(a, r, true, c, s4);
+            }
+        }
     }
     return active;
 }

@@ -151,6 +151,13 @@ struct DirectArgs {
     // here, [M*topk][I] (a2q / a2s unused)
     uint16_t* h16 = nullptr;
     int h_lds = 0;                 // stage 2: bytes of h it stages in LDS (set by its launcher)
+    // split-K stage 1 (ks_parts > 1): each unit's K in ks_parts parts on as
+    // many workgroups, fp32 partial sums in `part` ([ks_parts][M*topk][2I]),
+    // merged by the last part to finish, counted in split_ctr
+    // ([slots][stage-1 x extent], zero before the first call, zero again after)
+    int ks_parts = 1;
+    float* part = nullptr;
+    uint32_t* split_ctr = nullptr;
 };
 hipError_t direct_allow_lds();     // lift the dynamic-LDS limit of the stage-2 kernels
 hipError_t launch_gemm1_direct(const DirectArgs& a, hipStream_t stream, const KernelEvents& ev = {});

@@ -63,6 +63,9 @@ _DRIVER = textwrap.dedent('''
     lib.moe_mxfp4_persistent_workspace_bytes.argtypes = [I] * 5
     lib.moe_mxfp4_persistent_workspace_bytes.restype = SZ
     lib.moe_mxfp4_workspace_init.argtypes = [P, SZ, P]
+    lib.moe_mxfp4_forward_splitk.argtypes = fwd + [P]
+    lib.moe_mxfp4_splitk_workspace_bytes.argtypes = [I] * 5
+    lib.moe_mxfp4_splitk_workspace_bytes.restype = SZ
     shapes = []
     for M in (0, 1, 7, 16, 32, 33, 64, 1024, 4096, 1 << 21, 1 << 24):
         for D, Id in ((256, 256), (7168, 256), (7168, 2048), (65536, 65536), (500, 256)):
@@ -77,6 +80,7 @@ _DRIVER = textwrap.dedent('''
         lib.moe_mxfp4_launch_count(*s)
         lib.moe_mxfp4_stage1_workgroups(*s)
         lib.moe_mxfp4_persistent_workspace_bytes(*s)
+        lib.moe_mxfp4_splitk_workspace_bytes(*s)
         assert (path == 0) == (ws == 0) or s[0] == 0, s
         for bm in (1, 16, 256):
             lib.moe_mxfp4_route_capacity(s[0], s[3], s[4], bm)
@@ -102,6 +106,9 @@ _DRIVER = textwrap.dedent('''
     assert lib.moe_mxfp4_forward_persistent(*([null] * 8), 4, 512, 256, 9, 3, null, 1 << 30, null) == 1
     assert lib.moe_mxfp4_forward_persistent(*([ok] * 8), 64, 512, 256, 9, 3, ok, 1 << 30, null) == 2
     assert lib.moe_mxfp4_forward_persistent(*([ok] * 8), 4, 512, 256, 9, 3, ok, 16, null) == 3
+    assert lib.moe_mxfp4_forward_splitk(*([null] * 8), 4, 512, 256, 9, 3, null, 1 << 30, null) == 1
+    assert lib.moe_mxfp4_forward_splitk(*([ok] * 8), 64, 512, 256, 9, 3, ok, 1 << 30, null) == 2
+    assert lib.moe_mxfp4_forward_splitk(*([ok] * 8), 4, 512, 256, 9, 3, ok, 16, null) == 3
     assert lib.moe_mxfp4_workspace_init(null, 256, null) == 1
     assert lib.moe_mxfp4_workspace_init(ok, 100, null) == 1
     assert lib.moe_mxfp4_workspace_init(ok, 0, null) == 0
