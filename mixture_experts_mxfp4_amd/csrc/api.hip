@@ -435,7 +435,7 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
     if (L.path == MOE_MXFP4_PATH_DIRECT)
         return int64_t(moe::direct_stage1_x(I)) * moe::direct_slots(M, E, topk);
     if (L.path == MOE_MXFP4_PATH_TILED) return moe::tile_grid(2 * I / 256, int(L.nb));
-    return int64_t(I / (32 * moe::stream_stage1_groups(L.bm))) * L.nb;
+    return moe::tile_grid(I / (32 * moe::stream_stage1_groups(L.bm)), int(L.nb));
 }
 
 MOE_API int moe_mxfp4_wall_clock_khz(void)

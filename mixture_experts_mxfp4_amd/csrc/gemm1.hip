@@ -11,7 +11,8 @@
 //
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows (one
 // expert) and NG 64-row groups of the prepared gate_up weight; a group is 32
-// gate + 32 up columns = one MXFP4 group of h.  The four waves split the K
+// gate + 32 up columns = one MXFP4 group of h.  Workgroups take (group, block)
+// units in the XCD-aware order of xcd_unit.  The four waves split the K
 // dimension; each wave runs NG x RT x 4 MFMA tiles of 16x16x128, streaming its weight
 // fragments (1 KiB each, contiguous) with non-temporal loads and gathering the
 // block's activation rows by token id.  Partial sums meet in LDS; the epilogue
@@ -46,14 +47,14 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     constexpr int U = g1_unroll<RT, NG>();
     __shared__ float red[4][RT][4][4][kWave];   // [wave][row tile][slice][i][lane]
 
-    const int c0 = blockIdx.x * NG;    // first MXFP4 group of h = 64-row group of w13p
-    const int blk = blockIdx.y;
     span_begin(clk);
-    const int e = block_expert[blk];       // -1 past the used blocks
-    if (e < 0) {
+    int xg, blk;                          // NG-group pair xg of block blk (XCD-aware order)
+    if (!xcd_unit(I / (32 * NG), num_valid[0] / BM, xg, blk)) {
         span_end(clk);
         return;
     }
+    const int c0 = xg * NG;               // first MXFP4 group of h = 64-row group of w13p
+    const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
     const int KT = D / 128;
@@ -170,7 +171,8 @@ template <int RT>
 static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     constexpr int NG = stream_stage1_groups(16 * RT);
-    MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT, NG>), dim3(a.I / (32 * NG), a.nb_cap), dim3(kGemmThreads), 0,
+    MOE_LAUNCH((gemm1_swiglu_quant_kernel<RT, NG>), dim3(tile_grid(a.I / (32 * NG), a.nb_cap)),
+               dim3(kGemmThreads), 0,
                stream, ev, a.a1q, a.a1s, a.w13p, a.w13sp, a.sorted_route, a.block_expert,
                a.num_valid, a.a2q, a.a2s, a.h_dbg, a.M, a.D, a.I, a.topk, a.cap, a.clk);
     return hipGetLastError();

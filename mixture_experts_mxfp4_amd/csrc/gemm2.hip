@@ -18,7 +18,7 @@
 // to bf16 is bounded by 2^-9 of that contribution.
 //
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows and
-// 256*NG output columns; each wave owns NG groups of 64 columns (4 MFMA tiles
+// 256*NG output columns (units in the XCD-aware order of xcd_unit); each wave owns NG groups of 64 columns (4 MFMA tiles
 // per row tile each) and runs the whole K = I loop for each, streaming 1 KiB
 // weight fragments with non-temporal loads; the A fragments (MXFP4 h, written
 // by stage 1 in the fragment layout) are contiguous 1 KiB loads as well.
@@ -54,11 +54,11 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
     constexpr int kRow = 256 * 2 + 16;       // staged output row: 256 bf16 + 16 B bank stagger
     __shared__ __attribute__((aligned(16))) uint8_t stage[BM * kRow];
     __shared__ int32_t s_route[BM];
-    const int blk = blockIdx.y;
-    const int e = block_expert[blk];       // -1 past the used blocks
-    if (e < 0) return;
+    int ct, blk;                           // 256-column tile ct of block blk (XCD-aware order)
+    if (!xcd_unit(D / 256, num_valid[0] / BM, ct, blk)) return;
+    const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int n64 = blockIdx.x * 4 + wave;
+    const int n64 = ct * 4 + wave;
     const int KT = I / 128;
     const int R = M * topk;
 
@@ -137,7 +137,7 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
         const int sr = s_route[row];
         const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kRow + ch * 16);
         if (sr < R)
-            *reinterpret_cast<uint4*>(partial + int64_t(sr) * D + blockIdx.x * 256 + ch * 8) = v;
+            *reinterpret_cast<uint4*>(partial + int64_t(sr) * D + ct * 256 + ch * 8) = v;
     }
 }
 
@@ -156,13 +156,13 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
                       int M, int D, int I, int topk, int64_t cap)
 {
     constexpr int BM = 16 * RT;
-    const int blk = blockIdx.y;
-    const int e = block_expert[blk];       // -1 past the used blocks
-    if (e < 0) return;
+    int ct, blk;                           // column range ct of block blk (XCD-aware order)
+    if (!xcd_unit(D / (256 * NG), num_valid[0] / BM, ct, blk)) return;
+    const int e = block_expert[blk];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int KT = I / 128;                 // a multiple of U
     const int R = M * topk;
-    const int n64_0 = blockIdx.x * 4 * NG + wave;
+    const int n64_0 = ct * 4 * NG + wave;
 
     const uint8_t* wexp = w2p + int64_t(e) * D * (I / 2) + lane * 16;
     const uint8_t* sexp = w2sp + int64_t(e) * D * (I / 32) + lane * 4;
@@ -260,7 +260,7 @@ gemm2_weighted_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict
 template <int RT, int U, int NG>
 static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    MOE_LAUNCH((gemm2_weighted_kernel<RT, U, NG>), dim3(a.D / (256 * NG), a.nb_cap),
+    MOE_LAUNCH((gemm2_weighted_kernel<RT, U, NG>), dim3(tile_grid(a.D / (256 * NG), a.nb_cap)),
                dim3(kGemmThreads), 0, stream, ev, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route,
                a.sorted_w, a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
     return hipGetLastError();
@@ -269,7 +269,7 @@ static hipError_t launch_g2(const Gemm2Args& a, hipStream_t stream, const Kernel
 template <int RT>
 static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
 {
-    MOE_LAUNCH((gemm2_simple_kernel<RT>), dim3(a.D / 256, a.nb_cap), dim3(kGemmThreads), 0,
+    MOE_LAUNCH((gemm2_simple_kernel<RT>), dim3(tile_grid(a.D / 256, a.nb_cap)), dim3(kGemmThreads), 0,
                stream, ev, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w,
                a.block_expert, a.num_valid, a.partial, a.M, a.D, a.I, a.topk, a.cap);
     return hipGetLastError();

@@ -61,7 +61,7 @@ hipError_t launch_prepare(const uint8_t* src_codes, const uint8_t* src_scales, u
                           int n_cu, hipStream_t stream);
 
 // Gather the token-major activations a1 into sorted-row fragment layout
-// (tiled path), padding rows zeroed.
+// (tiled path); padding rows are not written (no kernel uses them).
 hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_t* sorted_route,
                             const int32_t* num_valid, int M, int D, int topk, int64_t cap,
                             uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream,
@@ -113,6 +113,24 @@ constexpr int kXcds = 8;
 inline unsigned tile_grid(int n_tiles, int nb_cap)
 {
     return unsigned((int64_t(n_tiles) * nb_cap + kXcds - 1) / kXcds * kXcds);
+}
+// Unit (x, block) of workgroup blockIdx.x in a grid of tile_grid(X,
+// nb_cap) for the streaming GEMMs: the dispatcher deals workgroups to the
+// XCDs round-robin, so workgroup w runs on XCD w % 8 as its (w / 8)-th; each
+// XCD takes a contiguous equal share of the U = X * nb_used units ordered
+// x-major, then block.  An expert's blocks at one x (one weight slice) then
+// run side by side on one XCD and share that slice in its L2, instead of
+// every XCD fetching it.  False past the used units.
+__device__ __forceinline__ bool xcd_unit(int X, int nb_used, int& x, int& blk)
+{
+    const int w = blockIdx.x, k = w % kXcds, j = w / kXcds;
+    const int64_t U = int64_t(X) * nb_used;
+    const int64_t lo = U * k / kXcds, hi = U * (k + 1) / kXcds;
+    if (lo + j >= hi) return false;
+    const int64_t u = lo + j;
+    x = int(u / nb_used);
+    blk = int(u % nb_used);
+    return true;
 }
 hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
 hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});

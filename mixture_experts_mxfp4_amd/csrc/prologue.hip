@@ -505,8 +505,16 @@ route_scatter_kernel(PrologueArgs a, int G)
 // Sorted-row fragment copy of the quantized activations for the tiled
 // kernels: one thread per (sorted row, K tile), 64 code bytes + one scale word.
 // Consecutive threads take consecutive rows of a 16-row slice, so each store
-// instruction writes 256 contiguous bytes.  Rows past num_valid[0] are left
-// alone (never read); padding rows are zero.
+// instruction writes 256 contiguous bytes.  Only rows holding a route are
+// written: padding rows (and rows past num_valid[0]) are left as they are.
+// Stage 1 never reads the rows of an all-padding 64-row group, and a padding
+// row it does read only decides that row of the product (an MFMA output row
+// depends on its own A row and scale alone), whose h and stage-2 result are
+// never stored to a route.
+// Each thread copies kGatherKt consecutive K tiles of one row (256 code bytes
+// and four scale words), so that a thread has four loads in flight.
+constexpr int kGatherKt = 4;
+
 __global__ void __launch_bounds__(256)
 gather_a1_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
                  const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ num_valid,
@@ -514,28 +522,41 @@ gather_a1_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1
                  uint8_t* __restrict__ a1fs)
 {
     const int KT = D / 128;
+    const int KG = (KT + kGatherKt - 1) / kGatherKt;      // K-tile groups per row
     const int64_t rows = num_valid[0];
-    const int64_t n = rows * KT;
+    const int64_t n = rows * KG;
     const int R = M * topk;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t slice = i / (16 * KT);
-        const int kt = int((i / 16) % KT);
+        // consecutive threads: consecutive rows of a 16-row slice, so every
+        // store instruction writes 256 contiguous bytes (64 for the scales)
+        const int64_t slice = i / (16 * KG);
+        const int kg = int((i / 16) % KG);
         const int64_t row = slice * 16 + (i % 16);
         const int sr = sorted_route[row];
-        uint4 v[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                      make_uint4(0, 0, 0, 0)};
-        uint32_t sc = 0;
-        if (sr < R) {
-            const int64_t tok = sr / topk;
-            const uint8_t* src = a1q + tok * (D / 2) + kt * 64;
+        if (sr >= R) continue;
+        const int64_t tok = sr / topk;
+        const int kt0 = kg * kGatherKt, nk = min(kGatherKt, KT - kt0);
+        const uint8_t* src = a1q + tok * (D / 2) + kt0 * 64;
+        uint4 v[kGatherKt][4];
+        uint32_t sc[kGatherKt];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = ld16(src + c * 16);
-            sc = *reinterpret_cast<const uint32_t*>(a1s + tok * (D / 32) + kt * 4);
+        for (int u = 0; u < kGatherKt; ++u) {
+            if (u < nk) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[u][c] = ld16(src + u * 64 + c * 16);
+                sc[u] = *reinterpret_cast<const uint32_t*>(a1s + tok * (D / 32) + (kt0 + u) * 4);
+            }
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(a1f + frag_code_off(row, kt, c, KT)) = v[c];
-        *reinterpret_cast<uint32_t*>(a1fs + frag_scale_off(row, kt, cap)) = sc;
+        for (int u = 0; u < kGatherKt; ++u) {
+            if (u < nk) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<uint4*>(a1f + frag_code_off(row, kt0 + u, c, KT)) = v[u][c];
+                *reinterpret_cast<uint32_t*>(a1fs + frag_scale_off(row, kt0 + u, cap)) = sc[u];
+            }
+        }
     }
 }
 
@@ -544,7 +565,7 @@ hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_
                             uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream,
                             const KernelEvents& ev)
 {
-    const int64_t n = cap * (D / 128);
+    const int64_t n = cap * ((D / 128 + kGatherKt - 1) / kGatherKt);
     if (n == 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
     if (blocks > int64_t(n_cu) * 8) blocks = int64_t(n_cu) * 8;
