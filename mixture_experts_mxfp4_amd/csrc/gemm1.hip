@@ -14,8 +14,11 @@
 // gate + 32 up columns = one MXFP4 group of h.  Workgroups take (group, block)
 // units in the XCD-aware order of xcd_unit.  The four waves split the K
 // dimension; each wave runs NG x RT x 4 MFMA tiles of 16x16x128, streaming its weight
-// fragments (1 KiB each, contiguous) with non-temporal loads and gathering the
-// block's activation rows by token id.  Partial sums meet in LDS; the epilogue
+// fragments (1 KiB each, contiguous) and gathering the block's activation rows
+// by token id.  Weight loads are non-temporal, except for experts with several
+// blocks: their blocks at one group pair run side by side on one XCD, and
+// cached loads let all but the first find the slice in L2 (prefill at E=257:
+// stage-1 fetch 604 -> 575 MB, 124.5 -> 118 us).  Partial sums meet in LDS; the epilogue
 // quantizes h with cross-lane reductions and writes it in sorted-row order in
 // the fragment layout (moe_common.h) that stage 2 loads contiguously.
 #include <type_traits>
@@ -49,12 +52,17 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 
     span_begin(clk);
     int xg, blk;                          // NG-group pair xg of block blk (XCD-aware order)
-    if (!xcd_unit(I / (32 * NG), num_valid[0] / BM, xg, blk)) {
+    const int nb_used = num_valid[0] / BM;
+    if (!xcd_unit(I / (32 * NG), nb_used, xg, blk)) {
         span_end(clk);
         return;
     }
     const int c0 = xg * NG;               // first MXFP4 group of h = 64-row group of w13p
     const int e = block_expert[blk];
+    // an expert with several blocks: its blocks at this xg run side by side on
+    // one XCD and share the weight slice through L2 (cached loads)
+    const bool shared_w = (blk > 0 && block_expert[blk - 1] == e) ||
+                          (blk + 1 < nb_used && block_expert[blk + 1] == e);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
     const int KT = D / 128;
@@ -84,8 +92,9 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[g][rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto steps = [&](auto u_const, int kt) {
+    auto steps = [&](auto u_const, auto nt_const, int kt) {
         constexpr int UU = decltype(u_const)::value;
+        constexpr bool NT = decltype(nt_const)::value;
         uint32_t sw[UU][NG], sa[UU][RT];
         uint4 b[UU][NG][4], a[UU][RT];
 #pragma unroll
@@ -95,7 +104,8 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                 sw[u][g] = *reinterpret_cast<const uint32_t*>(sb + int64_t(g) * KT * 256 + (kt + u) * 256);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    b[u][g][q] = ld16_nt(wb + (int64_t(g) * KT + kt + u) * 4096 + q * 1024);
+                    b[u][g][q] = NT ? ld16_nt(wb + (int64_t(g) * KT + kt + u) * 4096 + q * 1024)
+                                    : ld16(wb + (int64_t(g) * KT + kt + u) * 4096 + q * 1024);
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -115,10 +125,16 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                                                            (sa[u][rt] >> ash) & 0xFFu,
                                                            (sw[u][g] >> (8 * q)) & 0xFFu);
     };
-    const int kt1 = (wave + 1) * KT / 4;
-    int kt = wave * KT / 4;
-    for (; kt + U <= kt1; kt += U) steps(std::integral_constant<int, U>{}, kt);
-    for (; kt < kt1; ++kt) steps(std::integral_constant<int, 1>{}, kt);
+    auto kloop = [&](auto nt_const) {
+        const int kt1 = (wave + 1) * KT / 4;
+        int kt = wave * KT / 4;
+        for (; kt + U <= kt1; kt += U) steps(std::integral_constant<int, U>{}, nt_const, kt);
+        for (; kt < kt1; ++kt) steps(std::integral_constant<int, 1>{}, nt_const, kt);
+    };
+    if (shared_w)
+        kloop(std::false_type{});
+    else
+        kloop(std::true_type{});
 
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
