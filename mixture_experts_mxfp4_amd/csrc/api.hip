@@ -137,7 +137,7 @@ struct Layout {
     int bm;
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
-        slot_expert, slot_layers, route_of, n_active, chunk_counts, block_info, h16, barrier,
+        slot_expert, slot_layers, route_of, n_active, block_info, h16, barrier,
         split_ctr, part, total;
 };
 
@@ -163,7 +163,7 @@ Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
     L.nb = L.cap / L.bm;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.chunk_counts = L.block_info = 0;
+    L.slot_expert = L.slot_layers = L.route_of = L.n_active = L.block_info = 0;
     L.h16 = L.barrier = L.split_ctr = L.part = 0;
     // the persistent forward's barrier words and the split-K counters come
     // first (offset 0)
@@ -192,7 +192,6 @@ Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
         L.total = off;
         return L;
     }
-    L.chunk_counts = take(sizeof(int32_t) * size_t(moe::route_chunks(M, topk)) * E);
     L.sorted_route = take(sizeof(int32_t) * size_t(L.cap));
     L.sorted_w = take(sizeof(float) * size_t(L.cap));
     L.block_expert = take(sizeof(int32_t) * size_t(L.nb));
@@ -358,7 +357,7 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
     const bool tile = L.bm == 256;
     moe::PrologueArgs pa{topk_ids, topk_w, M, topk, E, L.bm, nb, sorted_route, sorted_w,
                          block_expert, num_valid, hidden, D, a1q, a1s,
-                         reinterpret_cast<int32_t*>(ws + L.chunk_counts), block_info};
+                         block_info};
     const moe::KernelEvents ev0 = kernel_events(dbg, 0);
     hipError_t e = moe::launch_prologue(pa, n_cu, stream,
                                         tile ? moe::KernelEvents{ev0.start, nullptr} : ev0);
@@ -424,8 +423,9 @@ MOE_API int moe_mxfp4_launch_count(int M, int D, int I, int E, int topk)
     if (check_shape(M, D, I, E, topk) || M == 0) return 0;
     const int path = choose_path(M, E, topk);
     if (path == MOE_MXFP4_PATH_DIRECT) return 2;
-    const int prologue = moe::route_chunks(M, topk) > 0 ? 2 : 1;
-    return prologue + (path == MOE_MXFP4_PATH_TILED ? 1 : 0) + 3;   // + stage 1, stage 2, sum
+    // prologue (sort + quantization), the tiled path's sorted activation
+    // copy, stage 1, stage 2, the slot sum
+    return 1 + (path == MOE_MXFP4_PATH_TILED ? 1 : 0) + 3;
 }
 
 MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk)

@@ -29,6 +29,9 @@
 namespace moe {
 
 constexpr int kGemmThreads = 256;
+// Row tiles per LDS reduction pass of the epilogue: two (32 KiB of LDS at
+// four waves) leave room for a third workgroup per CU.
+constexpr int kRedTiles = 2;
 
 // Loads of U consecutive K tiles are issued before their MFMAs so that every
 // wave keeps U x NG x 4 KiB of weight fragments in flight (U = 2 at 64-row
@@ -48,7 +51,11 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 {
     constexpr int BM = 16 * RT;
     constexpr int U = g1_unroll<RT, NG>();
-    __shared__ float red[4][RT][4][4][kWave];   // [wave][row tile][slice][i][lane]
+    // the partial sums meet in LDS kRedTiles row tiles at a time:
+    // [wave][row tile][slice][i][lane]
+    constexpr int RTH = RT < kRedTiles ? RT : kRedTiles;
+    constexpr int WPT = 4 / RTH;          // waves finishing each row tile of a pass
+    __shared__ float red[4][RTH][4][4][kWave];
 
     span_begin(clk);
     int xg, blk;                          // NG-group pair xg of block blk (XCD-aware order)
@@ -139,23 +146,27 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int c = c0 + g;
-        if (g > 0) __syncthreads();        // red is reused group by group
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int p = 0; p < RT; p += RTH) {
+            if (g > 0 || p > 0) __syncthreads();   // red is reused pass by pass
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int r = 0; r < RTH; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) red[wave][rt][q][i][lane] = acc[g][rt][q][i];
-        __syncthreads();
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[wave][r][q][i][lane] = acc[g][p + r][q][i];
+            __syncthreads();
 
-        for (int rt = wave; rt < RT; rt += 4) {
+            // wave w finishes rows i = (w % WPT) * (4 / WPT) ... of row tile w / WPT
+            const int r = wave / WPT, rt = p + r;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int ii = 0; ii < 4 / WPT; ++ii) {
+                const int i = (wave % WPT) * (4 / WPT) + ii;
                 float s4[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    s4[q] = red[0][rt][q][i][lane] + red[1][rt][q][i][lane] +
-                            red[2][rt][q][i][lane] + red[3][rt][q][i][lane];
+                    s4[q] = red[0][r][q][i][lane] + red[1][r][q][i][lane] +
+                            red[2][r][q][i][lane] + red[3][r][q][i][lane];
                 // slices 0,1 = gate columns c*32 + lane%16 (+16), slices 2,3 = up
                 const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
                 const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);

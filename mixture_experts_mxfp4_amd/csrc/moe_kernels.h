@@ -46,12 +46,12 @@ struct PrologueArgs {
     const uint16_t* hidden;
     int D;
     uint8_t *a1q, *a1s;
-    int32_t* chunk_counts;         // [route_chunks][E] for long lists (else unused)
     // [nb_cap][4], per used block: its expert, the expert's first block, its
     // number of blocks and its number of routes (tiled kernels; may be null)
     int32_t* block_info;
 };
-// Chunks of the two-launch route sort for this many routes (0: one workgroup).
+// Chunks (workgroups) of the route sort for this many routes (0: a short
+// list, sorted by one wave).
 int route_chunks(int M, int topk);
 hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
                            const KernelEvents& ev = {});

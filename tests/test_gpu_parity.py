@@ -353,7 +353,9 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     n = int(want["num_valid"][0])
     log(f"chunked route list M={M} k={k} E={E}: block_m {dbg['block_m']}, {n} sorted rows")
     np.testing.assert_array_equal(dbg["num_valid"].cpu().numpy(), want["num_valid"])
-    np.testing.assert_array_equal(dbg["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+    got = dbg["sorted_route"].cpu().numpy()
+    np.testing.assert_array_equal(got[:n], want["sorted_route"])
+    assert np.all(got[n:] == M * k)        # rows past the used blocks are padding too
     assert torch.all(dbg["out"].float() == 0)
 
 
