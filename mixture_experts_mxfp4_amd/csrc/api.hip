@@ -368,13 +368,13 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
                       a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap,
-                      dbg ? dbg->stage1_clock : nullptr, block_info};
+                      dbg ? dbg->stage1_clock : nullptr, block_info, n_cu};
     const moe::KernelEvents ev1 = kernel_events(dbg, 1);
     e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      partial, M, D, I, topk, L.bm, nb, L.cap, block_info};
+                      partial, M, D, I, topk, L.bm, nb, L.cap, block_info, nullptr, n_cu};
     const moe::KernelEvents ev2 = kernel_events(dbg, 2);
     e = tile ? moe::launch_gemm2_tile(g2, stream, ev2) : moe::launch_gemm2(g2, stream, ev2);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
@@ -434,7 +434,14 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
     const Layout L = layout(M, D, I, E, topk);
     if (L.path == MOE_MXFP4_PATH_DIRECT)
         return int64_t(moe::direct_stage1_x(I)) * moe::direct_slots(M, E, topk);
-    if (L.path == MOE_MXFP4_PATH_TILED) return moe::tile_grid(2 * I / 256, int(L.nb));
+    if (L.path == MOE_MXFP4_PATH_TILED) {
+        // the persistent grid the launch takes on the current device
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n_cu = 0;
+        return moe::tile_persistent_grid(2 * I / 256, int(L.nb), n_cu);
+    }
     return moe::tile_grid(I / (32 * moe::stream_stage1_groups(L.bm)), int(L.nb));
 }
 

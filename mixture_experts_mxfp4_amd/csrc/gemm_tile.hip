@@ -22,6 +22,8 @@
 // Per stage a wave issues 16 MFMAs of 32x32x64 (512 cycles) against 6 KiB of
 // LDS fragment reads; the workgroup fetches 34 KiB per stage, 2 x 256 x 256 x
 // 128 / 34 KiB = 480 FLOP per byte of L2 traffic.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -402,8 +404,12 @@ __device__ __forceinline__ void a_sources(const TileArgs& p, int blk, StageSrc& 
 // tiles, ordered expert by expert and, inside an expert, column tile by
 // column tile across the expert's row blocks: the workgroups resident on
 // one XCD at a time share an expert's weight tiles and activation blocks
-// in their L2 instead of every XCD fetching every block.  The grid is
-// rounded up to a multiple of 8 (tile_grid), so every share fits.
+// in their L2 instead of every XCD fetching every block.  Both kernels are
+// persistent: one workgroup per CU (tile_persistent_grid, a multiple of 8)
+// walks its XCD's share with a stride of the XCD's workgroup count, so the
+// workgroups resident on an XCD at a time take consecutive tiles; a new
+// tile's ring fill then follows the previous tile's epilogue on the same CU
+// without a workgroup launch in between.
 
 // This workgroup's XCD share [lo, hi) of the used tiles and its index j in
 // that XCD.
@@ -418,32 +424,35 @@ __device__ __forceinline__ void xcd_share(const TileArgs& p, int n_tiles, int64_
     hi = used * (xcd + 1) / kXcds;
 }
 
+// One 16-byte record of the sort at a wave-uniform address, through the
+// scalar cache and waited for inside the asm block.  A vector load here
+// would make the compiler wait for every older vector-memory operation of the
+// wave (s_waitcnt vmcnt(0)), a persistent workgroup's previous stores
+// included.
+__device__ __forceinline__ int4 load_record(const int4* rec)
+{
+    typedef int v4i_t __attribute__((ext_vector_type(4)));
+    // both halves as unsigned 32-bit words (uniform_ptr): readfirstlane
+    // returns int, which would sign-extend the low word into the high one
+    const uint8_t* au = uniform_ptr(reinterpret_cast<const uint8_t*>(rec));
+    v4i_t v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(au) : "memory");
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
 // Column tile, block, expert and the block's number of routes for tile t of
 // the order above: one 16-byte record of the sort (tiles t of an expert's
 // n_tiles * nb run lie within its blocks' records).
 __device__ __forceinline__ void tile_at(const TileArgs& p, int n_tiles, int64_t t, int& ntile,
                                         int& blk, int& e, int& valid)
 {
-    const int4 bi = p.block_info[t / n_tiles];
+    const int4 bi = load_record(p.block_info + t / n_tiles);
     e = bi.x;
     const int first = bi.y, nb = bi.z;
     const int local = int(t - int64_t(n_tiles) * first);
     ntile = local / nb;
     blk = first + local % nb;
     valid = min(kTM, bi.w - (blk - first) * kTM);
-}
-
-// Column tile, block, expert and valid rows of this workgroup (one tile per
-// workgroup); false past the used tiles.
-__device__ __forceinline__ bool tile_of(const TileArgs& p, int n_tiles, int& ntile, int& blk,
-                                        int& e, int& valid)
-{
-    int64_t lo, hi;
-    int j;
-    xcd_share(p, n_tiles, lo, hi, j);
-    if (lo + j >= hi) return false;
-    tile_at(p, n_tiles, lo + j, ntile, blk, e, valid);
-    return true;
 }
 
 // ------------------------------------------------------------ stage 1 ----
@@ -453,92 +462,108 @@ gemm1_tile_kernel(TileArgs p, int I)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     span_begin(p.clk);
-    int ntile, blk, e, valid;
-    if (!tile_of(p, p.N / kTN, ntile, blk, e, valid)) {
-        span_end(p.clk);
-        return;
-    }
+    const int n_tiles = p.N / kTN;
+    int64_t lo, hi;
+    int jx;                                  // this workgroup's index in its XCD
+    xcd_share(p, n_tiles, lo, hi, jx);
+    const int per_xcd = int(gridDim.x) / kXcds;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
+#pragma unroll 1
+    for (int64_t t = lo + jx; t < hi; t += per_xcd) {
+        int ntile, blk, e, valid;
+        tile_at(p, n_tiles, t, ntile, blk, e, valid);
 
-    // A: the sorted, fragment-layout copy of the activations (gather kernel)
-    StageSrc src;
-    a_sources(p, blk, src);
-    b_sources(p, e, ntile, src);
+        // A: the sorted, fragment-layout copy of the activations (gather kernel)
+        StageSrc src;
+        a_sources(p, blk, src);
+        b_sources(p, e, ntile, src);
 
-    v16f acc[2][4];
-    zero_acc(acc);
-    if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
-    else tile_mainloop_idle(src, p.K / 128, lds);
+        v16f acc[2][4];
+        zero_acc(acc);
+        if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
+        else tile_mainloop_idle(src, p.K / 128, lds);
 
-    // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
-    // wave_n*2 + 1 of the tile (prepared 64-row group = 32 gate rows then 32 up
-    // rows: gate and up of an h column sit at the same place of tiles 2gi and
-    // 2gi+1); the tile's 128 h columns are K tile `ntile` of stage 2.  With the
-    // swapped product a lane holds, for row mt*32 + lane%32, 16 of the 32
-    // columns of an MXFP4 block (columns (i/4)*8 + (lane/32)*4 + i%4) and lane
-    // lane^32 the other 16: the block maximum takes one exchange, and after a
-    // second each half stores 8 contiguous code bytes of the row's 16-byte chunk
-    // (lanes < 32 bytes 0-7, lanes >= 32 bytes 8-15).
-    const bool upper = lane >= 32;
+        // Epilogue.  The wave's N tiles are (gate, up) of h groups wave_n*2 and
+        // wave_n*2 + 1 of the tile (prepared 64-row group = 32 gate rows then 32 up
+        // rows: gate and up of an h column sit at the same place of tiles 2gi and
+        // 2gi+1); the tile's 128 h columns are K tile `ntile` of stage 2.  With the
+        // swapped product a lane holds, for row mt*32 + lane%32, 16 of the 32
+        // columns of an MXFP4 block (columns (i/4)*8 + (lane/32)*4 + i%4) and lane
+        // lane^32 the other 16: the block maximum takes one exchange, and after a
+        // second each half stores 8 contiguous code bytes of the row's 16-byte chunk
+        // (lanes < 32 bytes 0-7, lanes >= 32 bytes 8-15).
+        const bool upper = lane >= 32;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int64_t srow = int64_t(blk) * kTM + wave_m * 64 + mt * 32 + (lane & 31);
+        for (int mt = 0; mt < 2; ++mt) {
+            const int64_t srow = int64_t(blk) * kTM + wave_m * 64 + mt * 32 + (lane & 31);
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int c = wave_n * 2 + gi;               // 32-column chunk in K tile `ntile`
-            // h of element pairs (2j, 2j+1) as packed bf16; block maximum on
-            // the 15-bit magnitudes, two per packed 16-bit max
-            typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-            uint32_t hp[8];
-            u16x2_t m2 = {0, 0};
+            for (int gi = 0; gi < 2; ++gi) {
+                const int c = wave_n * 2 + gi;               // 32-column chunk in K tile `ntile`
+                // h of element pairs (2j, 2j+1) as packed bf16; block maximum on
+                // the 15-bit magnitudes, two per packed 16-bit max
+                typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+                uint32_t hp[8];
+                u16x2_t m2 = {0, 0};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                hp[j] = f32x2_to_bf16x2(silu_fast(acc[mt][2 * gi][2 * j]) * acc[mt][2 * gi + 1][2 * j],
-                                        silu_fast(acc[mt][2 * gi][2 * j + 1]) * acc[mt][2 * gi + 1][2 * j + 1]);
-                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, hp[j] & 0x7FFF7FFFu));
-            }
-            uint32_t amax = max(uint32_t(m2.x), uint32_t(m2.y));
-            amax = max(amax, uint32_t(__shfl_xor(int(amax), 32)));
-            const uint32_t s = mx_scale_from_amax(amax);
-            const float so = mx_scale_operand(s);
-            // element pair j of this lane's 16 -> chunk byte (j/2)*4 + (lane/32)*2 + j%2:
-            // bytes of pairs 0-3 in `lo`, of pairs 4-7 in `hi`
-            uint32_t lo = 0, hi = 0;
-            lo = mx_code_pair<0>(lo, hp[0], so);
-            lo = mx_code_pair<1>(lo, hp[1], so);
-            lo = mx_code_pair<2>(lo, hp[2], so);
-            lo = mx_code_pair<3>(lo, hp[3], so);
-            hi = mx_code_pair<0>(hi, hp[4], so);
-            hi = mx_code_pair<1>(hi, hp[5], so);
-            hi = mx_code_pair<2>(hi, hp[6], so);
-            hi = mx_code_pair<3>(hi, hp[7], so);
-            // lanes < 32 hold chunk bytes {0,1,4,5} and {8,9,12,13}, lanes >= 32
-            // {2,3,6,7} and {10,11,14,15}
-            const uint32_t recv = uint32_t(__shfl_xor(int(upper ? lo : hi), 32));
-            uint2 out;
-            if (!upper) {
-                out.x = (lo & 0xFFFFu) | (recv << 16);
-                out.y = (lo >> 16) | (recv & 0xFFFF0000u);
-            } else {
-                out.x = (recv & 0xFFFFu) | (hi << 16);
-                out.y = (recv >> 16) | (hi & 0xFFFF0000u);
-            }
-            *reinterpret_cast<uint2*>(p.a2q + frag_code_off(srow, ntile, c, I / 128) + (upper ? 8 : 0)) = out;
-            if (!upper) p.a2s[frag_scale_off(srow, ntile, p.cap) + c] = uint8_t(s);
-            if (p.h_dbg) {
+                for (int j = 0; j < 8; ++j) {
+                    hp[j] = f32x2_to_bf16x2(silu_fast(acc[mt][2 * gi][2 * j]) * acc[mt][2 * gi + 1][2 * j],
+                                            silu_fast(acc[mt][2 * gi][2 * j + 1]) * acc[mt][2 * gi + 1][2 * j + 1]);
+                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, hp[j] & 0x7FFF7FFFu));
+                }
+                uint32_t amax = max(uint32_t(m2.x), uint32_t(m2.y));
+                amax = max(amax, uint32_t(__shfl_xor(int(amax), 32)));
+                const uint32_t s = mx_scale_from_amax(amax);
+                const float so = mx_scale_operand(s);
+                // element pair j of this lane's 16 -> chunk byte (j/2)*4 + (lane/32)*2 + j%2:
+                // bytes of pairs 0-3 in `lo`, of pairs 4-7 in `hi`
+                uint32_t lo = 0, hi = 0;
+                lo = mx_code_pair<0>(lo, hp[0], so);
+                lo = mx_code_pair<1>(lo, hp[1], so);
+                lo = mx_code_pair<2>(lo, hp[2], so);
+                lo = mx_code_pair<3>(lo, hp[3], so);
+                hi = mx_code_pair<0>(hi, hp[4], so);
+                hi = mx_code_pair<1>(hi, hp[5], so);
+                hi = mx_code_pair<2>(hi, hp[6], so);
+                hi = mx_code_pair<3>(hi, hp[7], so);
+                // lanes < 32 hold chunk bytes {0,1,4,5} and {8,9,12,13}, lanes >= 32
+                // {2,3,6,7} and {10,11,14,15}
+                const uint32_t recv = uint32_t(__shfl_xor(int(upper ? lo : hi), 32));
+                uint2 out;
+                if (!upper) {
+                    out.x = (lo & 0xFFFFu) | (recv << 16);
+                    out.y = (lo >> 16) | (recv & 0xFFFF0000u);
+                } else {
+                    out.x = (recv & 0xFFFFu) | (hi << 16);
+                    out.y = (recv >> 16) | (hi & 0xFFFF0000u);
+                }
+                *reinterpret_cast<uint2*>(p.a2q + frag_code_off(srow, ntile, c, I / 128) + (upper ? 8 : 0)) = out;
+                if (!upper) p.a2s[frag_scale_off(srow, ntile, p.cap) + c] = uint8_t(s);
+                if (p.h_dbg) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    p.h_dbg[srow * I + ntile * 128 + c * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)] =
-                        uint16_t(hp[i >> 1] >> (16 * (i & 1)));
+                    for (int i = 0; i < 16; ++i)
+                        p.h_dbg[srow * I + ntile * 128 + c * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)] =
+                            uint16_t(hp[i >> 1] >> (16 * (i & 1)));
+                }
             }
         }
+        // the next tile's loads overwrite the ring: every wave is past this
+        // tile's LDS reads (the stores stay in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     span_end(p.clk);
 }
 
 // ------------------------------------------------------------ stage 2 ----
 
+// Persistent: one workgroup per CU walks its XCD's share of the tiles with a
+// stride of the XCD's workgroup count, so the workgroups resident on an XCD
+// at a time still take consecutive tiles.  The partial-row stores of a tile
+// are issued before the next tile's first loads and are not waited for: the
+// next tile's ring waits (s_waitcnt vmcnt(N)) only need its own loads, which
+// complete in issue order after the older stores.  With one tile per
+// workgroup, every workgroup drained its 256 KiB of stores before the CU
+// could start the next tile (58 us of the kernel's time at 4,096 tokens).
 __global__ void __launch_bounds__(kTThreads, 1)
 gemm2_tile_kernel(TileArgs p)
 {
@@ -546,66 +571,84 @@ gemm2_tile_kernel(TileArgs p)
     __shared__ int32_t s_route[kTM];
     __shared__ float s_w[kTM];
     span_begin(p.clk);
-    int ntile, blk, e, valid;
-    if (!tile_of(p, p.N / kTN, ntile, blk, e, valid)) {
-        span_end(p.clk);
-        return;
-    }
+    const int n_tiles = p.N / kTN;
+    int64_t lo, hi;
+    int jx;                                  // this workgroup's index in its XCD
+    xcd_share(p, n_tiles, lo, hi, jx);
+    const int per_xcd = int(gridDim.x) / kXcds;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wave_m = wave >> 1, wave_n = wave & 1;
     const int R = p.M * p.topk;
     const int D = p.N;
-    // the rows' routes and weights travel in registers through the main loop
-    // (nothing waits for them before the first K stages are requested)
-    const int my_route = tid < kTM ? p.sorted_route[blk * kTM + tid] : R;
-    const float my_w = tid < kTM ? p.sorted_w[blk * kTM + tid] : 0.f;
-    StageSrc src;
-    a_sources(p, blk, src);
-    b_sources(p, e, ntile, src);
+#pragma unroll 1
+    for (int64_t t = lo + jx; t < hi; t += per_xcd) {
+        int ntile, blk, e, valid;
+        tile_at(p, n_tiles, t, ntile, blk, e, valid);
+        // the rows' routes (waves 0-3) and weights (waves 4-7) go straight to
+        // LDS ahead of the first K stages; the main loop's waits cover them
+        {
+            const int q = wave & 3;
+            const uint8_t* base = wave < 4 ? reinterpret_cast<const uint8_t*>(p.sorted_route)
+                                           : reinterpret_cast<const uint8_t*>(p.sorted_w);
+            const uint8_t* dst = wave < 4 ? reinterpret_cast<const uint8_t*>(s_route)
+                                          : reinterpret_cast<const uint8_t*>(s_w);
+            dma4s(uniform_ptr(base + (int64_t(blk) * kTM + q * kWave) * 4), uint32_t(lane * 4),
+                  __builtin_amdgcn_readfirstlane(lds_address(dst) + q * kWave * 4));
+        }
+        StageSrc src;
+        a_sources(p, blk, src);
+        b_sources(p, e, ntile, src);
 
-    v16f acc[2][4];
-    zero_acc(acc);
-    if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
-    else tile_mainloop_idle(src, p.K / 128, lds);
-    if (tid < kTM) {
-        s_route[tid] = my_route;
-        s_w[tid] = my_w;
-    }
+        v16f acc[2][4];
+        zero_acc(acc);
+        if (rows_in_use(valid, wave_m)) tile_mainloop<true>(src, p.K / 128, lds, acc);
+        else tile_mainloop_idle(src, p.K / 128, lds);
 
-    // Epilogue: the routing weight times the sum, rounded to bf16, goes through
-    // LDS as the 256 x 256 tile; then each half-wave stores one row's 512
-    // contiguous bytes into its route's partial row (padding rows are skipped).
-    // With the swapped product a lane holds one row (mt*32 + lane%32 of the
-    // wave's 64) and, per group of four elements, four consecutive columns:
-    // one routing weight per row tile and 8-byte LDS writes.
-    uint8_t* ps = lds;                                   // [256 rows][kPStride]
-    __syncthreads();
+        // Epilogue: the routing weight times the sum, rounded to bf16, goes
+        // through LDS as the 256 x 256 tile; then each half-wave stores one
+        // row's 512 contiguous bytes into its route's partial row (padding rows
+        // are skipped).  With the swapped product a lane holds one row (mt*32 +
+        // lane%32 of the wave's 64) and, per group of four elements, four
+        // consecutive columns: one routing weight per row tile and 8-byte LDS
+        // writes.
+        uint8_t* ps = lds;                                   // [256 rows][kPStride]
+        __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int row = wave_m * 64 + mt * 32 + (lane & 31);
-        const float w = s_w[row];
+        for (int mt = 0; mt < 2; ++mt) {
+            const int row = wave_m * 64 + mt * 32 + (lane & 31);
+            const float w = s_w[row];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+            for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wave_n * 128 + nt * 32 + q * 8 + (lane >> 5) * 4;
-                uint2 v;
-                v.x = f32x2_to_bf16x2(w * acc[mt][nt][4 * q], w * acc[mt][nt][4 * q + 1]);
-                v.y = f32x2_to_bf16x2(w * acc[mt][nt][4 * q + 2], w * acc[mt][nt][4 * q + 3]);
-                *reinterpret_cast<uint2*>(ps + row * kPStride + col * 2) = v;
+                for (int q = 0; q < 4; ++q) {
+                    const int col = wave_n * 128 + nt * 32 + q * 8 + (lane >> 5) * 4;
+                    uint2 v;
+                    v.x = f32x2_to_bf16x2(w * acc[mt][nt][4 * q], w * acc[mt][nt][4 * q + 1]);
+                    v.y = f32x2_to_bf16x2(w * acc[mt][nt][4 * q + 2], w * acc[mt][nt][4 * q + 3]);
+                    *reinterpret_cast<uint2*>(ps + row * kPStride + col * 2) = v;
+                }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 #pragma unroll 4
-    for (int k = 0; k < kTM / 16; ++k) {
-        const int row = wave * (kTM / 8) + 2 * k + (lane >> 5);
-        const int sr = s_route[row];
-        const uint4 v = *reinterpret_cast<const uint4*>(ps + row * kPStride + (lane & 31) * 16);
-        if (sr < R)
-            *reinterpret_cast<uint4*>(p.partial + int64_t(sr) * D + ntile * kTN + (lane & 31) * 8) = v;
+        for (int k = 0; k < kTM / 16; ++k) {
+            const int row = wave * (kTM / 8) + 2 * k + (lane >> 5);
+            const int sr = s_route[row];
+            const uint4 v = *reinterpret_cast<const uint4*>(ps + row * kPStride + (lane & 31) * 16);
+            if (sr < R)
+                *reinterpret_cast<uint4*>(p.partial + int64_t(sr) * D + ntile * kTN + (lane & 31) * 8) = v;
+        }
+        // the next tile's loads overwrite the ring and s_route: every wave's
+        // LDS reads of this tile are done (the stores stay in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     span_end(p.clk);
+}
+
+unsigned tile_persistent_grid(int n_tiles, int nb_cap, int n_cu)
+{
+    const unsigned g = tile_grid(n_tiles, nb_cap);
+    return n_cu >= kXcds ? std::min(g, unsigned(n_cu / kXcds * kXcds)) : g;
 }
 
 hipError_t tile_allow_lds()
@@ -626,8 +669,8 @@ hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const Kerne
     TileArgs p{a.a1f, a.a1fs, a.w13p, a.w13sp, a.sorted_route, nullptr, a.num_valid,
                reinterpret_cast<const int4*>(a.block_info), a.M, a.topk, 2 * a.I, a.D, a.cap, a.a2q, a.a2s,
                a.h_dbg, nullptr, a.clk};
-    MOE_LAUNCH(gemm1_tile_kernel, dim3(tile_grid(2 * a.I / kTN, a.nb_cap)), dim3(kTThreads),
-               uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
+    MOE_LAUNCH(gemm1_tile_kernel, dim3(tile_persistent_grid(2 * a.I / kTN, a.nb_cap, a.n_cu)),
+               dim3(kTThreads), uint32_t(tile_lds_bytes()), stream, ev, p, a.I);
     return hipGetLastError();
 }
 
@@ -639,8 +682,8 @@ hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const Kerne
     TileArgs p{a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w, a.num_valid,
                reinterpret_cast<const int4*>(a.block_info), a.M, a.topk, a.D, a.I, a.cap, nullptr, nullptr,
                nullptr, a.partial, a.clk};
-    MOE_LAUNCH(gemm2_tile_kernel, dim3(tile_grid(a.D / kTN, a.nb_cap)), dim3(kTThreads),
-               uint32_t(tile_lds_bytes()), stream, ev, p);
+    MOE_LAUNCH(gemm2_tile_kernel, dim3(tile_persistent_grid(a.D / kTN, a.nb_cap, a.n_cu)),
+               dim3(kTThreads), uint32_t(tile_lds_bytes()), stream, ev, p);
     return hipGetLastError();
 }
 

@@ -82,6 +82,7 @@ struct Gemm1Args {
     int64_t cap;
     uint64_t* clk = nullptr;       // optional kernel span (span_begin / span_end)
     const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
+    int n_cu = 0;                  // compute units: the tiled kernel's persistent grid
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 // 64-row gate_up groups per workgroup of the streaming stage 1 (grid: I/32 /
@@ -104,6 +105,7 @@ struct Gemm2Args {
     int64_t cap;
     const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
     uint64_t* clk = nullptr;       // optional workgroup spans (tiled kernel)
+    int n_cu = 0;                  // compute units: the tiled kernel's persistent grid
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
@@ -133,6 +135,9 @@ __device__ __forceinline__ bool xcd_unit(int X, int nb_used, int& x, int& blk)
     return true;
 }
 hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
+// Workgroups of a persistent tiled launch: one per CU (a multiple of the XCD
+// count), fewer when there are fewer tiles; n_cu < 8: one per tile.
+unsigned tile_persistent_grid(int n_tiles, int nb_cap, int n_cu);
 hipError_t launch_gemm1_tile(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm2_tile(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 

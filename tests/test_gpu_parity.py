@@ -359,6 +359,28 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     assert torch.all(dbg["out"].float() == 0)
 
 
+@pytest.mark.parametrize("high", [False, True])
+def test_tiled_workspace_address_bit31(binding, high):
+    """The tiled kernels form the scalar address of each tile's record from two
+    32-bit halves: a workspace whose address has bit 31 of its low word set
+    (or clear) gives the same bits as one from the allocator."""
+    M, D, I, E, n_routed, seed = 1400, 512, 256, 5, 2, 25
+    case = custom_case(M, D, I, E, n_routed, seed)
+    d = case.device_inputs()
+    ref = binding.moe_mxfp4_forward(d["hidden"], *d["prepared"], d["ids"], d["tw"])
+    n = binding.moe_mxfp4_workspace_bytes(M, D, I, E, case.topk)
+    raw = torch.empty(n + (1 << 32) + 256, dtype=torch.uint8, device="cuda")
+    base = raw.data_ptr()
+    want = (0x80000000 if high else 0) + 0x100
+    off = (want - (base & 0xFFFFFFFF)) % (1 << 32)
+    ws = raw[off:off + n]
+    assert (ws.data_ptr() & 0x80000000 != 0) == high and ws.data_ptr() % 256 == 0
+    log(f"tiled forward with workspace at {ws.data_ptr():#x}")
+    out = binding.moe_mxfp4_forward(d["hidden"], *d["prepared"], d["ids"], d["tw"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,D,I,E,n_routed,seed", [
     (1, 512, 256, 9, 2, 21),          # single token (route-indexed path)
     (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
