@@ -33,6 +33,8 @@
 // one 32-element block (8 bf16 = 16 bytes each); the block maximum is reduced
 // across the four lanes, each lane writes 4 code bytes and the first lane the
 // scale byte.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -510,60 +512,59 @@ prologue_sort_kernel(PrologueArgs a, int G)
 }
 
 // Sorted-row fragment copy of the quantized activations for the tiled
-// kernels: one thread per (sorted row, K tile), 64 code bytes + one scale word.
-// Consecutive threads take consecutive rows of a 16-row slice, so each store
-// instruction writes 256 contiguous bytes.  Only rows holding a route are
-// written: padding rows (and rows past num_valid[0]) are left as they are.
+// kernels.  A workgroup copies one 16-row slice at a time: the slice's codes
+// are one contiguous run of KT KiB in the fragment layout ([K tile][32-element
+// chunk][row][16 B]), so thread i of the slice writes 16-byte piece i of that
+// run (a wave stores 1 KiB contiguous per instruction) and reads it from its
+// row, 16 rows x 64 contiguous bytes per wave instruction; the scale words go
+// the same way (64 contiguous bytes per K tile).  Only rows holding a route
+// are written: padding rows (and rows past num_valid[0]) are left as they are.
 // Stage 1 never reads the rows of an all-padding 64-row group, and a padding
 // row it does read only decides that row of the product (an MFMA output row
 // depends on its own A row and scale alone), whose h and stage-2 result are
 // never stored to a route.
-// Each thread copies kGatherKt consecutive K tiles of one row (256 code bytes
-// and four scale words), so that a thread has four loads in flight.
-constexpr int kGatherKt = 4;
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 8;       // 16-byte pieces in flight per thread
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kGatherThreads)
 gather_a1_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
                  const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ num_valid,
                  int M, int D, int topk, int64_t cap, uint8_t* __restrict__ a1f,
                  uint8_t* __restrict__ a1fs)
 {
     const int KT = D / 128;
-    const int KG = (KT + kGatherKt - 1) / kGatherKt;      // K-tile groups per row
-    const int64_t rows = num_valid[0];
-    const int64_t n = rows * KG;
+    const int64_t slices = num_valid[0] / 16;
     const int R = M * topk;
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += int64_t(gridDim.x) * blockDim.x) {
-        // consecutive threads: consecutive rows of a 16-row slice, so every
-        // store instruction writes 256 contiguous bytes (64 for the scales)
-        const int64_t slice = i / (16 * KG);
-        const int kg = int((i / 16) % KG);
-        const int64_t row = slice * 16 + (i % 16);
+    const int r = threadIdx.x % 16;            // this thread's row of every slice
+    const int pieces = KT * 64;                // 16-byte code pieces per slice
+#pragma unroll 1
+    for (int64_t sl = blockIdx.x; sl < slices; sl += gridDim.x) {
+        const int64_t row = sl * 16 + r;
         const int sr = sorted_route[row];
-        if (sr >= R) continue;
-        const int64_t tok = sr / topk;
-        const int kt0 = kg * kGatherKt, nk = min(kGatherKt, KT - kt0);
-        const uint8_t* src = a1q + tok * (D / 2) + kt0 * 64;
-        uint4 v[kGatherKt][4];
-        uint32_t sc[kGatherKt];
+        if (sr >= R) continue;                 // a padding row: nothing to copy
+        const uint8_t* src = a1q + int64_t(sr / topk) * (D / 2);
+        uint8_t* dst = a1f + frag_code_off(sl * 16, 0, 0, KT);
+        // piece i = (kt, chunk c, row r): i = (kt * 4 + c) * 16 + r
+#pragma unroll 1
+        for (int i0 = threadIdx.x; i0 < pieces; i0 += kGatherThreads * kGatherUnroll) {
+            uint4 v[kGatherUnroll];
 #pragma unroll
-        for (int u = 0; u < kGatherKt; ++u) {
-            if (u < nk) {
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const int i = i0 + u * kGatherThreads;
+                if (i < pieces) v[u] = ld16(src + (i >> 4) * 16);   // (kt * 4 + c) * 16 bytes
+            }
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v[u][c] = ld16(src + u * 64 + c * 16);
-                sc[u] = *reinterpret_cast<const uint32_t*>(a1s + tok * (D / 32) + (kt0 + u) * 4);
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const int i = i0 + u * kGatherThreads;
+                if (i < pieces) *reinterpret_cast<uint4*>(dst + int64_t(i) * 16) = v[u];
             }
         }
-#pragma unroll
-        for (int u = 0; u < kGatherKt; ++u) {
-            if (u < nk) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<uint4*>(a1f + frag_code_off(row, kt0 + u, c, KT)) = v[u][c];
-                *reinterpret_cast<uint32_t*>(a1fs + frag_scale_off(row, kt0 + u, cap)) = sc[u];
-            }
-        }
+        // scale words: (kt, r) for kt = threadIdx.x / 16, + 16, ...
+        const uint8_t* ssrc = a1s + int64_t(sr / topk) * (D / 32);
+#pragma unroll 1
+        for (int kt = threadIdx.x / 16; kt < KT; kt += kGatherThreads / 16)
+            *reinterpret_cast<uint32_t*>(a1fs + frag_scale_off(row, kt, cap)) =
+                *reinterpret_cast<const uint32_t*>(ssrc + kt * 4);
     }
 }
 
@@ -572,12 +573,11 @@ hipError_t launch_gather_a1(const uint8_t* a1q, const uint8_t* a1s, const int32_
                             uint8_t* a1f, uint8_t* a1fs, int n_cu, hipStream_t stream,
                             const KernelEvents& ev)
 {
-    const int64_t n = cap * ((D / 128 + kGatherKt - 1) / kGatherKt);
-    if (n == 0) return hipSuccess;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > int64_t(n_cu) * 8) blocks = int64_t(n_cu) * 8;
-    MOE_LAUNCH(gather_a1_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, ev, a1q, a1s,
-               sorted_route, num_valid, M, D, topk, cap, a1f, a1fs);
+    const int64_t slices = cap / 16;
+    if (slices == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>(slices, int64_t(n_cu) * 8);
+    MOE_LAUNCH(gather_a1_kernel, dim3(unsigned(blocks)), dim3(kGatherThreads), 0, stream, ev, a1q,
+               a1s, sorted_route, num_valid, M, D, topk, cap, a1f, a1fs);
     return hipGetLastError();
 }
 
