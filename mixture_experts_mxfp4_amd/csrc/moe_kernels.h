@@ -33,9 +33,9 @@ hipError_t launch_route_sort(const int32_t* ids, const float* tw, int M, int top
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                              uint8_t* scales, int n_cu, hipStream_t stream);
 
-// Route sort + activation quantization: one launch (workgroup 0 sorts, the
-// others quantize), or for long lists two (counting + quantization, then the
-// chunked scatter).
+// Route sort + activation quantization in one launch: the first workgroup
+// (short lists) or the first route_chunks workgroups (long lists) sort, the
+// others quantize.
 struct PrologueArgs {
     const int32_t* ids;
     const float* tw;
