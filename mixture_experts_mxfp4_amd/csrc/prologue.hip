@@ -359,10 +359,12 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
     }
 }
 
-// The same route sort for short route lists (decode): the workgroup stages
-// topk_ids / topk_w in LDS with one coalesced load, then ONE wave sorts from
-// LDS (one histogram row, DPP wave scans, no further barriers).  The output
-// order is identical to route_sort_body's (ascending route per expert).
+// The same route sort for short route lists: the workgroup stages topk_ids /
+// topk_w in LDS with one coalesced load and counts them with LDS atomics, then
+// ONE wave scans (DPP wave scans), writes each expert's blocks and padding
+// rows, and scatters from LDS (no further barriers).  Nothing is filled
+// beforehand: every row is written once, by the scatter or as padding.  The
+// output order is identical to route_sort_body's (ascending route per expert).
 constexpr int kShortList = 4096;
 
 __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* __restrict__ tw_g,
@@ -375,32 +377,26 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
     int32_t* ids = lds;                                          // [R]
     float* tw = reinterpret_cast<float*>(lds + kShortList);      // [R]
     int32_t* cnt = lds + 2 * kShortList;                         // [E]
-    for (int r = threadIdx.x; r < M * topk; r += kPrologueThreads) {
-        ids[r] = ids_g[r];
+    const int R = M * topk;
+    for (int e = threadIdx.x; e < E; e += kPrologueThreads) cnt[e] = 0;
+    __syncthreads();
+    // pass 1: the whole workgroup stages the list in LDS and counts it (order-
+    // free LDS atomics; only the scatter below needs the ordered walk)
+    for (int r = threadIdx.x; r < R; r += kPrologueThreads) {
+        const int id = ids_g[r];
+        ids[r] = id;
         tw[r] = tw_g[r];
+        if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
     }
-    fill_padding(M * topk, bm, nb_cap, sorted_route, sorted_w, block_expert);
     __syncthreads();
     if (threadIdx.x >= kWave) return;
     const int lane = threadIdx.x;
-    const int R = M * topk;
     const int nbits = E > 1 ? 32 - __builtin_clz(unsigned(E - 1)) : 0;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-#pragma unroll 1
-    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
-    __builtin_amdgcn_wave_barrier();
-    // pass 1: histogram
-#pragma unroll 1
-    for (int base = 0; base < R; base += kWave) {
-        const int r = base + lane;
-        const int id = r < R ? ids[r] : -1;
-        const bool valid = id >= 0 && id < E;
-        const uint64_t peers = same_expert_lanes(id, valid, nbits);
-        if (valid && (peers & lanes_below) == 0) cnt[id] += __popcll(peers);
-        __builtin_amdgcn_wave_barrier();
-    }
-    // scan of padded counts; cnt[e] becomes the expert's first row
+    // scan of padded counts; cnt[e] becomes the expert's first row.  The
+    // lane of expert e also writes its blocks' records and its padding rows
+    // (no other store touches those rows, so nothing is filled beforehand).
     int carry = 0, vcarry = 0;
 #pragma unroll 1
     for (int e0 = 0; e0 < E; e0 += kWave) {
@@ -419,11 +415,22 @@ __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* 
                     *reinterpret_cast<int4*>(block_info + 4 * b) =
                         make_int4(e, base_e / bm, padded / bm, total);
             }
+#pragma unroll 1
+            for (int p = base_e + total; p < base_e + padded; ++p) {
+                sorted_route[p] = R;
+                sorted_w[p] = 0.0f;
+            }
         }
         carry += __builtin_amdgcn_readlane(inc, kWave - 1);
         vcarry += __builtin_amdgcn_readlane(vinc, kWave - 1);
         __builtin_amdgcn_wave_barrier();
     }
+    // rows past the used blocks are padding, blocks past them unused
+    for (int64_t p = carry + lane; p < int64_t(nb_cap) * bm; p += kWave) {
+        sorted_route[p] = R;
+        sorted_w[p] = 0.0f;
+    }
+    for (int b = carry / bm + lane; b < nb_cap; b += kWave) block_expert[b] = -1;
     if (lane == 0) {
         num_valid[0] = carry;
         num_valid[1] = vcarry;
