@@ -199,9 +199,9 @@ int moe_mxfp4_block_m(int M, int D, int I, int E, int topk);
 int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m);
 
 /* Kernel launches moe_mxfp4_forward enqueues for this shape (0 for an invalid
- * shape or M = 0): DIRECT 2 (stage 1, stage 2); STREAM 4, or 5 when the route
- * sort runs as a counting and a scattering launch (more than 4,096 routes);
- * TILED one more than STREAM (the sorted copy of the activations). */
+ * shape or M = 0): DIRECT 2 (stage 1, stage 2); STREAM 4 (route sort with the
+ * activation quantization, stage 1, stage 2, slot sum); TILED one more than
+ * STREAM (the sorted copy of the activations). */
 int moe_mxfp4_launch_count(int M, int D, int I, int E, int topk);
 
 /* ---------------------------------------------------------------------------

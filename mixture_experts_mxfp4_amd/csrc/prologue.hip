@@ -24,8 +24,8 @@
 // a 4x unrolled walk that keeps more loads in flight; every chunk workgroup
 // also counts the other chunks' routes (plain LDS atomics: counts need no
 // order), so the whole sort is one launch with no workgroup waiting on
-// another (9,216 routes: 20.3 us with the quantization, against 8.2 + 13.4 us
-// for a counting launch followed by a scattering one; 36,864 routes: 20.3
+// another (9,216 routes: 16.4 us with the quantization, against 8.2 + 13.4 us
+// for a counting launch followed by a scattering one; 36,864 routes: 20.4
 // against 15.1 + 13.0 us).
 //
 // Activation quantization (OCP MX v1.0; the FP4 branch of 754773 quantizes
