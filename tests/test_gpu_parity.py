@@ -330,7 +330,13 @@ def test_forward_route_list_long(binding, name):
     np.testing.assert_array_equal(dbg["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
 
 
-@pytest.mark.parametrize("M,k,E", [(3000, 9, 40), (5000, 9, 257), (4100, 9, 5)])
+@pytest.mark.parametrize("M,k,E", [
+    (3000, 9, 40), (5000, 9, 257), (4100, 9, 5),
+    (456, 9, 40),       # 4,104 routes: just past the short-list limit, a last chunk of 8
+    (1137, 9, 33),      # every chunk sees at most 8,192 other routes (loaded up front)
+    (1138, 9, 33),      # the first chunks see 8,194 (loaded in two batches)
+    (5000, 1, 1),       # one expert, one slot per token
+])
 def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     """Long lists sorted in chunks over several workgroups, with invalid ids,
     repeated ids within a token and one hot expert: the forward's route list
@@ -339,7 +345,8 @@ def test_forward_route_list_chunked_edge_ids(binding, M, k, E):
     rng = np.random.default_rng(M + E)
     ids = rng.integers(-2, E + 2, (M, k)).astype(np.int32)
     ids[:, 0] = 0
-    ids[::3, 1] = ids[::3, 0]
+    if k > 1:
+        ids[::3, 1] = ids[::3, 0]
     ids[::7, -1] = 1 << 20
     tw = rng.random((M, k)).astype(np.float32)
     prep = binding.moe_mxfp4_prepare_weights(
