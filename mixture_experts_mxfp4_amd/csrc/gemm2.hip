@@ -20,11 +20,11 @@
 // Tiling: a workgroup (4 waves) owns one block of BM = 16*RT sorted rows and
 // 256*NG output columns (units in the XCD-aware order of xcd_unit); each wave
 // owns NG groups of 64 columns (4 MFMA tiles per row tile each) and runs the
-// whole K = I loop for each, streaming 1 KiB weight fragments; the A fragments (MXFP4 h, written by stage 1 in the
-// fragment layout) are contiguous 1 KiB loads as well.  Weight loads are
-// non-temporal, except in gemm2_simple_kernel for experts with several blocks,
-// whose blocks at one column tile share the slice through L2 (64 tokens on
-// E=33: 47.6 -> 44.9 us).
+// whole K = I loop for each, streaming 1 KiB weight fragments; the A
+// fragments (MXFP4 h, written by stage 1 in the fragment layout) are
+// contiguous 1 KiB loads as well.  Weight loads are non-temporal, except in
+// gemm2_simple_kernel for experts with several blocks, whose blocks at one
+// column tile share the slice through L2 (64 tokens on E=33: 47.6 -> 44.9 us).
 #include <type_traits>
 
 #include "moe_common.h"
