@@ -111,30 +111,50 @@ int64_t route_capacity(int M, int E, int topk, int bm)
 // E=33, I=2048 506 -> 280 us; I=512 172 -> 131 us; M=256, E=33, I=2048
 // 326 -> 260 us); at 32-64 they lose (M=128, E=33: 91 -> 107 us; M=1024,
 // E=257 Zipf: 255 -> 431 us).
-int choose_block_m(int M, int E, int topk)
+int choose_block_m(int M, int I, int E, int topk)
 {
     const double avg = double(M) * topk / double(E);
     if (avg < 8.0) return 16;
     if (avg < 32.0) return 32;
+    if (avg < 40.0 && I <= 512) return 32;   // paired 32-row blocks (pair_blocks)
     if (avg < 64.0) return 64;
     return 256;       // LDS-tiled kernels (gemm_tile.hip)
+}
+
+// 32-row blocks whose pairs run as 64-row units (the streaming kernels'
+// paired_block rule): an expert with 33 to 128 routes reads its weights once
+// per pair instead of once per block, while a Zipf-hot expert keeps 32-row
+// units, which spread it over more workgroups.  A pair's two workgroups split
+// the 64-row unit by columns, which doubles the activation reads per weight
+// byte; that pays where a block has few column units (I <= 512) and the
+// experts' routes cluster around 32-40.  Measured at D=7168 against 64-row
+// blocks: M=1024, E=257, I=256 Zipf 248.5 -> 235.2 us, uniform 233.4 -> 229.7;
+// M=128, E=33, I=512 79.2 -> 77.7.  It loses at 43.6 routes per expert (M=160,
+// E=33, I=512: 84.2 -> 86.4), at 59.5 (M=1700, E=257, I=256: 284 -> 318) and
+// at I=2048 (M=140, E=33: 184 -> 208 us; M=64, E=33, unpaired 32-row blocks:
+// 146.1 -> 149.8).
+bool pair_blocks(int M, int I, int E, int topk)
+{
+    const double avg = double(M) * topk / double(E);
+    return choose_block_m(M, I, E, topk) == 32 && avg >= 32.0;
 }
 
 // Few tokens with few routes per expert: the route-indexed kernels, which
 // need no route sort (a single-workgroup sort costs more than their whole
 // bookkeeping); otherwise the expert-sorted kernels.
-int choose_path(int M, int E, int topk)
+int choose_path(int M, int I, int E, int topk)
 {
     const int64_t R = int64_t(M) * topk;
     if (M <= moe::kDirectMaxTokens && topk <= moe::kMaxTopkDirect && R <= moe::kDirectMaxRoutes &&
-        E <= moe::kDirectMaxE && choose_block_m(M, E, topk) == 16)
+        E <= moe::kDirectMaxE && choose_block_m(M, I, E, topk) == 16)
         return MOE_MXFP4_PATH_DIRECT;
-    return choose_block_m(M, E, topk) == 256 ? MOE_MXFP4_PATH_TILED : MOE_MXFP4_PATH_STREAM;
+    return choose_block_m(M, I, E, topk) == 256 ? MOE_MXFP4_PATH_TILED : MOE_MXFP4_PATH_STREAM;
 }
 
 struct Layout {
     int path;
     int bm;
+    bool pair;          // block_m 32 with paired blocks (pair_blocks)
     int64_t cap, nb;
     size_t sorted_route, sorted_w, block_expert, num_valid, a1q, a1s, a1f, a1fs, a2q, a2s, partial,
         slot_expert, slot_layers, route_of, n_active, block_info, h16, barrier,
@@ -157,8 +177,9 @@ Layout layout(int M, int D, int I, int E, int topk, Variant v = Variant::Plain)
 {
     const bool a16 = v == Variant::A16W4;
     Layout L;
-    L.path = v != Variant::Plain ? MOE_MXFP4_PATH_DIRECT : choose_path(M, E, topk);
-    L.bm = choose_block_m(M, E, topk);
+    L.path = v != Variant::Plain ? MOE_MXFP4_PATH_DIRECT : choose_path(M, I, E, topk);
+    L.bm = choose_block_m(M, I, E, topk);
+    L.pair = L.bm == 32 && pair_blocks(M, I, E, topk);
     L.cap = route_capacity(M, E, topk, L.bm);
     L.nb = L.cap / L.bm;
     size_t off = 0;
@@ -227,7 +248,7 @@ int check_shape(int M, int D, int I, int E, int topk)
     if (M < 0 || E < 1 || topk < 1 || topk > kMaxTopk || !dims_ok(D, I))
         return MOE_MXFP4_ERR_INVALID_ARG;
     if (E > kMaxE || int64_t(M) * topk > kMaxRoutes) return MOE_MXFP4_ERR_UNSUPPORTED;
-    if (choose_path(M, E, topk) == MOE_MXFP4_PATH_TILED && !tiled_offsets_ok(M, D, I, E, topk))
+    if (choose_path(M, I, E, topk) == MOE_MXFP4_PATH_TILED && !tiled_offsets_ok(M, D, I, E, topk))
         return MOE_MXFP4_ERR_UNSUPPORTED;
     return MOE_MXFP4_OK;
 }
@@ -368,13 +389,13 @@ int forward_impl(const uint16_t* hidden, const uint8_t* w13, const uint8_t* w13_
 
     moe::Gemm1Args g1{a1q, a1s, a1f, a1fs, w13, w13_scale, sorted_route, block_expert, num_valid,
                       a2q, a2s, dbg ? dbg->h : nullptr, M, D, I, topk, L.bm, nb, L.cap,
-                      dbg ? dbg->stage1_clock : nullptr, block_info, n_cu};
+                      dbg ? dbg->stage1_clock : nullptr, block_info, n_cu, L.pair};
     const moe::KernelEvents ev1 = kernel_events(dbg, 1);
     e = tile ? moe::launch_gemm1_tile(g1, stream, ev1) : moe::launch_gemm1(g1, stream, ev1);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
 
     moe::Gemm2Args g2{a2q, a2s, w2, w2_scale, sorted_route, sorted_w, block_expert, num_valid,
-                      partial, M, D, I, topk, L.bm, nb, L.cap, block_info, nullptr, n_cu};
+                      partial, M, D, I, topk, L.bm, nb, L.cap, block_info, nullptr, n_cu, L.pair};
     const moe::KernelEvents ev2 = kernel_events(dbg, 2);
     e = tile ? moe::launch_gemm2_tile(g2, stream, ev2) : moe::launch_gemm2(g2, stream, ev2);
     if (e != hipSuccess) return MOE_MXFP4_ERR_HIP;
@@ -415,13 +436,13 @@ MOE_API const char* moe_mxfp4_status_string(int status)
 MOE_API int moe_mxfp4_block_m(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk)) return 0;
-    return choose_block_m(M, E, topk);
+    return choose_block_m(M, I, E, topk);
 }
 
 MOE_API int moe_mxfp4_launch_count(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk) || M == 0) return 0;
-    const int path = choose_path(M, E, topk);
+    const int path = choose_path(M, I, E, topk);
     if (path == MOE_MXFP4_PATH_DIRECT) return 2;
     // prologue (sort + quantization), the tiled path's sorted activation
     // copy, stage 1, stage 2, the slot sum
@@ -457,7 +478,7 @@ MOE_API int moe_mxfp4_wall_clock_khz(void)
 MOE_API int moe_mxfp4_path(int M, int D, int I, int E, int topk)
 {
     if (check_shape(M, D, I, E, topk)) return 0;
-    return choose_path(M, E, topk);
+    return choose_path(M, I, E, topk);
 }
 
 MOE_API int64_t moe_mxfp4_route_capacity(int M, int E, int topk, int block_m)

@@ -39,37 +39,21 @@ constexpr int kRedTiles = 2;
 template <int RT, int NG>
 constexpr int g1_unroll() { return NG == 1 ? (RT <= 2 ? 4 : 2) : (RT <= 2 ? 2 : 1); }
 
-template <int RT, int NG>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
-gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
-                          const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
-                          const int32_t* __restrict__ sorted_route,
-                          const int32_t* __restrict__ block_expert,
-                          const int32_t* __restrict__ num_valid, uint8_t* __restrict__ a2q,
-                          uint8_t* __restrict__ a2s, uint16_t* __restrict__ h_dbg, int M, int D,
-                          int I, int topk, int64_t cap, uint64_t* clk)
+// One unit: the 16*RT sorted rows from row0 (all of expert e) times the NG
+// MXFP4 groups of h from c0.  red: the LDS of the partial-sum passes.
+template <int RT, int NG, typename Red>
+__device__ __forceinline__ void g1_unit(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
+                                        const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
+                                        const int32_t* __restrict__ sorted_route,
+                                        uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s,
+                                        uint16_t* __restrict__ h_dbg, int M, int D, int I, int topk,
+                                        int64_t cap, int64_t row0, int c0, int e, bool shared_w, Red& red)
 {
-    constexpr int BM = 16 * RT;
     constexpr int U = g1_unroll<RT, NG>();
     // the partial sums meet in LDS kRedTiles row tiles at a time:
-    // [wave][row tile][slice][i][lane]
+    // red[wave][row tile][slice][i][lane]
     constexpr int RTH = RT < kRedTiles ? RT : kRedTiles;
     constexpr int WPT = 4 / RTH;          // waves finishing each row tile of a pass
-    __shared__ float red[4][RTH][4][4][kWave];
-
-    span_begin(clk);
-    int xg, blk;                          // NG-group pair xg of block blk (XCD-aware order)
-    const int nb_used = num_valid[0] / BM;
-    if (!xcd_unit(I / (32 * NG), nb_used, xg, blk)) {
-        span_end(clk);
-        return;
-    }
-    const int c0 = xg * NG;               // first MXFP4 group of h = 64-row group of w13p
-    const int e = block_expert[blk];
-    // an expert with several blocks: its blocks at this xg run side by side on
-    // one XCD and share the weight slice through L2 (cached loads)
-    const bool shared_w = (blk > 0 && block_expert[blk - 1] == e) ||
-                          (blk + 1 < nb_used && block_expert[blk + 1] == e);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int R = M * topk;
     const int KT = D / 128;
@@ -80,7 +64,7 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
     bool ok[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int sr = sorted_route[blk * BM + rt * 16 + lane % 16];
+        const int sr = sorted_route[row0 + rt * 16 + lane % 16];
         ok[rt] = sr < R;
         const int64_t tok = ok[rt] ? sr / topk : 0;
         a_ptr[rt] = a1q + tok * a_row + (lane / 16) * 16;
@@ -171,7 +155,7 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
                 const uint32_t h0 = f32_to_bf16_rne(silu_fast(s4[0]) * s4[2]);
                 const uint32_t h1 = f32_to_bf16_rne(silu_fast(s4[1]) * s4[3]);
                 const int row = 4 * (lane / 16) + i;                     // row within the tile
-                const int64_t srow = int64_t(blk) * BM + rt * 16 + row;  // sorted row
+                const int64_t srow = row0 + rt * 16 + row;               // sorted row
                 if (h_dbg) {
                     h_dbg[srow * I + c * 32 + lane % 16] = uint16_t(h0);
                     h_dbg[srow * I + c * 32 + 16 + lane % 16] = uint16_t(h1);
@@ -191,6 +175,69 @@ gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __rest
             }
         }
     }
+}
+
+// Uniform blocks of BM = 16*RT rows: one unit per (group pair, block).
+template <int RT, int NG>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gemm1_swiglu_quant_kernel(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
+                          const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
+                          const int32_t* __restrict__ sorted_route,
+                          const int32_t* __restrict__ block_expert,
+                          const int32_t* __restrict__ num_valid, uint8_t* __restrict__ a2q,
+                          uint8_t* __restrict__ a2s, uint16_t* __restrict__ h_dbg, int M, int D,
+                          int I, int topk, int64_t cap, uint64_t* clk)
+{
+    constexpr int BM = 16 * RT;
+    constexpr int RTH = RT < kRedTiles ? RT : kRedTiles;
+    __shared__ float red[4][RTH][4][4][kWave];
+    span_begin(clk);
+    int xg, blk;                          // NG-group pair xg of block blk (XCD-aware order)
+    const int nb_used = num_valid[0] / BM;
+    if (xcd_unit(I / (32 * NG), nb_used, xg, blk)) {
+        const int e = block_expert[blk];
+        // an expert with several blocks: its blocks at this xg run side by side on
+        // one XCD and share the weight slice through L2 (cached loads)
+        const bool shared_w = (blk > 0 && block_expert[blk - 1] == e) ||
+                              (blk + 1 < nb_used && block_expert[blk + 1] == e);
+        g1_unit<RT, NG>(a1q, a1s, w13p, w13sp, sorted_route, a2q, a2s, h_dbg, M, D, I, topk, cap,
+                        int64_t(blk) * BM, xg * NG, e, shared_w, red);
+    }
+    span_end(clk);
+}
+
+// 32-row blocks, where the blocks of an expert with few of them run in pairs
+// as 64-row units (paired_block): the workgroup of block j of a pair takes
+// the pair's 64 rows for group j of the group pair (same accumulator count
+// as a 32-row unit of two groups), so the pair reads each weight group once
+// and both workgroups work.  An expert with 33 to 64 routes then reads its
+// weights once, not once per block; a Zipf-hot expert's many blocks keep
+// 32-row units.
+template <int NG>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gemm1_swiglu_quant_kernel_paired(const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s,
+                   const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ w13sp,
+                   const int32_t* __restrict__ sorted_route, const int4* __restrict__ block_info,
+                   const int32_t* __restrict__ num_valid, uint8_t* __restrict__ a2q,
+                   uint8_t* __restrict__ a2s, uint16_t* __restrict__ h_dbg, int M, int D, int I,
+                   int topk, int64_t cap, uint64_t* clk)
+{
+    __shared__ float red[4][kRedTiles][4][4][kWave];
+    span_begin(clk);
+    int xg, blk;
+    if (xcd_unit(I / (32 * NG), num_valid[0] / 32, xg, blk)) {
+        const int4 bi = block_info[blk];      // expert, its first block, its block count, routes
+        // other units of the expert read the same weight slice: cached loads
+        if (!paired_block(bi, blk)) {
+            g1_unit<2, NG>(a1q, a1s, w13p, w13sp, sorted_route, a2q, a2s, h_dbg, M, D, I, topk, cap,
+                           int64_t(blk) * 32, xg * NG, bi.x, bi.z > 1, red);
+        } else {
+            const int j = (blk - bi.y) & 1;
+            g1_unit<4, NG / 2>(a1q, a1s, w13p, w13sp, sorted_route, a2q, a2s, h_dbg, M, D, I, topk,
+                               cap, int64_t(blk - j) * 32, xg * NG + j * (NG / 2), bi.x, bi.z > 2,
+                               red);
+        }
+    }
     span_end(clk);
 }
 
@@ -205,12 +252,23 @@ static hipError_t launch_g1(const Gemm1Args& a, hipStream_t stream, const Kernel
     return hipGetLastError();
 }
 
+static hipError_t launch_g1_paired(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
+{
+    constexpr int NG = stream_stage1_groups(32);
+    if (!a.block_info) return hipErrorInvalidValue;
+    MOE_LAUNCH((gemm1_swiglu_quant_kernel_paired<NG>), dim3(tile_grid(a.I / (32 * NG), a.nb_cap)),
+               dim3(kGemmThreads), 0, stream, ev, a.a1q, a.a1s, a.w13p, a.w13sp, a.sorted_route,
+               reinterpret_cast<const int4*>(a.block_info), a.num_valid, a.a2q, a.a2s, a.h_dbg,
+               a.M, a.D, a.I, a.topk, a.cap, a.clk);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev)
 {
     if (a.nb_cap == 0) return hipSuccess;
     switch (a.block_m) {
     case 16: return launch_g1<1>(a, stream, ev);
-    case 32: return launch_g1<2>(a, stream, ev);
+    case 32: return a.pair_blocks ? launch_g1_paired(a, stream, ev) : launch_g1<2>(a, stream, ev);
     case 64: return launch_g1<4>(a, stream, ev);
     default: return hipErrorInvalidValue;
     }

@@ -34,71 +34,71 @@ namespace moe {
 
 constexpr int kGemmThreads = 256;
 
-// K tiles per load batch.  64-row blocks carry four row tiles of accumulators; batching more
-// than one K tile raises their register count and measured slower on the 1100-token prefill.
+// K tiles per load batch.  64-row units take one: batching more raised the register count
+// (five waves per SIMD fit at one) and measured slower on the 1100-token prefill.
 template <int RT>
 constexpr int g2_unroll() { return RT <= 2 ? 4 : 1; }
 
-// Four waves per SIMD: the register allocation then fits 128 registers (116
-// VGPRs at 64-row blocks, no accumulation registers) instead of taking 150 and
-// three waves; one wave more per SIMD keeps more weight loads in flight
-// (prefill stage 2 90 -> 88.5 us, 128 tokens on E=33 19 -> 17 us).
-template <int RT>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)))
-gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
-                      const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
-                      const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
-                      const int32_t* __restrict__ block_expert,
-                      const int32_t* __restrict__ num_valid, uint16_t* __restrict__ partial,
-                      int M, int D, int I, int topk, int64_t cap)
+// Staged output rows of a unit of 16*RT rows x 64*NQ columns: the row's bf16
+// plus 16 B, so that consecutive rows start four banks apart.
+template <int NQ>
+constexpr int stage_row() { return 64 * NQ * 2 + 16; }
+template <int RT, int NQ>
+constexpr int stage_bytes() { return 16 * RT * stage_row<NQ>(); }
+
+// One unit: the 16*RT sorted rows from row0 (all of expert e) times the
+// 64*NQ output columns from col0 (each wave NQ 16-column MFMA tiles of one
+// prepared 64-row group).  stage, s_route: LDS of at least 16*RT staged rows
+// and routes.
+template <int RT, int NQ>
+__device__ __forceinline__ void g2_unit(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
+                                        const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
+                                        const int32_t* __restrict__ sorted_route,
+                                        const float* __restrict__ sorted_w, uint16_t* __restrict__ partial,
+                                        int M, int D, int I, int topk, int64_t cap, int64_t row0, int col0,
+                                        int e, bool shared_w, uint8_t* stage, int32_t* s_route)
 {
+    static_assert(NQ == 2 || NQ == 4, "a wave covers half or all of a 64-row weight group");
     constexpr int BM = 16 * RT;
     constexpr int U = g2_unroll<RT>();
-    constexpr int kRow = 256 * 2 + 16;       // staged output row: 256 bf16 + 16 B bank stagger
-    __shared__ __attribute__((aligned(16))) uint8_t stage[BM * kRow];
-    __shared__ int32_t s_route[BM];
-    int ct, blk;                           // 256-column tile ct of block blk (XCD-aware order)
-    const int nb_used = num_valid[0] / BM;
-    if (!xcd_unit(D / 256, nb_used, ct, blk)) return;
-    const int e = block_expert[blk];
-    // an expert with several blocks: its blocks at this ct run side by side on
-    // one XCD and share the weight slice through L2 (cached loads)
-    const bool shared_w = (blk > 0 && block_expert[blk - 1] == e) ||
-                          (blk + 1 < nb_used && block_expert[blk + 1] == e);
+    constexpr int kCols = 64 * NQ;          // output columns of the unit
+    constexpr int kRow = stage_row<NQ>();
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int n64 = ct * 4 + wave;
+    const int wcol = col0 + wave * 16 * NQ; // the wave's first output column
+    const int n64 = wcol / 64, q0 = (wcol % 64) / 16;
     const int KT = I / 128;
     const int R = M * topk;
 
-    const uint8_t* wb = w2p + int64_t(e) * D * (I / 2) + int64_t(n64) * KT * 4096 + lane * 16;
+    const uint8_t* wb = w2p + int64_t(e) * D * (I / 2) + int64_t(n64) * KT * 4096 + q0 * 1024 + lane * 16;
     const uint8_t* sb = w2sp + int64_t(e) * D * (I / 32) + int64_t(n64) * KT * 256 + lane * 4;
     // A operand: the 1 KiB fragment of row tile rt at K tile kt; scales kt-major
     const uint8_t* a_ptr[RT];
     const uint8_t* as_ptr[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int64_t row0 = int64_t(blk) * BM + rt * 16;
-        a_ptr[rt] = a2q + frag_code_off(row0, 0, 0, KT) + lane * 16;
-        as_ptr[rt] = a2s + frag_scale_off(row0 + lane % 16, 0, cap);
+        const int64_t r0 = row0 + rt * 16;
+        a_ptr[rt] = a2q + frag_code_off(r0, 0, 0, KT) + lane * 16;
+        as_ptr[rt] = a2s + frag_scale_off(r0 + lane % 16, 0, cap);
     }
     const int ash = 8 * (lane / 16);
 
-    v4f acc[RT][4];
+    v4f acc[RT][NQ];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < NQ; ++q) acc[rt][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto steps = [&](auto u_const, auto nt_const, int kt) {
         constexpr int UU = decltype(u_const)::value;
         constexpr bool NT = decltype(nt_const)::value;
         uint32_t sw[UU], sa[UU][RT];
-        uint4 b[UU][4], a[UU][RT];
+        uint4 b[UU][NQ], a[UU][RT];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
-            sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256);
+            // byte q0 + q of the group's scale word: column tile q of this wave
+            sw[u] = *reinterpret_cast<const uint32_t*>(sb + (kt + u) * 256) >> (8 * q0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < NQ; ++q)
                 b[u][q] = NT ? ld16_nt(wb + int64_t((kt + u) * 4 + q) * 1024)
                              : ld16(wb + int64_t((kt + u) * 4 + q) * 1024);
 #pragma unroll
@@ -112,7 +112,7 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < NQ; ++q)
                     // weights as the first operand: acc[rt][q] holds the transposed
                     // 16x16 tile (lane: row rt*16 + lane%16, columns 4*(lane/16) + i)
                     acc[rt][q] = mfma_fp4_16x16x128(b[u][q], a[u][rt], acc[rt][q],
@@ -130,16 +130,17 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
         kloop(std::true_type{});
 
     // Epilogue: the routing weight times the sum, rounded to bf16, goes through
-    // LDS as the block's BM x 256 tile; then each half-wave stores one row's
-    // 512 contiguous bytes of its route's partial row (padding rows skipped).
-    if (threadIdx.x < BM) s_route[threadIdx.x] = sorted_route[int64_t(blk) * BM + threadIdx.x];
+    // LDS as the unit's BM x kCols tile; then 4*NQ consecutive lanes store one
+    // row's contiguous 2*kCols bytes of its route's partial row (padding rows
+    // skipped).
+    if (threadIdx.x < BM) s_route[threadIdx.x] = sorted_route[row0 + threadIdx.x];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int row = rt * 16 + lane % 16;
-        const float w = sorted_w[int64_t(blk) * BM + row];
+        const float w = sorted_w[row0 + row];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = wave * 64 + q * 16 + 4 * (lane / 16);
+        for (int q = 0; q < NQ; ++q) {
+            const int col = wave * 16 * NQ + q * 16 + 4 * (lane / 16);
             uint2 v;
             v.x = f32x2_to_bf16x2(w * acc[rt][q][0], w * acc[rt][q][1]);
             v.y = f32x2_to_bf16x2(w * acc[rt][q][2], w * acc[rt][q][3]);
@@ -147,14 +148,76 @@ gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__
         }
     }
     __syncthreads();
+    constexpr int kChunks = kCols / 8;                  // 16-byte chunks per row
 #pragma unroll
-    for (int k = 0; k < BM / 8; ++k) {
-        const int c = k * kGemmThreads + threadIdx.x;   // 16-byte chunk: row c/32, chunk c%32
-        const int row = c >> 5, ch = c & 31;
+    for (int k = 0; k < BM * kChunks / kGemmThreads; ++k) {
+        const int c = k * kGemmThreads + threadIdx.x;   // row c / kChunks, chunk c % kChunks
+        const int row = c / kChunks, ch = c % kChunks;
         const int sr = s_route[row];
         const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kRow + ch * 16);
         if (sr < R)
-            *reinterpret_cast<uint4*>(partial + int64_t(sr) * D + ct * 256 + ch * 8) = v;
+            *reinterpret_cast<uint4*>(partial + int64_t(sr) * D + col0 + ch * 8) = v;
+    }
+}
+
+// Uniform blocks of BM = 16*RT rows: one unit per (256-column tile, block).
+// Four waves per SIMD at least: the register allocation then fits 128
+// registers (116 VGPRs at 64-row blocks, no accumulation registers) instead
+// of taking 150 and three waves; one wave more per SIMD keeps more weight
+// loads in flight (prefill stage 2 90 -> 88.5 us, 128 tokens on E=33 19 -> 17
+// us).
+template <int RT>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)))
+gemm2_simple_kernel(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
+                    const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
+                    const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
+                    const int32_t* __restrict__ block_expert,
+                    const int32_t* __restrict__ num_valid, uint16_t* __restrict__ partial,
+                    int M, int D, int I, int topk, int64_t cap)
+{
+    constexpr int BM = 16 * RT;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[stage_bytes<RT, 4>()];
+    __shared__ int32_t s_route[BM];
+    int ct, blk;                           // 256-column tile ct of block blk (XCD-aware order)
+    const int nb_used = num_valid[0] / BM;
+    if (!xcd_unit(D / 256, nb_used, ct, blk)) return;
+    const int e = block_expert[blk];
+    // an expert with several blocks: its blocks at this ct run side by side on
+    // one XCD and share the weight slice through L2 (cached loads)
+    const bool shared_w = (blk > 0 && block_expert[blk - 1] == e) ||
+                          (blk + 1 < nb_used && block_expert[blk + 1] == e);
+    g2_unit<RT, 4>(a2q, a2s, w2p, w2sp, sorted_route, sorted_w, partial, M, D, I, topk, cap,
+                   int64_t(blk) * BM, ct * 256, e, shared_w, stage, s_route);
+}
+
+// 32-row blocks, where the blocks of an expert with few of them run in pairs
+// as 64-row units (paired_block, the same rule as stage 1): the workgroup of
+// block j of a pair takes the pair's 64 rows for column half j of the tile
+// (same accumulator count as a 32-row unit of the whole tile, and the same
+// staged bytes).
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4)))
+gemm2_simple_kernel_paired(const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s,
+                   const uint8_t* __restrict__ w2p, const uint8_t* __restrict__ w2sp,
+                   const int32_t* __restrict__ sorted_route, const float* __restrict__ sorted_w,
+                   const int4* __restrict__ block_info, const int32_t* __restrict__ num_valid,
+                   uint16_t* __restrict__ partial, int M, int D, int I, int topk, int64_t cap)
+{
+    // staged rows: 32 x 256 or 64 x 128 columns
+    __shared__ __attribute__((aligned(16))) uint8_t stage[stage_bytes<2, 4>() > stage_bytes<4, 2>()
+                                                          ? stage_bytes<2, 4>() : stage_bytes<4, 2>()];
+    __shared__ int32_t s_route[64];
+    int ct, blk;                           // 256-column tile ct of block blk (XCD-aware order)
+    if (!xcd_unit(D / 256, num_valid[0] / 32, ct, blk)) return;
+    const int4 bi = block_info[blk];       // expert, its first block, its block count, routes
+    // other units of the expert at this ct run side by side on one XCD and
+    // share the weight slice through L2 (cached loads)
+    if (!paired_block(bi, blk)) {
+        g2_unit<2, 4>(a2q, a2s, w2p, w2sp, sorted_route, sorted_w, partial, M, D, I, topk, cap,
+                      int64_t(blk) * 32, ct * 256, bi.x, bi.z > 1, stage, s_route);
+    } else {
+        const int j = (blk - bi.y) & 1;
+        g2_unit<4, 2>(a2q, a2s, w2p, w2sp, sorted_route, sorted_w, partial, M, D, I, topk, cap,
+                      int64_t(blk - j) * 32, ct * 256 + j * 128, bi.x, bi.z > 2, stage, s_route);
     }
 }
 
@@ -292,6 +355,16 @@ static hipError_t launch_g2_simple(const Gemm2Args& a, hipStream_t stream, const
     return hipGetLastError();
 }
 
+static hipError_t launch_g2_paired(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev)
+{
+    if (!a.block_info) return hipErrorInvalidValue;
+    MOE_LAUNCH(gemm2_simple_kernel_paired, dim3(tile_grid(a.D / 256, a.nb_cap)), dim3(kGemmThreads), 0,
+               stream, ev, a.a2q, a.a2s, a.w2p, a.w2sp, a.sorted_route, a.sorted_w,
+               reinterpret_cast<const int4*>(a.block_info), a.num_valid, a.partial, a.M, a.D, a.I,
+               a.topk, a.cap);
+    return hipGetLastError();
+}
+
 // Few rows per block (decode, block_m 16): each wave walks two column groups
 // with double-buffered loads, which keeps enough weight bytes in flight with
 // half the workgroups.  Larger blocks keep one group per wave (their
@@ -303,7 +376,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEven
     case 16:
         return (a.D / 256) % 2 == 0 ? launch_g2<1, 2, 2>(a, stream, ev)
                                     : launch_g2<1, 2, 1>(a, stream, ev);
-    case 32: return launch_g2_simple<2>(a, stream, ev);
+    case 32: return a.pair_blocks ? launch_g2_paired(a, stream, ev) : launch_g2_simple<2>(a, stream, ev);
     case 64: return launch_g2_simple<4>(a, stream, ev);
     default: return hipErrorInvalidValue;
     }

@@ -81,8 +81,9 @@ struct Gemm1Args {
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
     uint64_t* clk = nullptr;       // optional kernel span (span_begin / span_end)
-    const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
+    const int32_t* block_info = nullptr;   // [nb_cap][4] (paired blocks, tiled kernels)
     int n_cu = 0;                  // compute units: the tiled kernel's persistent grid
+    bool pair_blocks = false;      // block_m 32: pairs of an expert's blocks as 64-row units
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream, const KernelEvents& ev = {});
 // 64-row gate_up groups per workgroup of the streaming stage 1 (grid: I/32 /
@@ -103,9 +104,10 @@ struct Gemm2Args {
     uint16_t* partial;          // bf16 [M*topk][D], weighted contribution per route
     int M, D, I, topk, block_m, nb_cap;
     int64_t cap;
-    const int32_t* block_info = nullptr;   // [nb_cap][4] (tiled kernels)
+    const int32_t* block_info = nullptr;   // [nb_cap][4] (paired blocks, tiled kernels)
     uint64_t* clk = nullptr;       // optional workgroup spans (tiled kernel)
     int n_cu = 0;                  // compute units: the tiled kernel's persistent grid
+    bool pair_blocks = false;      // block_m 32: pairs of an expert's blocks as 64-row units
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream, const KernelEvents& ev = {});
 
@@ -133,6 +135,15 @@ __device__ __forceinline__ bool xcd_unit(int X, int nb_used, int& x, int& blk)
     x = int(u / nb_used);
     blk = int(u % nb_used);
     return true;
+}
+// Streaming kernels at block_m 32 with pair_blocks: the blocks 2j, 2j+1 of an
+// expert with at most kPairMaxBlocks blocks form a 64-row unit (block_info
+// record bi: expert, first block, block count, routes), which the two blocks'
+// workgroups split by columns; a last odd block stays a 32-row unit.
+constexpr int kPairMaxBlocks = 4;
+__device__ __forceinline__ bool paired_block(int4 bi, int blk)
+{
+    return bi.z <= kPairMaxBlocks && ((blk - bi.y) ^ 1) < bi.z;
 }
 hipError_t tile_allow_lds();   // lift the dynamic-LDS limit of the tiled kernels
 // Workgroups of a persistent tiled launch: one per CU (a multiple of the XCD

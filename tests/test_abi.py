@@ -61,7 +61,9 @@ def test_block_m_and_capacity(binding):
     assert binding.moe_mxfp4_block_m(16, 7168, 256, 257, 9) == 16
     assert binding.moe_mxfp4_block_m(64, 7168, 2048, 33, 9) == 32
     assert binding.moe_mxfp4_block_m(4096, 7168, 2048, 33, 9) == 256
-    assert binding.moe_mxfp4_block_m(1024, 7168, 256, 257, 9) == 64
+    assert binding.moe_mxfp4_block_m(1024, 7168, 256, 257, 9) == 32    # paired blocks
+    assert binding.moe_mxfp4_block_m(1024, 7168, 2048, 257, 9) == 64
+    assert binding.moe_mxfp4_block_m(1700, 7168, 256, 257, 9) == 64
     assert binding.moe_mxfp4_block_m(16, 7168, 100, 257, 9) == 0       # I % 256 != 0
     for M, E, k, bm in [(16, 257, 9, 16), (1, 1, 1, 16), (4096, 33, 9, 64), (3, 500, 2, 32)]:
         cap = binding.moe_mxfp4_route_capacity(M, E, k, bm)

@@ -454,6 +454,26 @@ def test_forward_tiled_invalid_and_duplicate_ids(binding):
     _check_forward(case, dbg, "tiled invalid/duplicate ids")
 
 
+def test_forward_paired_blocks(binding):
+    """32-row blocks whose pairs run as 64-row units split by columns (37.5
+    routes per expert at I=256): experts with 33 and 64 routes (one pair), 65
+    (a pair and a lone block), 97 and 128 (two pairs), 129 (five blocks: 32-row
+    units), a lone 20-route block, unused experts, and the shared expert with
+    every token (seventeen blocks: 32-row units)."""
+    M, D, I, E = 536, 512, 256, 30
+    counts = [33, 64, 65, 97, 128, 129, 20]
+    rng = np.random.default_rng(61)
+    ids = np.empty((M, 2), np.int32)
+    ids[:, 0] = rng.permutation(np.repeat(np.arange(len(counts), dtype=np.int32), counts))
+    ids[:, 1] = E - 1
+    tw = rng.random((M, 2)).astype(np.float32)
+    assert 32 <= M * 2 / E < 40                  # the paired-block range at I <= 512
+    case = custom_case(M, D, I, E, 1, 62, ids=torch.from_numpy(ids), tw=torch.from_numpy(tw))
+    dbg = case.run_gpu(debug=True)
+    assert dbg["path"] == binding.PATH_STREAM and dbg["block_m"] == 32
+    _check_forward(case, dbg, "paired 32-row blocks")
+
+
 def test_forward_all_tokens_one_expert(binding):
     """Every token routed to expert 0 (many blocks of one expert) plus the shared one."""
     M, D, I, E = 300, 512, 512, 4
