@@ -194,7 +194,7 @@ int moe_mxfp4_path(int M, int D, int I, int E, int topk);
 
 /* The block_m (rows per expert block of the sorted route list; the row tile
  * of the DIRECT path) the forward uses for this shape, and the capacity
- * (rows) of the sorted route list.  With 32 to 40 routes per expert on
+ * (rows) of the sorted route list.  With 32 to 37 routes per expert on
  * average and I <= 512 the forward's 32-row blocks run in pairs of an
  * expert's blocks as 64-row units (the route list itself is the plain
  * 32-row one). */

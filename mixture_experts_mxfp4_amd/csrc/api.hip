@@ -116,7 +116,7 @@ int choose_block_m(int M, int I, int E, int topk)
     const double avg = double(M) * topk / double(E);
     if (avg < 8.0) return 16;
     if (avg < 32.0) return 32;
-    if (avg < 40.0 && I <= 512) return 32;   // paired 32-row blocks (pair_blocks)
+    if (avg < 37.0 && I <= 512) return 32;   // paired 32-row blocks (pair_blocks)
     if (avg < 64.0) return 64;
     return 256;       // LDS-tiled kernels (gemm_tile.hip)
 }
@@ -127,12 +127,13 @@ int choose_block_m(int M, int I, int E, int topk)
 // units, which spread it over more workgroups.  A pair's two workgroups split
 // the 64-row unit by columns, which doubles the activation reads per weight
 // byte; that pays where a block has few column units (I <= 512) and the
-// experts' routes cluster around 32-40.  Measured at D=7168 against 64-row
+// experts' routes cluster around 32-37.  Measured at D=7168 against 64-row
 // blocks: M=1024, E=257, I=256 Zipf 248.5 -> 235.2 us, uniform 233.4 -> 229.7;
-// M=128, E=33, I=512 79.2 -> 77.7.  It loses at 43.6 routes per expert (M=160,
-// E=33, I=512: 84.2 -> 86.4), at 59.5 (M=1700, E=257, I=256: 284 -> 318) and
-// at I=2048 (M=140, E=33: 184 -> 208 us; M=64, E=33, unpaired 32-row blocks:
-// 146.1 -> 149.8).
+// M=300, E=80, I=256 114.0 -> 104.2; M=128, E=33, I=512 79.2 -> 77.7; M=256,
+// E=65, I=512 129.2 -> 128.6.  It loses at 38.5 routes per expert (M=1100,
+// E=257, I=256: 237.7 -> 242.9), at 43.6 (M=160, E=33, I=512: 84.2 -> 86.4),
+// at 59.5 (M=1700, E=257, I=256: 284 -> 318) and at I=2048 (M=140, E=33: 184
+// -> 208 us; M=64, E=33, unpaired 32-row blocks: 146.1 -> 149.8).
 bool pair_blocks(int M, int I, int E, int topk)
 {
     const double avg = double(M) * topk / double(E);

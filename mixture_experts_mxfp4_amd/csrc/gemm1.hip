@@ -15,12 +15,14 @@
 // units in the XCD-aware order of xcd_unit.  The four waves split the K
 // dimension; each wave runs NG x RT x 4 MFMA tiles of 16x16x128, streaming its weight
 // fragments (1 KiB each, contiguous) and gathering the block's activation rows
-// by token id.  Weight loads are non-temporal, except for experts with several
-// blocks: their blocks at one group pair run side by side on one XCD, and
-// cached loads let all but the first find the slice in L2 (prefill at E=257:
-// stage-1 fetch 604 -> 575 MB, 124.5 -> 118 us).  Partial sums meet in LDS; the epilogue
-// quantizes h with cross-lane reductions and writes it in sorted-row order in
-// the fragment layout (moe_common.h) that stage 2 loads contiguously.
+// by token id.  With paired 32-row blocks (gemm1_swiglu_quant_kernel_paired)
+// a pair's two workgroups take the pair's 64 rows for one group each.  Weight
+// loads are non-temporal, except for experts with several units: their units
+// at one group pair run side by side on one XCD, and cached loads let all but
+// the first find the slice in L2 (prefill at E=257: stage-1 fetch 604 -> 575
+// MB, 124.5 -> 118 us).  Partial sums meet in LDS; the epilogue quantizes h
+// with cross-lane reductions and writes it in sorted-row order in the
+// fragment layout (moe_common.h) that stage 2 loads contiguously.
 #include <type_traits>
 
 #include "moe_common.h"
@@ -29,8 +31,8 @@
 namespace moe {
 
 constexpr int kGemmThreads = 256;
-// Row tiles per LDS reduction pass of the epilogue: two (32 KiB of LDS at
-// four waves) leave room for a third workgroup per CU.
+// Row tiles per LDS reduction pass of the epilogue: two keep the pass at 32
+// KiB of LDS for four waves, whatever the block size.
 constexpr int kRedTiles = 2;
 
 // Loads of U consecutive K tiles are issued before their MFMAs so that every

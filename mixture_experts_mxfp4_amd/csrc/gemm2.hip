@@ -22,9 +22,12 @@
 // owns NG groups of 64 columns (4 MFMA tiles per row tile each) and runs the
 // whole K = I loop for each, streaming 1 KiB weight fragments; the A
 // fragments (MXFP4 h, written by stage 1 in the fragment layout) are
-// contiguous 1 KiB loads as well.  Weight loads are non-temporal, except in
-// gemm2_simple_kernel for experts with several blocks, whose blocks at one
-// column tile share the slice through L2 (64 tokens on E=33: 47.6 -> 44.9 us).
+// contiguous 1 KiB loads as well.  With paired 32-row blocks
+// (gemm2_simple_kernel_paired) a pair's two workgroups take the pair's 64
+// rows for half of the 256-column tile each.  Weight loads are non-temporal,
+// except in the simple kernels for experts with several units, whose units at
+// one column tile share the slice through L2 (64 tokens on E=33: 47.6 -> 44.9
+// us).
 #include <type_traits>
 
 #include "moe_common.h"
