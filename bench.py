@@ -37,6 +37,10 @@ Helper modes (used to make the committed rocprofv3 summaries):
                                stages (profiles/<kernel>_<workload>_mfma.txt)
                                from a `--pmc SQ_INSTS_VALU_MFMA_MOPS_F6F4
                                MfmaUtil` pass of the workload
+    --mfma-ceiling             the library's register-only FP4 MFMA probe
+                               (moe_mxfp4_mfma_probe) with random and with
+                               single-bit operands: the practical ceiling of
+                               the MFMA-bound kernels next to the published peak
 """
 import argparse
 import csv
@@ -534,6 +538,22 @@ def run(args):
 
 # ------------------------------------------------------- profiling helpers ---
 
+def mfma_ceiling(iters=2_000_000):
+    """The FP4 MFMA rate on register operands (no memory traffic), with random
+    and with single-bit operands, against the published dense peak."""
+    import torch
+
+    from mixture_experts_mxfp4_amd import binding
+    torch.cuda.set_device(0)
+    out = {"published_peak_tflops": FP4_PEAK_TFLOPS, "iters_per_wave": iters}
+    for name, rnd in (("random_operands", True), ("single_bit_operands", False)):
+        r = binding.moe_mxfp4_mfma_probe(rnd, iters)
+        out[name] = {"tflops": round(r["tflops"], 1), "shader_mhz": round(r["shader_mhz"], 1),
+                     "per_clock_frac": round(r["per_clock_frac"], 4),
+                     "frac_of_peak": round(r["tflops"] / FP4_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -688,6 +708,7 @@ def main():
     p.add_argument("--cpu-sample-s", type=float, default=16.0,
                    help="CPU-seconds of oracle work in the baseline sample")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--mfma-ceiling", action="store_true")
     p.add_argument("--mfma-summary", nargs=2, metavar=("WORKLOAD", "PMC_DIR"))
     p.add_argument("--summarize-stats", metavar="DIR")
     p.add_argument("--summarize-pmc", metavar="DIR")
@@ -709,6 +730,8 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration()
+    if args.mfma_ceiling:
+        return mfma_ceiling()
     if args.steps < 1:
         p.error("--steps must be >= 1")
     run(args)

@@ -39,6 +39,8 @@ _lib.moe_mxfp4_forward_debug.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ] + [_P] *
 _lib.moe_mxfp4_forward_debug.restype = _I
 _lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _P, _P]
 _lib.moe_mxfp4_wall_clock_khz.argtypes, _lib.moe_mxfp4_wall_clock_khz.restype = [], _I
+_lib.moe_mxfp4_mfma_probe.argtypes = [_I, _I, _P, _P, _P, _P]
+_lib.moe_mxfp4_mfma_probe.restype = _I
 _lib.moe_mxfp4_stage1_workgroups.argtypes = [_I] * 5
 _lib.moe_mxfp4_stage1_workgroups.restype = _I64
 _lib.moe_mxfp4_forward_profiled.restype = _I
@@ -80,7 +82,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_bl
            "moe_mxfp4_workspace_init", "moe_mxfp4_persistent_workgroups",
            "moe_mxfp4_forward_persistent", "moe_mxfp4_forward_persistent_debug",
            "moe_mxfp4_splitk_workspace_bytes", "moe_mxfp4_forward_splitk",
-           "moe_mxfp4_forward_splitk_debug")
+           "moe_mxfp4_forward_splitk_debug", "moe_mxfp4_mfma_probe")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -252,6 +254,16 @@ PATH_LAUNCHES = {PATH_DIRECT: (1, 2), PATH_STREAM: (0, 1, 2, 3), PATH_TILED: (0,
 def moe_mxfp4_wall_clock_khz() -> int:
     """Frequency of the device clock that stage-1 spans are counted in."""
     return int(_lib.moe_mxfp4_wall_clock_khz())
+
+
+def moe_mxfp4_mfma_probe(random_operands: bool, iters: int, stream=None) -> dict:
+    """Register-only FP4 MFMA rate on the current device: TFLOP/s, mean
+    shader clock (MHz) and share of the per-clock MFMA rate."""
+    tf, mhz, frac = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check("moe_mxfp4_mfma_probe",
+           _lib.moe_mxfp4_mfma_probe(int(bool(random_operands)), int(iters), ctypes.byref(tf),
+                                     ctypes.byref(mhz), ctypes.byref(frac), _stream(stream)))
+    return {"tflops": tf.value, "shader_mhz": mhz.value, "per_clock_frac": frac.value}
 
 
 def moe_mxfp4_stage1_workgroups(M, D, I, E, topk) -> int:

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
 SOURCES = ["api.hip", "prologue.hip", "prepare.hip", "gemm1.hip", "gemm2.hip", "gemm_tile.hip", "direct.hip",
-           "decode_fused.hip"]
+           "decode_fused.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -16,6 +16,7 @@
 #include <atomic>
 
 #include "moe_kernels.h"
+#include "probe.h"
 #include "moe_mxfp4.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -465,6 +466,23 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
         return moe::tile_persistent_grid(2 * I / 256, int(L.nb), n_cu);
     }
     return moe::tile_grid(I / (32 * moe::stream_stage1_groups(L.bm)), int(L.nb));
+}
+
+MOE_API int moe_mxfp4_mfma_probe(int random_operands, int iters, double* tflops, double* shader_mhz,
+                                 double* per_clock_frac, hipStream_t stream)
+{
+    if (iters < 1 || iters > (1 << 24) || !tflops || !shader_mhz || !per_clock_frac)
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    int n_cu = 0, khz = 0;
+    int st = device_check(&n_cu, nullptr, &khz);
+    if (st) return st;
+    moe::ProbeResult r{};
+    if (moe::run_mfma_probe(random_operands ? 1 : 0, iters, n_cu, khz, stream, &r) != hipSuccess)
+        return MOE_MXFP4_ERR_HIP;
+    *tflops = r.tflops;
+    *shader_mhz = r.shader_mhz;
+    *per_clock_frac = r.per_clock_frac;
+    return MOE_MXFP4_OK;
 }
 
 MOE_API int moe_mxfp4_wall_clock_khz(void)
