@@ -423,7 +423,9 @@ def test_forward_large_topk(binding, M, D, I, E, n_routed, seed, path):
     _check_forward(case, dbg, f"top-{case.topk} {path} M={M} E={E}")
 
 
-@pytest.mark.parametrize("M,E", [(20, 6), (8, 40)])      # sorted and route-indexed paths
+# sorted path (32-row blocks), paired 32-row blocks (33.3 routes per expert at
+# I=256), route-indexed path
+@pytest.mark.parametrize("M,E", [(20, 6), (100, 12), (8, 40)])
 def test_forward_invalid_and_duplicate_ids(binding, M, E):
     D, I = 512, 256
     rng = np.random.default_rng(5)
