@@ -365,7 +365,13 @@ __device__ void route_sort_body(const int32_t* __restrict__ ids, const float* __
 // rows, and scatters from LDS (no further barriers).  Nothing is filled
 // beforehand: every row is written once, by the scatter or as padding.  The
 // output order is identical to route_sort_body's (ascending route per expert).
-constexpr int kShortList = 4096;
+// Its scatter walks the list 64 routes at a time in that one wave, so longer
+// lists go to the workgroup sort (route_sort_body), whose waves scatter side
+// by side.  Measured (sort plus the activation quantization, one launch):
+// 576 routes at E=33 7.7 against 10.5 us; 900 routes at E=33 10.8 against
+// 10.0; 1,152 routes at E=257 18.7 against 14.3; 2,700 routes at E=257 39.0
+// against 17.1.
+constexpr int kShortList = 768;
 
 __device__ void route_sort_wave(const int32_t* __restrict__ ids_g, const float* __restrict__ tw_g,
                                 int M, int topk, int E, int bm, int nb_cap,

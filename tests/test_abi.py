@@ -226,13 +226,13 @@ def test_binding_refuses_host_tensors():
 
 def test_launch_count():
     """Launches per forward by path: 2 route-indexed; 4 streaming (one
-    prologue launch: the sort, chunked above 4,096 routes, and the activation
+    prologue launch: the sort, on a workgroup per 2,048-route chunk above 768 routes, and the activation
     quantization); tiled one more (the sorted copy of the activations)."""
     from mixture_experts_mxfp4_amd import binding
     assert binding.moe_mxfp4_launch_count(16, 7168, 256, 257, 9) == 2        # decode
     assert binding.moe_mxfp4_launch_count(64, 7168, 2048, 33, 9) == 4        # small batch
     assert binding.moe_mxfp4_launch_count(1024, 7168, 256, 257, 9) == 4      # prefill
     assert binding.moe_mxfp4_launch_count(4096, 7168, 2048, 33, 9) == 5      # large prefill
-    assert binding.moe_mxfp4_launch_count(1000, 768, 512, 3, 2) == 5         # tiled, short list
+    assert binding.moe_mxfp4_launch_count(1000, 768, 512, 3, 2) == 5         # tiled, one chunk
     assert binding.moe_mxfp4_launch_count(0, 7168, 256, 257, 9) == 0
     assert binding.moe_mxfp4_launch_count(16, 7000, 256, 257, 9) == 0        # D % 256 != 0

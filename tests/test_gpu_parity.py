@@ -332,7 +332,9 @@ def test_forward_route_list_long(binding, name):
 
 @pytest.mark.parametrize("M,k,E", [
     (3000, 9, 40), (5000, 9, 257), (4100, 9, 5),
-    (456, 9, 40),       # 4,104 routes: just past the short-list limit, a last chunk of 8
+    (86, 9, 40),        # 774 routes: just past the one-wave sort's limit, one chunk
+    (300, 9, 257),      # 2,700 routes: two chunks
+    (456, 9, 40),       # 4,104 routes: three chunks, a last chunk of 8
     (1137, 9, 33),      # every chunk sees at most 8,192 other routes (loaded up front)
     (1138, 9, 33),      # the first chunks see 8,194 (loaded in two batches)
     (5000, 1, 1),       # one expert, one slot per token
