@@ -395,7 +395,8 @@ def test_tiled_workspace_address_bit31(binding, high):
     (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
     (200, 512, 256, 257, 8, 28),      # sorted streaming path with block_m 16
     (37, 768, 768, 5, 3, 22),         # ragged M, D and I not multiples of 512
-    (130, 1024, 512, 33, 8, 23),      # several blocks per expert
+    (130, 1024, 512, 33, 8, 23),      # several blocks per expert (paired 32-row blocks)
+    (200, 512, 256, 33, 8, 32),       # 64-row blocks (54.5 routes per expert)
     (3, 256, 256, 2, 1, 24),          # smallest dims
     (1400, 512, 256, 5, 2, 25),       # LDS-tiled path (block_m 256), ragged blocks
     (1000, 768, 512, 3, 1, 26),       # LDS-tiled path, D not a multiple of 512
@@ -407,6 +408,23 @@ def test_forward_shapes(binding, M, D, I, E, n_routed, seed):
     log(f"forward shape M={M} D={D} I={I} E={E} topk={n_routed + 1}")
     case = custom_case(M, D, I, E, n_routed, seed)
     _check_forward(case, case.run_gpu(debug=True), f"shape M={M} D={D} I={I} E={E}")
+
+
+@pytest.mark.parametrize("M,D,I,E,n_routed,seed,path", [
+    (96, 16384, 1024, 9, 2, 71, "stream"),     # 128 K tiles per stage-1 unit, 64-row blocks
+    (640, 16384, 512, 3, 1, 72, "tiled"),      # 128 K stages per stage-1 tile, 4 per stage-2 tile
+])
+def test_forward_long_k(binding, M, D, I, E, n_routed, seed, path):
+    """D = 16,384, beyond the workloads' 7,168: the K loops of both stage-1
+    kernels run 128 K tiles.  Checked on a set of tokens covering every used
+    block (and its first and last 16-row slices), intermediates included."""
+    case = custom_case(M, D, I, E, n_routed, seed)
+    dbg = case.run_gpu(debug=True)
+    want = {"stream": binding.PATH_STREAM, "tiled": binding.PATH_TILED}[path]
+    assert dbg["path"] == want
+    toks = covering_tokens(case.ids, case.tw, case.E, dbg["block_m"], must=(0, case.M - 1))
+    log(f"long K {path} M={M} D={D} I={I} E={E}: block_m {dbg['block_m']}, oracle on {toks.size} tokens")
+    _check_forward(case, dbg, f"long K {path}", tokens=toks)
 
 
 @pytest.mark.parametrize("M,D,I,E,n_routed,seed,path", [
