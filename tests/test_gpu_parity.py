@@ -394,6 +394,7 @@ def test_tiled_workspace_address_bit31(binding, high):
     (1, 512, 256, 9, 2, 21),          # single token (route-indexed path)
     (32, 512, 256, 65, 8, 27),        # route-indexed, shared expert spans two row tiles
     (200, 512, 256, 257, 8, 28),      # sorted streaming path with block_m 16
+    (200, 768, 256, 257, 8, 33),      # block_m 16, an odd number of 256-column tiles
     (37, 768, 768, 5, 3, 22),         # ragged M, D and I not multiples of 512
     (130, 1024, 512, 33, 8, 23),      # several blocks per expert (paired 32-row blocks)
     (200, 512, 256, 33, 8, 32),       # 64-row blocks (54.5 routes per expert)
@@ -431,6 +432,9 @@ def test_forward_long_k(binding, M, D, I, E, n_routed, seed, path):
     (20, 512, 256, 130, 15, 51, "direct"),     # 16 slots: the route-indexed path's limit
     (100, 512, 256, 64, 19, 52, "stream"),     # 20 slots: the 32-slot reduction
     (300, 512, 256, 20, 16, 53, "tiled"),      # 17 slots on the LDS-tiled path
+    (60, 512, 256, 40, 14, 54, "stream"),      # 15 slots: the 16-slot reduction, two columns per thread
+    (600, 1024, 256, 40, 14, 55, "tiled"),     # 15 slots, eight columns per thread
+    (600, 1024, 256, 40, 19, 56, "tiled"),     # 20 slots, eight columns per thread
 ])
 def test_forward_large_topk(binding, M, D, I, E, n_routed, seed, path):
     """Many slots per token: per-token route tables on the route-indexed path,
