@@ -447,6 +447,49 @@ def test_forward_large_topk(binding, M, D, I, E, n_routed, seed, path):
     _check_forward(case, dbg, f"top-{case.topk} {path} M={M} E={E}")
 
 
+def _random_shapes(n=40, seed=2026):
+    """Seeded shapes across all paths and block sizes: M from 1 to 2,500, D and
+    I multiples of 256 up to 1,280 and 1,024, E from 2 to 300, up to 13 slots,
+    uniform or Zipf routing, a quarter with repeated and invalid ids; every
+    eighth aims at the paired 32-row blocks (~34 routes per expert, I <= 512)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 41)) if i % 3 == 0 else int(rng.integers(41, 2501))
+        D = 256 * int(rng.integers(1, 6))
+        I = 256 * int(rng.integers(1, 5))
+        E = int(rng.integers(2, 301))
+        n_routed = int(rng.integers(1, min(E - 1, 12) + 1))
+        if i % 8 == 7:
+            M = int(rng.integers(200, 1501))
+            I = 256 * int(rng.integers(1, 3))
+            n_routed = int(rng.integers(2, 9))
+            E = max(n_routed + 1, round(M * (n_routed + 1) / 34.0))
+        routing = "zipf" if rng.random() < 0.3 else "uniform"
+        dirty = bool(rng.random() < 0.25)
+        out.append((M, D, I, E, n_routed, routing, dirty, 100 + i))
+    return out
+
+
+@pytest.mark.parametrize("M,D,I,E,n_routed,routing,dirty,seed", _random_shapes())
+def test_forward_random_shapes(binding, M, D, I, E, n_routed, routing, dirty, seed):
+    """Seeded random shapes, intermediates included, checked on a set of
+    tokens covering every used block of the oracle's route list."""
+    hidden, ids, tw = inputs.make_activations(M, D, E, n_routed, routing, seed)
+    if dirty:
+        ids = ids.clone()
+        if n_routed > 1:
+            ids[::3, 1] = ids[::3, 0]           # a repeated id within a token
+        ids[::5, 0] = -1                        # invalid ids
+        ids[1::7, -1] = E + 11
+    case = custom_case(M, D, I, E, n_routed, seed, routing=routing, ids=ids, tw=tw)
+    dbg = case.run_gpu(debug=True)
+    toks = covering_tokens(case.ids, case.tw, case.E, dbg["block_m"], must=(0, case.M - 1))
+    log(f"random shape M={M} D={D} I={I} E={E} topk={n_routed + 1} {routing} dirty={dirty}: path "
+        f"{binding.PATH_NAMES[dbg['path']]}, block_m {dbg['block_m']}, oracle on {toks.size} tokens")
+    _check_forward(case, dbg, f"random shape seed {seed}", tokens=toks)
+
+
 # sorted path (32-row blocks), paired 32-row blocks (33.3 routes per expert at
 # I=256), route-indexed path
 @pytest.mark.parametrize("M,E", [(20, 6), (100, 12), (8, 40)])
