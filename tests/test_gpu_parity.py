@@ -447,27 +447,35 @@ def test_forward_large_topk(binding, M, D, I, E, n_routed, seed, path):
     _check_forward(case, dbg, f"top-{case.topk} {path} M={M} E={E}")
 
 
-def _random_shapes(n=40, seed=2026):
-    """Seeded shapes across all paths and block sizes: M from 1 to 2,500, D and
-    I multiples of 256 up to 1,280 and 1,024, E from 2 to 300, up to 13 slots,
-    uniform or Zipf routing, a quarter with repeated and invalid ids; every
-    eighth aims at the paired 32-row blocks (~34 routes per expert, I <= 512)."""
+def _random_shapes(n=None, seed=None):
+    """Seeded shapes across all paths and block sizes: M from 1 to 3,200, D up
+    to 1,536 and I up to 1,024 (multiples of 256), E from 2 to 400 (halved
+    while E*D*I exceeds 3.5e8, to keep the oracle's weight quantization short),
+    up to 16 slots, uniform or Zipf routing, a quarter with repeated and
+    invalid ids; every sixth aims at the paired 32-row blocks (30 to 40 routes
+    per expert, I <= 512).  MOE_RANDOM_SHAPES and MOE_RANDOM_SEED set the count
+    (40) and the generator's seed (2026) for a longer sweep."""
+    import os
+    n = int(os.environ.get("MOE_RANDOM_SHAPES", 40)) if n is None else n
+    seed = int(os.environ.get("MOE_RANDOM_SEED", 2026)) if seed is None else seed
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        M = int(rng.integers(1, 41)) if i % 3 == 0 else int(rng.integers(41, 2501))
-        D = 256 * int(rng.integers(1, 6))
+        M = int(rng.integers(1, 41)) if i % 3 == 0 else int(rng.integers(41, 3201))
+        D = 256 * int(rng.integers(1, 7))
         I = 256 * int(rng.integers(1, 5))
-        E = int(rng.integers(2, 301))
-        n_routed = int(rng.integers(1, min(E - 1, 12) + 1))
-        if i % 8 == 7:
-            M = int(rng.integers(200, 1501))
+        E = int(rng.integers(2, 401))
+        while E * D * I > 3.5e8:
+            E = max(2, E // 2)
+        n_routed = int(rng.integers(1, min(E - 1, 15) + 1))
+        if i % 6 == 5:
+            M = int(rng.integers(100, 2001))
             I = 256 * int(rng.integers(1, 3))
-            n_routed = int(rng.integers(2, 9))
-            E = max(n_routed + 1, round(M * (n_routed + 1) / 34.0))
+            n_routed = int(rng.integers(1, 9))
+            E = max(n_routed + 1, round(M * (n_routed + 1) / float(rng.uniform(30, 40))))
         routing = "zipf" if rng.random() < 0.3 else "uniform"
         dirty = bool(rng.random() < 0.25)
-        out.append((M, D, I, E, n_routed, routing, dirty, 100 + i))
+        out.append((M, D, I, E, n_routed, routing, dirty, seed * 1000 + i))
     return out
 
 
