@@ -161,6 +161,55 @@ def test_route_edge_cases(binding, M, E, k, bm):
                                   want["block_expert"])
 
 
+def _random_route_cases(n=30, seed=7):
+    """Seeded route lists: M up to 20,000, E up to 1,024, up to 32 slots, every
+    block size; ids uniform, Zipf-skewed or one hot expert, a third with
+    invalid (-1, E, large) and repeated ids.  They span the one-wave sort
+    (up to 768 routes) and the chunked workgroup sort (1 to ~300 chunks)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 65)) if i % 4 == 0 else int(rng.integers(65, 20001))
+        E = int(rng.integers(1, 1025))
+        k = int(rng.integers(1, 33))
+        bm = int(rng.choice([16, 32, 64, 128, 256]))
+        kind = ["uniform", "zipf", "hot"][i % 3]
+        out.append((M, E, k, bm, kind, bool(rng.random() < 0.34), 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("M,E,k,bm,kind,dirty,seed", _random_route_cases())
+def test_route_random(binding, M, E, k, bm, kind, dirty, seed):
+    """The sorted route list, weights, block experts and counts equal the
+    oracle's bit for bit on seeded random routings."""
+    rng = np.random.default_rng(seed)
+    if kind == "uniform":
+        ids = rng.integers(0, E, (M, k))
+    elif kind == "zipf":
+        ids = (rng.zipf(1.3, (M, k)) - 1) % E
+    else:
+        ids = np.where(rng.random((M, k)) < 0.7, E // 2, rng.integers(0, E, (M, k)))
+    ids = ids.astype(np.int32)
+    if dirty:
+        if k > 1:
+            ids[::3, 1] = ids[::3, 0]
+        ids[::5, 0] = -1
+        ids[1::7, -1] = E
+        ids[2::11, k // 2] = 1 << 30
+    tw = rng.random((M, k)).astype(np.float32)
+    log(f"route random M={M} E={E} k={k} bm={bm} {kind} dirty={dirty}")
+    got = binding.moe_mxfp4_route(torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda(), E, bm)
+    torch.cuda.synchronize()
+    want = oracle.route(ids, tw, E, bm)
+    n = int(want["num_valid"][0])
+    np.testing.assert_array_equal(got["num_valid"].cpu().numpy(), want["num_valid"])
+    np.testing.assert_array_equal(got["sorted_route"].cpu().numpy()[:n], want["sorted_route"])
+    np.testing.assert_array_equal(got["sorted_w"].cpu().numpy()[:n], want["sorted_w"])
+    be = got["block_expert"].cpu().numpy()
+    np.testing.assert_array_equal(be[: n // bm], want["block_expert"])
+    assert np.all(be[n // bm:] == -1)
+
+
 # --------------------------------------------------------------- prepare ---
 
 def _layout_reference(raw_codes, raw_scales, N, K, gate_up_I):
