@@ -120,10 +120,11 @@ hipError_t run_mfma_probe(int random_ops, int iters, int n_cu, int wall_khz, hip
         out->per_clock_frac =
             out->shader_mhz > 0 ? out->tflops * 1e12 / (per_clock * out->shader_mhz * 1e6) : 0.0;
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    if (rec) hipFree(rec);
-    if (sink) hipFree(sink);
+    // clean-up errors would not change the measurement already taken
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (rec) (void)hipFree(rec);
+    if (sink) (void)hipFree(sink);
     return err;
 }
 

@@ -686,11 +686,11 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint
 hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
                            const KernelEvents& ev)
 {
-    const uint32_t lds = uint32_t(route_lds_bytes(a.E));
+    const uint32_t lds_bytes = uint32_t(route_lds_bytes(a.E));
     const int G = route_chunks(a.M, a.topk);
     if (G > 0) {
         const int64_t blocks = G + quant_blocks(a.M, a.D, n_cu);
-        MOE_LAUNCH(prologue_sort_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds,
+        MOE_LAUNCH(prologue_sort_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds_bytes,
                    stream, ev, a, G);
         return hipGetLastError();
     }
@@ -698,7 +698,7 @@ hipError_t launch_prologue(const PrologueArgs& a, int n_cu, hipStream_t stream,
     // a single workgroup sorting 9,216 routes measured 28 us against 20 us for
     // the two chunked launches, 36,864 routes 86 against 30 us)
     const int64_t blocks = 1 + quant_blocks(a.M, a.D, n_cu);
-    MOE_LAUNCH(prologue_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds, stream, ev,
+    MOE_LAUNCH(prologue_kernel, dim3(unsigned(blocks)), dim3(kPrologueThreads), lds_bytes, stream, ev,
                a);
     return hipGetLastError();
 }
