@@ -540,14 +540,18 @@ def run(args):
 
 def mfma_ceiling(iters=2_000_000):
     """The FP4 MFMA rate on register operands (no memory traffic), with random
-    and with single-bit operands, against the published dense peak."""
+    and with single-bit operands, for the 32x32x64 instruction of the tiled
+    kernels and the 16x16x128 one of the streaming kernels, against the
+    published dense peak."""
     import torch
 
     from mixture_experts_mxfp4_amd import binding
     torch.cuda.set_device(0)
     out = {"published_peak_tflops": FP4_PEAK_TFLOPS, "iters_per_wave": iters}
-    for name, rnd in (("random_operands", True), ("single_bit_operands", False)):
-        r = binding.moe_mxfp4_mfma_probe(rnd, iters)
+    for name, rnd, small in (("random_operands", True, False), ("single_bit_operands", False, False),
+                             ("random_operands_16x16x128", True, True),
+                             ("single_bit_operands_16x16x128", False, True)):
+        r = binding.moe_mxfp4_mfma_probe(rnd, iters, small_tile=small)
         out[name] = {"tflops": round(r["tflops"], 1), "shader_mhz": round(r["shader_mhz"], 1),
                      "per_clock_frac": round(r["per_clock_frac"], 4),
                      "frac_of_peak": round(r["tflops"] / FP4_PEAK_TFLOPS, 4)}

@@ -322,19 +322,21 @@ int moe_mxfp4_forward_profiled(const uint16_t* hidden,
 int moe_mxfp4_wall_clock_khz(void);
 
 /* Measurement aid, not part of the forward: the rate the gfx950 block-scaled
- * FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E2M1) sustains
- * on register operands with no memory traffic, the practical ceiling of the
- * LDS-tiled GEMMs.  Two workgroups of four waves per CU run `iters` x 4
- * independent MFMAs per wave (1 <= iters <= 2^24) on operands with random
- * bits (random_operands != 0) or a single set bit per 32-bit word, after a
- * shorter settling launch; the call blocks until both have run on `stream`.
- * Outputs (host pointers): *tflops over the measured launch (events),
- * *shader_mhz the waves' mean shader clock (cycle counter against the
- * constant-rate real-time clock), *per_clock_frac the rate over one such MFMA
- * per 32 cycles per SIMD at that clock.  Allocates and frees its own
- * record buffers.  Returns OK, INVALID_ARG (iters out of range or a null
- * output), UNSUPPORTED (not gfx950) or HIP. */
-int moe_mxfp4_mfma_probe(int random_operands, int iters, double* tflops, double* shader_mhz,
+ * FP4 MFMA (both operands E2M1) sustains on register operands with no memory
+ * traffic, the practical ceiling of the LDS-tiled GEMMs.  flags: bit 0 set,
+ * operands with random bits, else a single set bit per 32-bit word; bit 1
+ * set, v_mfma_scale_f32_16x16x128_f8f6f4 (8 independent MFMAs per wave and
+ * iteration), else v_mfma_scale_f32_32x32x64_f8f6f4 (4); other bits must be
+ * clear.  Two workgroups of four waves per CU run `iters` iterations per
+ * wave (1 <= iters <= 2^24) after a shorter settling launch; the call blocks
+ * until both have run on `stream`.  Outputs (host pointers): *tflops over
+ * the measured launch (events), *shader_mhz the waves' mean shader clock
+ * (cycle counter against the constant-rate real-time clock), *per_clock_frac
+ * the rate over the FP4 peak at that clock (one 32x32x64 MFMA per 32 cycles
+ * per SIMD).  Allocates and frees its own record buffers.  Returns OK,
+ * INVALID_ARG (unknown flag bits, iters out of range or a null output),
+ * UNSUPPORTED (not gfx950) or HIP. */
+int moe_mxfp4_mfma_probe(int flags, int iters, double* tflops, double* shader_mhz,
                          double* per_clock_frac, hipStream_t stream);
 
 /* Number of workgroups of the stage-1 launch for this shape (0 for an

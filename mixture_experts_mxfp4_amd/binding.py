@@ -256,12 +256,17 @@ def moe_mxfp4_wall_clock_khz() -> int:
     return int(_lib.moe_mxfp4_wall_clock_khz())
 
 
-def moe_mxfp4_mfma_probe(random_operands: bool, iters: int, stream=None) -> dict:
+def moe_mxfp4_mfma_probe(random_operands: bool, iters: int, stream=None, small_tile=False,
+                         flags=None) -> dict:
     """Register-only FP4 MFMA rate on the current device: TFLOP/s, mean
-    shader clock (MHz) and share of the per-clock MFMA rate."""
+    shader clock (MHz) and share of the per-clock FP4 peak.  small_tile: the
+    16x16x128 instruction instead of 32x32x64.  flags, when given, is passed
+    to the C call as it is (bit 0 random operands, bit 1 small tile)."""
+    if flags is None:
+        flags = int(bool(random_operands)) | (2 if small_tile else 0)
     tf, mhz, frac = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     _check("moe_mxfp4_mfma_probe",
-           _lib.moe_mxfp4_mfma_probe(int(bool(random_operands)), int(iters), ctypes.byref(tf),
+           _lib.moe_mxfp4_mfma_probe(int(flags), int(iters), ctypes.byref(tf),
                                      ctypes.byref(mhz), ctypes.byref(frac), _stream(stream)))
     return {"tflops": tf.value, "shader_mhz": mhz.value, "per_clock_frac": frac.value}
 

@@ -468,16 +468,16 @@ MOE_API int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk
     return moe::tile_grid(I / (32 * moe::stream_stage1_groups(L.bm)), int(L.nb));
 }
 
-MOE_API int moe_mxfp4_mfma_probe(int random_operands, int iters, double* tflops, double* shader_mhz,
+MOE_API int moe_mxfp4_mfma_probe(int flags, int iters, double* tflops, double* shader_mhz,
                                  double* per_clock_frac, hipStream_t stream)
 {
-    if (iters < 1 || iters > (1 << 24) || !tflops || !shader_mhz || !per_clock_frac)
+    if ((flags & ~3) || iters < 1 || iters > (1 << 24) || !tflops || !shader_mhz || !per_clock_frac)
         return MOE_MXFP4_ERR_INVALID_ARG;
     int n_cu = 0, khz = 0;
     int st = device_check(&n_cu, nullptr, &khz);
     if (st) return st;
     moe::ProbeResult r{};
-    if (moe::run_mfma_probe(random_operands ? 1 : 0, iters, n_cu, khz, stream, &r) != hipSuccess)
+    if (moe::run_mfma_probe(flags & 1, (flags >> 1) & 1, iters, n_cu, khz, stream, &r) != hipSuccess)
         return MOE_MXFP4_ERR_HIP;
     *tflops = r.tflops;
     *shader_mhz = r.shader_mhz;

@@ -9,13 +9,14 @@ struct ProbeResult {
     double ms;               // the measured launch (events)
     double tflops;           // FP4 MFMA rate over it
     double shader_mhz;       // mean shader clock of its waves
-    double per_clock_frac;   // rate over one 32x32x64 MFMA per 32 cycles per SIMD at that clock
+    double per_clock_frac;   // rate over the FP4 peak per clock: one 32x32x64 MFMA per 32 cycles per SIMD
 };
 
 // Two workgroups of four waves per CU, each wave `iters` x 4 independent
-// MFMAs on register operands (random bits, or one set bit per word), after
-// a short settling launch.  Allocates and frees its own record buffers.
-hipError_t run_mfma_probe(int random_ops, int iters, int n_cu, int wall_khz, hipStream_t stream,
-                          ProbeResult* out);
+// 32x32x64 MFMAs (small_tile: 8 independent 16x16x128 ones) on register
+// operands (random bits, or one set bit per word), after a short settling
+// launch.  Allocates and frees its own record buffers.
+hipError_t run_mfma_probe(int random_ops, int small_tile, int iters, int n_cu, int wall_khz,
+                          hipStream_t stream, ProbeResult* out);
 
 }  // namespace moe
