@@ -26,11 +26,13 @@ def _case(kind):
         return workload_case("decode")
     if kind == "small_batch":
         return workload_case("small_batch", M=40)
+    if kind == "prefill":
+        return workload_case("prefill")                 # paired 32-row blocks, chunked sort
     return custom_case(1400, 512, 256, 5, 2, 25)       # LDS-tiled path
 
 
 @pytest.mark.parametrize("kind,a16", [("decode", False), ("decode", True), ("small_batch", False),
-                                      ("tiled", False)])
+                                      ("prefill", False), ("tiled", False)])
 def test_forward_graph_replay(binding, kind, a16):
     case = _case(kind)
     d = case.device_inputs()
