@@ -168,6 +168,13 @@ def test_host_validation_without_device(binding):
     assert lib.moe_mxfp4_prepare_weights(*([ok] * 4), 2, 512, 256, *([null] * 4), null) == 1
     # in-place (aliasing) prepare is rejected
     assert lib.moe_mxfp4_prepare_weights(*([ok] * 4), 2, 512, 256, *([ok] * 4), null) == 1
+    # the MFMA probe: unknown flag bits, iteration counts out of range and null outputs
+    lib.moe_mxfp4_mfma_probe.argtypes = binding._lib.moe_mxfp4_mfma_probe.argtypes
+    d = [ctypes.c_double() for _ in range(3)]
+    outs = [ctypes.byref(x) for x in d]
+    for flags, iters in ((4, 100), (-1, 100), (0, 0), (3, (1 << 24) + 1)):
+        assert lib.moe_mxfp4_mfma_probe(flags, iters, *outs, null) == 1
+    assert lib.moe_mxfp4_mfma_probe(1, 100, null, outs[1], outs[2], null) == 1
 
 
 def test_a16w4_sizing_and_validation(binding):
