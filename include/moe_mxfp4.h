@@ -339,6 +339,25 @@ int moe_mxfp4_wall_clock_khz(void);
 int moe_mxfp4_mfma_probe(int flags, int iters, double* tflops, double* shader_mhz,
                          double* per_clock_frac, hipStream_t stream);
 
+/* Debug check of one block-scaled FP4 MFMA instruction, the building block of
+ * every GEMM here.  The MXFP4 product it computes is the one kernelindex
+ * submission 754773's FP4 branch (`custom_kernel`) runs on both GEMM inputs:
+ * E2M1 codes with one e8m0 scale per 32 elements.  The value of a code times
+ * 2^(scale-127) is the decode of submission 723815's `_dequant`.
+ * rows 16: v_mfma_scale_f32_16x16x128_f8f6f4 on 16 x 128 operands; rows 32:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on 32 x 64.  a, b: device, row-major
+ * [rows][K/2] code bytes (element 2j in the low nibble), 16-byte aligned;
+ * a_scales, b_scales: device [rows][K/32] e8m0 bytes; out: device fp32
+ * [rows][rows], out[i][j] = sum_k A[i][k] * B[j][k], accumulated by the
+ * instruction.  Each scale reaches the instruction in byte `sel` (0-3) of its
+ * 32-bit word, the other bytes 0xFF (NaN), so a wrong byte select yields NaN.
+ * One wave on `stream`; no allocation, stream-ordered.  Returns OK,
+ * INVALID_ARG (rows not 16 or 32, sel outside 0-3, a null or misaligned
+ * pointer), UNSUPPORTED (not gfx950) or HIP. */
+int moe_mxfp4_debug_mfma(int rows, int sel, const uint8_t* a, const uint8_t* a_scales,
+                         const uint8_t* b, const uint8_t* b_scales, float* out,
+                         hipStream_t stream);
+
 /* Number of workgroups of the stage-1 launch for this shape (0 for an
  * invalid shape or M = 0). */
 int64_t moe_mxfp4_stage1_workgroups(int M, int D, int I, int E, int topk);

@@ -41,6 +41,8 @@ _lib.moe_mxfp4_forward_profiled.argtypes = [_P] * 8 + [_I] * 5 + [_P, _SZ, _P, _
 _lib.moe_mxfp4_wall_clock_khz.argtypes, _lib.moe_mxfp4_wall_clock_khz.restype = [], _I
 _lib.moe_mxfp4_mfma_probe.argtypes = [_I, _I, _P, _P, _P, _P]
 _lib.moe_mxfp4_mfma_probe.restype = _I
+_lib.moe_mxfp4_debug_mfma.argtypes = [_I, _I] + [_P] * 5 + [_P]
+_lib.moe_mxfp4_debug_mfma.restype = _I
 _lib.moe_mxfp4_stage1_workgroups.argtypes = [_I] * 5
 _lib.moe_mxfp4_stage1_workgroups.restype = _I64
 _lib.moe_mxfp4_forward_profiled.restype = _I
@@ -82,7 +84,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_workspace_bytes", "moe_mxfp4_bl
            "moe_mxfp4_workspace_init", "moe_mxfp4_persistent_workgroups",
            "moe_mxfp4_forward_persistent", "moe_mxfp4_forward_persistent_debug",
            "moe_mxfp4_splitk_workspace_bytes", "moe_mxfp4_forward_splitk",
-           "moe_mxfp4_forward_splitk_debug", "moe_mxfp4_mfma_probe")
+           "moe_mxfp4_forward_splitk_debug", "moe_mxfp4_mfma_probe", "moe_mxfp4_debug_mfma")
 
 
 class MoeMxfp4Error(RuntimeError):
@@ -269,6 +271,26 @@ def moe_mxfp4_mfma_probe(random_operands: bool, iters: int, stream=None, small_t
            _lib.moe_mxfp4_mfma_probe(int(flags), int(iters), ctypes.byref(tf),
                                      ctypes.byref(mhz), ctypes.byref(frac), _stream(stream)))
     return {"tflops": tf.value, "shader_mhz": mhz.value, "per_clock_frac": frac.value}
+
+
+def moe_mxfp4_debug_mfma(a, a_scales, b, b_scales, sel=0, stream=None):
+    """One block-scaled FP4 MFMA: a, b uint8 [R, K/2] E2M1 codes, a_scales,
+    b_scales uint8 [R, K/32] e8m0 (R x K = 16 x 128 or 32 x 64), on the GPU;
+    returns A . B^T as float32 [R, R], the scales passed in byte `sel` of
+    their words."""
+    R = a.shape[0]
+    if R not in (16, 32):
+        raise ValueError("rows must be 16 or 32")
+    K = 128 if R == 16 else 64
+    dev = a.device
+    pa = _ptr(a, torch.uint8, (R, K // 2), "a", dev)
+    ps = _ptr(a_scales, torch.uint8, (R, K // 32), "a_scales", dev)
+    pb = _ptr(b, torch.uint8, (R, K // 2), "b", dev)
+    pbs = _ptr(b_scales, torch.uint8, (R, K // 32), "b_scales", dev)
+    out = torch.empty((R, R), dtype=torch.float32, device=dev)
+    _check("moe_mxfp4_debug_mfma",
+           _lib.moe_mxfp4_debug_mfma(R, int(sel), pa, ps, pb, pbs, _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_mxfp4_stage1_workgroups(M, D, I, E, topk) -> int:

@@ -485,6 +485,20 @@ MOE_API int moe_mxfp4_mfma_probe(int flags, int iters, double* tflops, double* s
     return MOE_MXFP4_OK;
 }
 
+MOE_API int moe_mxfp4_debug_mfma(int rows, int sel, const uint8_t* a, const uint8_t* a_scales,
+                                 const uint8_t* b, const uint8_t* b_scales, float* out,
+                                 hipStream_t stream)
+{
+    if ((rows != 16 && rows != 32) || sel < 0 || sel > 3 || !a || !a_scales || !b || !b_scales ||
+        !out || reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(b) % 16 ||
+        reinterpret_cast<uintptr_t>(out) % 4)
+        return MOE_MXFP4_ERR_INVALID_ARG;
+    int n_cu = 0;
+    const int st = device_check(&n_cu, nullptr, nullptr);
+    if (st) return st;
+    return hip_status(moe::run_mfma_unit(rows, sel, a, a_scales, b, b_scales, out, stream));
+}
+
 MOE_API int moe_mxfp4_wall_clock_khz(void)
 {
     int dev = 0, khz = 0;

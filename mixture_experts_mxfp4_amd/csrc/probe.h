@@ -19,4 +19,11 @@ struct ProbeResult {
 hipError_t run_mfma_probe(int random_ops, int small_tile, int iters, int n_cu, int wall_khz,
                           hipStream_t stream, ProbeResult* out);
 
+// One block-scaled FP4 MFMA (rows 16: 16x16x128, 32: 32x32x64) on row-major
+// E2M1 operands with per-32 e8m0 scales, the scale in byte `sel` (0-3) of its
+// word; out = A . B^T, fp32 row-major rows x rows.  One wave; arguments
+// checked by the caller.
+hipError_t run_mfma_unit(int rows, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                         const uint8_t* bs, float* out, hipStream_t stream);
+
 }  // namespace moe

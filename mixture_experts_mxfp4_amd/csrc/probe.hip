@@ -89,6 +89,65 @@ mfma_probe_kernel(int iters, int random_ops, uint64_t* __restrict__ rec, float* 
     }
 }
 
+// One block-scaled FP4 MFMA on given operands, one wave: the unit check of
+// the operand, scale and result layouts every GEMM kernel here relies on.  A
+// and B are R x K E2M1 codes (two per byte, element 2j in the low nibble) with
+// one e8m0 scale per 32 elements, R x K = 16 x 128 (16x16x128) or 32 x 64
+// (32x32x64); lane l holds row l % R and 32-element chunk l / R of each.
+// The lane's scale byte goes into byte SEL of a 32-bit word whose other bytes
+// are 0xFF (the e8m0 NaN), so a wrong byte select gives NaN.  out[i][j] =
+// sum_k A[i][k] B[j][k] (fp32, row-major R x R): the first operand's rows
+// run down the result, the second's across.
+template <int R, int SEL>
+__global__ void __launch_bounds__(kWave)
+mfma_unit_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
+                 const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, float* __restrict__ out)
+{
+    constexpr int K = R == 16 ? 128 : 64;
+    const int lane = threadIdx.x;
+    const int row = lane % R, chunk = lane / R;
+    const uint4 av = *reinterpret_cast<const uint4*>(a + row * (K / 2) + chunk * 16);
+    const uint4 bv = *reinterpret_cast<const uint4*>(b + row * (K / 2) + chunk * 16);
+    const uint32_t fill = ~(0xFFu << (8 * SEL));
+    const uint32_t sa = fill | (uint32_t(as[row * (K / 32) + chunk]) << (8 * SEL));
+    const uint32_t sb = fill | (uint32_t(bs[row * (K / 32) + chunk]) << (8 * SEL));
+    const v8i A = {int(av.x), int(av.y), int(av.z), int(av.w), 0, 0, 0, 0};
+    const v8i B = {int(bv.x), int(bv.y), int(bv.z), int(bv.w), 0, 0, 0, 0};
+    if constexpr (R == 16) {
+        v4f c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, SEL, int(sa), SEL, int(sb));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[(4 * (lane / 16) + i) * 16 + lane % 16] = c[i];
+    } else {
+        v16f c;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = 0.f;
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, SEL, int(sa), SEL, int(sb));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[((i / 4) * 8 + (lane / 32) * 4 + i % 4) * 32 + lane % 32] = c[i];
+    }
+}
+
+template <int R>
+static hipError_t launch_mfma_unit(int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                   const uint8_t* bs, float* out, hipStream_t stream)
+{
+    switch (sel) {
+    case 0: hipLaunchKernelGGL((mfma_unit_kernel<R, 0>), dim3(1), dim3(kWave), 0, stream, a, as, b, bs, out); break;
+    case 1: hipLaunchKernelGGL((mfma_unit_kernel<R, 1>), dim3(1), dim3(kWave), 0, stream, a, as, b, bs, out); break;
+    case 2: hipLaunchKernelGGL((mfma_unit_kernel<R, 2>), dim3(1), dim3(kWave), 0, stream, a, as, b, bs, out); break;
+    default: hipLaunchKernelGGL((mfma_unit_kernel<R, 3>), dim3(1), dim3(kWave), 0, stream, a, as, b, bs, out); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t run_mfma_unit(int rows, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                         const uint8_t* bs, float* out, hipStream_t stream)
+{
+    return rows == 16 ? launch_mfma_unit<16>(sel, a, as, b, bs, out, stream)
+                      : launch_mfma_unit<32>(sel, a, as, b, bs, out, stream);
+}
+
 hipError_t run_mfma_probe(int random_ops, int small_tile, int iters, int n_cu, int wall_khz,
                           hipStream_t stream, ProbeResult* out)
 {
